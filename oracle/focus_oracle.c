@@ -1,0 +1,343 @@
+/*
+ * Focus attention forward: plain CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the
+ * GPU library.
+ *
+ * Source of the method: "Why Attend to Everything? Focus is the Key"
+ * (arXiv 2604.03260), as summarised on the gist.science page, Technical
+ * Summary section 2 "Methodology: Focus", bullets Learnable Centroids,
+ * Token Grouping, Gated Attention (Local / Distant) and Inference
+ * Efficiency (Top-k); and on the jindou-blog deep read, method bullets
+ * (K centroids per layer, 16-dimensional routing, dot-product assignment,
+ * exact softmax in the local window and inside groups).
+ *
+ * What is computed, written out from those passages:
+ *   route : score(t, g) = <r_t, c_g> over the 16 routing dimensions; each
+ *           token keeps its top-k groups G(t).
+ *   attend: A(i) = { j <= i : i - j < w  or  G(i) and G(j) share a group }
+ *           and the output is the exact softmax over A(i).
+ *   bucket: the (token, group) entries sorted by group, then by the token's
+ *           lowest other group ("partner"), then by position.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   - score arithmetic: fp32, products and sums in index order 0..d_g-1,
+ *     no fused multiply-add (build with -ffp-contract=off);
+ *   - ties in the top-k: the lower group index wins; -0.0 equals +0.0;
+ *   - window: i - j < w (w keys including the query itself);
+ *   - softmax scale is an argument (1/sqrt(d) in every workload);
+ *   - attention sums are accumulated in double from the fp32 (or bf16
+ *     widened) inputs, so the oracle's own error is far below the
+ *     tolerances it is compared at.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+/* Score of one token against one centroid: fp32 products accumulated left to
+ * right (Technical Summary, Token Grouping: the projected state is compared
+ * with each centroid by a dot product). */
+static float score_fixed_order(const float *r, const float *c, int dg)
+{
+    float s = r[0] * c[0];
+    for (int e = 1; e < dg; ++e) {
+        float p = r[e] * c[e];
+        s = s + p;
+    }
+    return s;
+}
+
+/* Top-k routing (Technical Summary, Inference Efficiency (Top-k): each token
+ * joins its k highest-scoring groups).  Selection sort: pass s picks the best
+ * group not yet taken, scanning g upward and replacing only on a strictly
+ * larger score, so equal scores resolve to the lower index. */
+int oracle_route(const float *r, const float *centroids, int32_t H, int64_t n,
+                 int32_t dg, int32_t K, int32_t topk, int32_t *groups,
+                 uint32_t *gmask)
+{
+    if (!r || !centroids || !groups || H < 1 || n < 1 || dg < 1 || K < 1 ||
+        K > 32 || topk < 1 || topk > K)
+        return ORACLE_BAD_ARG;
+#pragma omp parallel
+    {
+        float scores[32];
+        int taken[32];
+#pragma omp for schedule(static)
+        for (int64_t ht = 0; ht < (int64_t)H * n; ++ht) {
+            int64_t h = ht / n;
+            const float *rt = r + ht * dg;
+            for (int g = 0; g < K; ++g) {
+                scores[g] = score_fixed_order(rt, centroids + ((int64_t)h * K + g) * dg, dg);
+                taken[g] = 0;
+            }
+            uint32_t bits = 0;
+            for (int s = 0; s < topk; ++s) {
+                int best = -1;
+                for (int g = 0; g < K; ++g) {
+                    if (taken[g])
+                        continue;
+                    if (best < 0 || scores[g] > scores[best])
+                        best = g;
+                }
+                taken[best] = 1;
+                groups[ht * topk + s] = best;
+                bits |= 1u << best;
+            }
+            if (gmask)
+                gmask[ht] = bits;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Partner of token t inside group g: its lowest group other than g, or K when
+ * it belongs to g alone (top-1). */
+static int partner_of(const int32_t *gt, int topk, int g, int K)
+{
+    int p = K;
+    for (int s = 0; s < topk; ++s)
+        if (gt[s] != g && gt[s] < p)
+            p = gt[s];
+    return p;
+}
+
+/* Bucketing: the per-group token lists that within-group causal attention
+ * runs over (Technical Summary, Key Contributions 5: the pattern splits into
+ * a local-window call and a within-group causal call).  Entries are listed
+ * group by group; inside a group, sub-bucket by partner 0..K, and inside a
+ * sub-bucket by ascending position.  offsets has K*(K+1)+1 entries per head;
+ * slot_entry[t][s] is the entry that holds (t, groups[t][s]). */
+int oracle_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
+                  int32_t topk, int32_t *offsets, int32_t *tokens,
+                  int32_t *slot_entry)
+{
+    if (!groups || !offsets || !tokens || !slot_entry || H < 1 || n < 1 ||
+        K < 1 || K > 32 || topk < 1 || topk > K || n * topk > INT32_MAX)
+        return ORACLE_BAD_ARG;
+    const int nsb = K * (K + 1);
+    int32_t *part = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    if (!part || !slot) {
+        free(part);
+        free(slot);
+        return ORACLE_NO_MEMORY;
+    }
+    for (int h = 0; h < H; ++h) {
+        const int32_t *gh = groups + (int64_t)h * n * topk;
+        int32_t *off = offsets + (int64_t)h * (nsb + 1);
+        int32_t *tok = tokens + (int64_t)h * n * topk;
+        int32_t *se = slot_entry + (int64_t)h * n * topk;
+        int32_t cursor = 0;
+        for (int g = 0; g < K; ++g) {
+            /* membership slot and partner of every token for this group */
+            for (int64_t t = 0; t < n; ++t) {
+                slot[t] = -1;
+                for (int s = 0; s < topk; ++s)
+                    if (gh[t * topk + s] == g)
+                        slot[t] = s;
+                part[t] = slot[t] >= 0 ? partner_of(gh + t * topk, topk, g, K) : -1;
+            }
+            for (int m = 0; m <= K; ++m) {
+                off[g * (K + 1) + m] = cursor;
+                for (int64_t t = 0; t < n; ++t) {
+                    if (slot[t] < 0 || part[t] != m)
+                        continue;
+                    tok[cursor] = (int32_t)t;
+                    se[t * topk + slot[t]] = cursor;
+                    ++cursor;
+                }
+            }
+        }
+        off[nsb] = cursor;
+    }
+    free(part);
+    free(slot);
+    return ORACLE_OK;
+}
+
+static uint32_t group_bits(const int32_t *gt, int topk)
+{
+    uint32_t b = 0;
+    for (int s = 0; s < topk; ++s)
+        b |= 1u << gt[s];
+    return b;
+}
+
+static double widen(const void *base, int is_bf16, int64_t idx)
+{
+    if (is_bf16) {
+        uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)base)[idx];
+}
+
+/* Exact softmax over the attended set A(i) (Technical Summary, Gated
+ * Attention: the local window w attends with exact softmax, distant tokens
+ * only when they share a group; Inference Efficiency (Top-k): sharing at
+ * least one of the top-k groups is enough).  Evaluates the listed (head, row)
+ * pairs.  Query head h reads key/value head h / (Hq/Hkv) and the routing of
+ * that key/value head.  Outputs: o[row][d] (double), lse[row] (natural log of
+ * the softmax denominator of the scaled scores), count[row] = |A(i)|. */
+int oracle_attn_rows(const void *q, const void *k, const void *v, int32_t is_bf16,
+                     int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
+                     const int32_t *groups, int32_t K, int32_t topk, int64_t w,
+                     double scale, const int32_t *row_head, const int64_t *row_pos,
+                     int64_t nrows, double *o, double *lse, int64_t *count,
+                     int32_t nthreads)
+{
+    if (!q || !k || !v || !groups || !row_head || !row_pos || Hq < 1 ||
+        Hkv < 1 || Hq % Hkv || n < 1 || d < 1 || K < 1 || K > 32 ||
+        topk < 1 || topk > K || w < 0 || nrows < 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (row_head[r] < 0 || row_head[r] >= Hq || row_pos[r] < 0 || row_pos[r] >= n)
+            return ORACLE_BAD_ARG;
+    uint32_t *bits = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(Hkv * n));
+    if (!bits)
+        return ORACLE_NO_MEMORY;
+    for (int64_t ht = 0; ht < (int64_t)Hkv * n; ++ht)
+        bits[ht] = group_bits(groups + ht * topk, topk);
+    const int ratio = Hq / Hkv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)n);
+        double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!sc || !qi || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (failed)
+                continue;
+            const int h = row_head[r];
+            const int64_t i = row_pos[r];
+            const int hk = h / ratio;
+            const uint32_t *bk = bits + (int64_t)hk * n;
+            for (int e = 0; e < d; ++e)
+                qi[e] = widen(q, is_bf16, ((int64_t)h * n + i) * d + e);
+            /* pass 1: scores of the attended keys and their maximum */
+            double mx = -INFINITY;
+            int64_t cnt = 0;
+            for (int64_t j = 0; j <= i; ++j) {
+                int in_window = (i - j) < w;
+                int shares = (bk[i] & bk[j]) != 0;
+                if (!in_window && !shares) {
+                    sc[j] = NAN;
+                    continue;
+                }
+                double s = 0.0;
+                const int64_t kb = ((int64_t)hk * n + j) * d;
+                for (int e = 0; e < d; ++e)
+                    s += qi[e] * widen(k, is_bf16, kb + e);
+                s *= scale;
+                sc[j] = s;
+                if (s > mx)
+                    mx = s;
+                ++cnt;
+            }
+            /* pass 2: softmax weights and the weighted sum of values */
+            double l = 0.0;
+            for (int e = 0; e < d; ++e)
+                acc[e] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                if (isnan(sc[j]))
+                    continue;
+                double p = exp(sc[j] - mx);
+                l += p;
+                const int64_t vb = ((int64_t)hk * n + j) * d;
+                for (int e = 0; e < d; ++e)
+                    acc[e] += p * widen(v, is_bf16, vb + e);
+            }
+            for (int e = 0; e < d; ++e)
+                o[r * d + e] = acc[e] / l;
+            lse[r] = mx + log(l);
+            count[r] = cnt;
+        }
+        free(sc);
+        free(qi);
+        free(acc);
+    }
+    free(bits);
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* |A(i)| for every row of every routing head, without touching q, k, v:
+ * min(i+1, w) window keys plus the keys j <= i - w whose group set meets
+ * G(i).  Walks i upward keeping, per distinct group set, how many keys at or
+ * before i - w carry it (the distinct sets are at most C(K, k) and never more
+ * than n). */
+int oracle_pair_counts(const int32_t *groups, int32_t H, int64_t n, int32_t K,
+                       int32_t topk, int64_t w, int64_t *count)
+{
+    if (!groups || !count || H < 1 || n < 1 || K < 1 || K > 32 || topk < 1 ||
+        topk > K || w < 0)
+        return ORACLE_BAD_ARG;
+    uint32_t *bits = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)n);
+    uint32_t *cls = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)n);
+    int32_t *cls_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    int64_t *cnt = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!bits || !cls || !cls_of || !cnt) {
+        free(bits);
+        free(cls);
+        free(cls_of);
+        free(cnt);
+        return ORACLE_NO_MEMORY;
+    }
+    for (int h = 0; h < H; ++h) {
+        const int32_t *gh = groups + (int64_t)h * n * topk;
+        int64_t ncls = 0;
+        for (int64_t t = 0; t < n; ++t) {
+            bits[t] = group_bits(gh + t * topk, topk);
+            int64_t c = 0;
+            while (c < ncls && cls[c] != bits[t])
+                ++c;
+            if (c == ncls) {
+                cls[ncls] = bits[t];
+                cnt[ncls] = 0;
+                ++ncls;
+            }
+            cls_of[t] = (int32_t)c;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t far_end = i - w; /* keys 0..far_end lie outside the window */
+            if (far_end >= 0)
+                cnt[cls_of[far_end]] += 1;
+            int64_t c_win = i + 1 < w ? i + 1 : w;
+            int64_t c_far = 0;
+            for (int64_t c = 0; c < ncls; ++c)
+                if (cls[c] & bits[i])
+                    c_far += cnt[c];
+            count[(int64_t)h * n + i] = c_win + c_far;
+        }
+    }
+    free(bits);
+    free(cls);
+    free(cls_of);
+    free(cnt);
+    return ORACLE_OK;
+}

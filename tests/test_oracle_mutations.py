@@ -1,0 +1,52 @@
+"""Planted mistakes: each mutation below is a plausible slip in the oracle
+(a dropped term, a wrong comparison, a wrong index).  Every one is compiled
+into a scratch copy of the oracle and the pin suite must fail against it.
+Runs on the CPU only; nothing here touches the GPU library."""
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+SRC = (ROOT / "oracle" / "focus_oracle.c").read_text()
+
+MUTATIONS = {
+    "window_le": ("int in_window = (i - j) < w;", "int in_window = (i - j) <= w;"),
+    "same_set_not_shared": ("int shares = (bk[i] & bk[j]) != 0;",
+                            "int shares = bk[i] == bk[j];"),
+    "fused_score": ("float p = r[e] * c[e];\n        s = s + p;",
+                    "s = fmaf(r[e], c[e], s);"),
+    "tie_to_higher": ("if (best < 0 || scores[g] > scores[best])",
+                      "if (best < 0 || scores[g] >= scores[best])"),
+    "gqa_modulo": ("const int hk = h / ratio;", "const int hk = h % Hkv;"),
+    "scale_dropped": ("s *= scale;", "(void)scale;"),
+    "lse_without_max": ("lse[r] = mx + log(l);", "lse[r] = log(l);"),
+    "not_causal_self": ("for (int64_t j = 0; j <= i; ++j) {\n                int in_window",
+                        "for (int64_t j = 0; j < i; ++j) {\n                int in_window"),
+    "partner_max": ("if (gt[s] != g && gt[s] < p)", "if (gt[s] != g && (p == K || gt[s] > p))"),
+    "count_far_edge": ("int64_t far_end = i - w;", "int64_t far_end = i - w + 1;"),
+    "value_index": ("acc[e] += p * widen(v, is_bf16, vb + e);",
+                    "acc[e] += p * widen(v, is_bf16, kb_unused(vb) + e);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
+    src = SRC.replace(old, new)
+    if name == "value_index":   # read v at the query row instead of the key row
+        src = src.replace("static double widen(",
+                          "#define kb_unused(x) (((int64_t)hk * n + i) * d)\nstatic double widen(")
+    cfile = tmp_path / "mut.c"
+    cfile.write_text(src)
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    "-std=c11", str(cfile), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, FOCUS_ORACLE_LIB=str(lib))
+    res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                          str(ROOT / "tests" / "test_oracle_pins.py")],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"pins did not catch mutation {name}:\n{res.stdout[-2000:]}"

@@ -1,0 +1,345 @@
+"""Pins for the CPU oracle: each check compares it with something other than
+itself — library softmax on the special cases where the Focus set reduces to
+plain causal attention, closed-form set sizes, exact integer arithmetic,
+hand-derived rounding cases and the statistics the pages print.
+
+Pages: "Why Attend to Everything? Focus is the Key" — gist.science Technical
+Summary section 2 (window, group gate, top-k), thelatestinai.com Table 7
+(pairs retained by top-k at K=4).
+"""
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from centroid_gated_sparse_amd.workloads import Workload, routing_inputs
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ----------------------------------------------------------------------------
+# helpers: library references (torch float64 on the CPU)
+
+def _rand_qkv(rng, hq, hkv, n, d, std=1.0):
+    q = (rng.standard_normal((hq, n, d)) * std).astype(np.float32)
+    k = (rng.standard_normal((hkv, n, d)) * std).astype(np.float32)
+    v = (rng.standard_normal((hkv, n, d)) * std).astype(np.float32)
+    return q, k, v
+
+
+def _expand_kv(x, hq):
+    """Key/value head h // (Hq/Hkv) serves query head h (contiguous GQA)."""
+    t = torch.from_numpy(x).double()
+    return t.repeat_interleave(hq // x.shape[0], dim=0)
+
+
+def _library_attention(q, k, v, scale, mask=None, causal=False):
+    """torch scaled_dot_product_attention plus logsumexp, float64."""
+    qt = torch.from_numpy(q).double()
+    kt = _expand_kv(k, q.shape[0])
+    vt = _expand_kv(v, q.shape[0])
+    if causal:
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                             scale=scale)
+        n = q.shape[1]
+        mask = torch.ones(n, n, dtype=torch.bool).tril()
+    else:
+        mask = torch.from_numpy(np.ascontiguousarray(mask))
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                             scale=scale)
+    s = torch.matmul(qt, kt.transpose(-1, -2)) * scale
+    s = s.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+def _assert_close(o, lse, o_ref, lse_ref, tol=1e-9):
+    np.testing.assert_allclose(o, o_ref, atol=tol, rtol=0)
+    np.testing.assert_allclose(lse, lse_ref, atol=tol, rtol=0)
+
+
+# ----------------------------------------------------------------------------
+# routing
+
+def test_route_integer_scores_exact():
+    """Small integers make every fp32 product and sum exact, so the ranking
+    equals numpy's stable sort of the exact integer dot products (ties to the
+    lower index)."""
+    rng = np.random.default_rng(1)
+    H, n, K, dg = 3, 400, 8, 16
+    r = rng.integers(-2, 3, (H, n, dg)).astype(np.float32)
+    c = rng.integers(-2, 3, (H, K, dg)).astype(np.float32)
+    exact = np.einsum("hnd,hkd->hnk", r.astype(np.int64), c.astype(np.int64))
+    for topk in (1, 2, 3, 8):
+        groups, gmask = oracle.route(r, c, topk)
+        want = np.argsort(-exact, axis=-1, kind="stable")[..., :topk]
+        np.testing.assert_array_equal(groups, want)
+        bits = np.zeros((H, n), np.uint32)
+        for s in range(topk):
+            bits |= (np.uint32(1) << want[..., s].astype(np.uint32))
+        np.testing.assert_array_equal(gmask, bits)
+    # many ties must exist for the tie rule to be exercised
+    assert (np.sort(exact, -1)[..., -1] == np.sort(exact, -1)[..., -2]).mean() > 0.03
+
+
+def test_route_golden_rounding_cases():
+    fx = json.loads((GOLDEN / "route_fixed_order.json").read_text())
+    for case in fx["cases"]:
+        r = np.array([[[float.fromhex(x) for x in case["r"]]]], np.float32)
+        c = np.array([[[float.fromhex(x) for x in row] for row in case["centroids"]]],
+                     np.float32)
+        groups, _ = oracle.route(r, c, case["topk"])
+        assert groups[0, 0].tolist() == case["expected_groups"], case["name"]
+
+
+def test_route_closed_forms():
+    rng = np.random.default_rng(2)
+    H, n, K = 2, 64, 6
+    c = rng.standard_normal((H, K, 16)).astype(np.float32)
+    # r = 0: every score is +-0, so the first k indices in order
+    g, _ = oracle.route(np.zeros((H, n, 16), np.float32), c, 3)
+    assert (g == np.array([0, 1, 2])).all()
+    # K = 1: the only group
+    g, m = oracle.route(rng.standard_normal((H, n, 16)).astype(np.float32), c[:, :1], 1)
+    assert (g == 0).all() and (m == 1).all()
+    # k = K: every group, each exactly once
+    g, m = oracle.route(rng.standard_normal((H, n, 16)).astype(np.float32), c, K)
+    assert (np.sort(g, -1) == np.arange(K)).all() and (m == (1 << K) - 1).all()
+    # duplicated centroids a < b: a is listed before b whenever both are kept
+    cd = c.copy()
+    cd[:, 4] = cd[:, 1]
+    r = rng.standard_normal((H, n, 16)).astype(np.float32)
+    g, _ = oracle.route(r, cd, K)
+    pos1 = np.argmax(g == 1, axis=-1)
+    pos4 = np.argmax(g == 4, axis=-1)
+    assert (pos1 + 1 == pos4).all()
+
+
+def test_route_recovers_cluster_labels():
+    """Clustered routing vectors (noise 0.3 around unit centroids): the top-1
+    group is the generating cluster for the large majority of tokens; a
+    negated or transposed score would fail this."""
+    wl = Workload("t", 4096, 2, 2, 64, 4, 1, 64, "f32")
+    c, r, z = routing_inputs(wl, 7)
+    g, _ = oracle.route(r, c, 1)
+    assert (g[..., 0] == z).mean() > 0.9
+
+
+# ----------------------------------------------------------------------------
+# bucketing: properties that together determine the output uniquely
+
+def _partner(gt, g, K):
+    others = [x for x in gt if x != g]
+    return min(others) if others else K
+
+
+@pytest.mark.parametrize("K,topk,n", [(4, 1, 300), (4, 2, 500), (8, 3, 257), (5, 5, 64),
+                                      (1, 1, 33)])
+def test_bucket_properties(K, topk, n):
+    rng = np.random.default_rng(K * 100 + topk)
+    H = 3
+    r = rng.standard_normal((H, n, 16)).astype(np.float32)
+    c = rng.standard_normal((H, K, 16)).astype(np.float32)
+    groups, _ = oracle.route(r, c, topk)
+    offsets, tokens, slot_entry = oracle.bucket(groups, K)
+    nsb = K * (K + 1)
+    for h in range(H):
+        off = offsets[h]
+        assert off[0] == 0 and off[nsb] == n * topk
+        assert (np.diff(off) >= 0).all()
+        seen = np.zeros(n, np.int64)
+        for sb in range(nsb):
+            g, m = divmod(sb, K + 1)
+            toks = tokens[h, off[sb]:off[sb + 1]]
+            assert (np.diff(toks) > 0).all()          # ascending positions
+            for t in toks:
+                gt = groups[h, t].tolist()
+                assert g in gt and _partner(gt, g, K) == m
+            seen[toks] += 1
+        assert (seen == topk).all()                   # each token k times
+        for t in range(n):
+            for s in range(topk):
+                e = slot_entry[h, t, s]
+                g = groups[h, t, s]
+                sb = g * (K + 1) + _partner(groups[h, t].tolist(), g, K)
+                assert tokens[h, e] == t and off[sb] <= e < off[sb + 1]
+
+
+# ----------------------------------------------------------------------------
+# attention: special cases that reduce to textbook causal attention
+
+def _random_groups(rng, H, n, K, topk):
+    r = rng.standard_normal((H, n, 16)).astype(np.float32)
+    c = rng.standard_normal((H, K, 16)).astype(np.float32)
+    return oracle.route(r, c, topk)[0]
+
+
+def _run(q, k, v, groups, K, w, scale):
+    return oracle.attn_full(q, k, v, groups, K, w, scale)
+
+
+@pytest.mark.parametrize("case", ["K1", "window_ge_n", "topk_majority", "same_sets"])
+def test_attn_reduces_to_dense_causal(case):
+    rng = np.random.default_rng(hash(case) % 2**32)
+    hq, hkv, n, d = 4, 2, 150, 32
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    scale = 1 / math.sqrt(d)
+    if case == "K1":
+        K, w, groups = 1, 7, np.zeros((hkv, n, 1), np.int32)
+    elif case == "window_ge_n":
+        K, w, groups = 4, n, _random_groups(rng, hkv, n, 4, 1)
+    elif case == "topk_majority":       # two 3-subsets of 4 groups always meet
+        K, w, groups = 4, 3, _random_groups(rng, hkv, n, 4, 3)
+    else:                               # every token in {0, 1}
+        K, w = 4, 5
+        groups = np.tile(np.array([1, 0], np.int32), (hkv, n, 1))
+    o, lse, cnt = _run(q, k, v, groups, K, w, scale)
+    o_ref, lse_ref = _library_attention(q, k, v, scale, causal=True)
+    _assert_close(o, lse, o_ref, lse_ref)
+    assert (cnt == np.arange(1, n + 1)).all()
+
+
+def test_attn_w1_top1_is_causal_within_each_group():
+    """w = 1 and top-1: token i sees exactly the earlier tokens of its own
+    group, i.e. textbook causal attention over that group's subsequence."""
+    rng = np.random.default_rng(11)
+    hq, hkv, n, d, K = 4, 2, 200, 16, 4
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    groups = _random_groups(rng, hkv, n, K, 1)
+    scale = 0.37
+    o, lse, _ = _run(q, k, v, groups, K, 1, scale)
+    for h in range(hq):
+        hk = h // (hq // hkv)
+        for g in range(K):
+            idx = np.nonzero(groups[hk, :, 0] == g)[0]
+            if idx.size == 0:
+                continue
+            o_ref, lse_ref = _library_attention(q[h:h + 1, idx], k[hk:hk + 1, idx],
+                                                v[hk:hk + 1, idx], scale, causal=True)
+            _assert_close(o[h, idx], lse[h, idx], o_ref[0], lse_ref[0])
+
+
+def test_attn_brute_force_mask_small():
+    """Random top-2 routing, small n: the oracle equals library softmax under
+    an explicit n x n boolean mask of the attended set."""
+    rng = np.random.default_rng(12)
+    hq, hkv, n, d, K, w = 2, 1, 96, 16, 4, 5
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    groups = _random_groups(rng, hkv, n, K, 2)
+    gm = np.zeros((hkv, n), np.int64)
+    for s in range(2):
+        gm |= 1 << groups[..., s].astype(np.int64)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    mask = (j <= i) & (((i - j) < w) | ((gm[0][:, None] & gm[0][None, :]) != 0))
+    o, lse, cnt = _run(q, k, v, groups, K, w, 0.25)
+    o_ref, lse_ref = _library_attention(q, k, v, 0.25, mask=np.broadcast_to(mask, (hq, n, n)))
+    _assert_close(o, lse, o_ref, lse_ref)
+    assert (cnt[0] == mask.sum(1)).all()
+    # some far pairs are dropped, so this is not dense attention
+    assert mask.sum() < n * (n + 1) // 2
+
+
+# ----------------------------------------------------------------------------
+# closed-form set sizes (q = 0 makes every logit 0: exp(LSE) = |A(i)| and the
+# output is the mean of v over A(i))
+
+def _rr_far_count(i, w, K, residues):
+    total = 0
+    for rho in residues:
+        x = i - w - ((i - rho) % K)
+        total += max(0, x // K + 1)
+    return total
+
+
+@pytest.mark.parametrize("K,w,topk", [(4, 8, 1), (3, 1, 1), (4, 6, 2), (5, 3, 2), (4, 0, 1)])
+def test_counts_round_robin_closed_form(K, w, topk):
+    n, d = 300, 8
+    t = np.arange(n)
+    if topk == 1:
+        groups = (t % K).astype(np.int32)[None, :, None]
+        residues = [0]
+    else:                       # {t mod K, t+1 mod K} meets {j mod K, ...} iff (i-j) mod K in {0, 1, K-1}
+        groups = np.stack([t % K, (t + 1) % K], -1).astype(np.int32)[None]
+        residues = sorted({0, 1, K - 1})
+    want = np.array([min(i + 1, w) + _rr_far_count(i, w, K, residues) if w > 0
+                     else _rr_far_count(i, 0, K, residues) for i in range(n)])
+    np.testing.assert_array_equal(oracle.pair_counts(groups, K, w)[0], want)
+    rng = np.random.default_rng(13)
+    q = np.zeros((1, n, d), np.float32)
+    k = rng.standard_normal((1, n, d)).astype(np.float32)
+    v = rng.standard_normal((1, n, d)).astype(np.float32)
+    o, lse, cnt = _run(q, k, v, groups, K, w, 0.5)
+    np.testing.assert_array_equal(cnt[0], want)
+    np.testing.assert_allclose(np.exp(lse[0]), want, rtol=1e-12)
+    for i in (0, 1, w, w + 1, 97, n - 1):
+        if i >= n:
+            continue
+        js = [j for j in range(i + 1) if i - j < w or (i - j) % K in residues]
+        np.testing.assert_allclose(o[0, i], v[0, js].astype(np.float64).mean(0), atol=1e-12)
+
+
+def test_pair_counts_brute_force_and_dense():
+    rng = np.random.default_rng(14)
+    H, n, K = 2, 180, 5
+    for topk, w in ((1, 4), (2, 9), (3, 1), (2, 0)):
+        groups = _random_groups(rng, H, n, K, topk)
+        gm = np.zeros((H, n), np.int64)
+        for s in range(topk):
+            gm |= 1 << groups[..., s].astype(np.int64)
+        got = oracle.pair_counts(groups, K, w)
+        i = np.arange(n)[:, None]
+        j = np.arange(n)[None, :]
+        for h in range(H):
+            mask = (j <= i) & (((i - j) < w) | ((gm[h][:, None] & gm[h][None, :]) != 0))
+            np.testing.assert_array_equal(got[h], mask.sum(1))
+    groups = _random_groups(rng, 1, n, K, 1)
+    assert oracle.pair_counts(groups, K, n)[0].sum() == n * (n + 1) // 2
+
+
+def test_far_pairs_retained_top1_balanced():
+    """Table 7 (thelatestinai.com): top-1 of K=4 keeps about a quarter of the
+    pairs (26% / 25%); with balanced clustered routing the far-pair share is
+    about 1/K."""
+    wl = Workload("t", 8192, 1, 1, 64, 4, 1, 128, "f32")
+    c, r, _ = routing_inputs(wl, 21)
+    groups, _ = oracle.route(r, c, 1)
+    cnt = oracle.pair_counts(groups, wl.K, wl.window)[0].astype(np.float64)
+    i = np.arange(wl.n)
+    win = np.minimum(i + 1, wl.window)
+    far_all = np.maximum(0, i - wl.window + 1)
+    share = (cnt - win).sum() / far_all.sum()
+    assert 0.22 < share < 0.29
+
+
+def test_attn_rows_matches_full_rows():
+    rng = np.random.default_rng(15)
+    hq, hkv, n, d, K = 4, 2, 120, 16, 4
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    groups = _random_groups(rng, hkv, n, K, 2)
+    o, lse, cnt = _run(q, k, v, groups, K, 9, 0.3)
+    rh = np.array([0, 3, 1, 2, 2], np.int32)
+    rp = np.array([0, 119, 57, 8, 9], np.int64)
+    o2, lse2, cnt2 = oracle.attn_rows(q, k, v, groups, K, 9, 0.3, rh, rp)
+    np.testing.assert_array_equal(o2, o[rh, rp])
+    np.testing.assert_array_equal(lse2, lse[rh, rp])
+    np.testing.assert_array_equal(cnt2, cnt[rh, rp])
+
+
+def test_attn_bf16_inputs_widen_exactly():
+    """bf16 inputs given as bit patterns equal the same values given as fp32."""
+    rng = np.random.default_rng(16)
+    hq, hkv, n, d, K = 2, 2, 64, 16, 4
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    tb = [torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v)]
+    bits = [t.view(torch.int16).numpy().view(np.uint16) for t in tb]
+    f32 = [t.float().numpy() for t in tb]
+    groups = _random_groups(rng, hkv, n, K, 2)
+    a = _run(*bits, groups, K, 4, 0.25)
+    b = _run(*f32, groups, K, 4, 0.25)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
