@@ -1,0 +1,236 @@
+// Bucketing: the per-group token lists for within-group causal attention.
+//
+// The pages split the sparse pattern into a local-window call and a
+// within-group causal call (Technical Summary, Key Contributions 5) without
+// saying how tokens are gathered.  Here the n*topk (token, group) entries of
+// each routing head are counting-sorted, stably, by the key
+// sb = group * (K + 1) + partner, where the partner is the token's lowest
+// group other than this one (K at top-1).  Inside a sub-bucket positions
+// ascend, so "causal" in bucket order is causal in positions, and a tile of
+// one sub-bucket meets a tile of another with a single owner decision.
+//
+// Three kernels, all bound by HBM and integer only:
+//   count   one wavefront per chunk of kChunk tokens; LDS histogram per wave
+//   scan    one block per head: exclusive scan over (sub-bucket, chunk)
+//   scatter one wavefront per chunk; stable ranks from wavefront ballots
+#include "common.hpp"
+
+namespace focus {
+namespace {
+
+constexpr int kChunk = 512;              // tokens per wavefront chunk
+constexpr int kWavesPerBlock = 4;
+constexpr int kScanThreads = 1024;
+
+// Lowest and second-lowest group of token t (second = K at top-1).
+__device__ __forceinline__ void two_lowest(const int32_t *gt, int topk, int K, int &lo1,
+                                           int &lo2)
+{
+    lo1 = K;
+    lo2 = K;
+    for (int s = 0; s < topk; ++s) {
+        const int g = gt[s];
+        if (g < lo1) {
+            lo2 = lo1;
+            lo1 = g;
+        } else if (g < lo2) {
+            lo2 = g;
+        }
+    }
+}
+
+__device__ __forceinline__ int subbucket(int g, int lo1, int lo2, int K)
+{
+    const int partner = (g == lo1) ? lo2 : lo1;
+    return g * (K + 1) + partner;
+}
+
+// counts[h][sb][chunk]
+__global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t *__restrict__ groups,
+                                                           int64_t n, int K, int topk,
+                                                           int nchunks,
+                                                           int32_t *__restrict__ counts)
+{
+    extern __shared__ int32_t hist[];  // [kWavesPerBlock][nsb]
+    const int nsb = num_subbuckets(K);
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int h = blockIdx.y;
+    const int chunk = blockIdx.x * kWavesPerBlock + wave;
+    int32_t *my = hist + wave * nsb;
+    for (int i = lane; i < nsb; i += kWave)
+        my[i] = 0;
+    __syncthreads();
+    if (chunk < nchunks) {
+        const int32_t *gh = groups + (int64_t)h * n * topk;
+        const int64_t t0 = (int64_t)chunk * kChunk;
+        for (int64_t t = t0 + lane; t < t0 + kChunk && t < n; t += kWave) {
+            const int32_t *gt = gh + t * topk;
+            int lo1, lo2;
+            two_lowest(gt, topk, K, lo1, lo2);
+            for (int s = 0; s < topk; ++s)
+                atomicAdd(&my[subbucket(gt[s], lo1, lo2, K)], 1);
+        }
+    }
+    __syncthreads();
+    if (chunk < nchunks) {
+        int32_t *ch = counts + (int64_t)h * nsb * nchunks;
+        for (int i = lane; i < nsb; i += kWave)
+            ch[(int64_t)i * nchunks + chunk] = my[i];
+    }
+}
+
+// In place: counts[h][sb][chunk] -> exclusive prefix in (sb, chunk) order;
+// offsets[h][sb] = start of sub-bucket sb, offsets[h][nsb] = total.
+__global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(int32_t *__restrict__ counts,
+                                                                   int nsb, int nchunks,
+                                                                   int32_t *__restrict__ offsets)
+{
+    __shared__ int32_t partial[kScanThreads / kWave];
+    __shared__ int32_t carry_s;
+    const int h = blockIdx.x;
+    int32_t *c = counts + (int64_t)h * nsb * nchunks;
+    int32_t *off = offsets + (int64_t)h * (nsb + 1);
+    const int64_t total = (int64_t)nsb * nchunks;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    if (threadIdx.x == 0)
+        carry_s = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < total; base += kScanThreads) {
+        const int64_t i = base + threadIdx.x;
+        const int32_t x = i < total ? c[i] : 0;
+        // inclusive scan inside the wavefront
+        int32_t inc = x;
+#pragma unroll
+        for (int off_l = 1; off_l < kWave; off_l <<= 1) {
+            const int32_t y = __shfl_up(inc, off_l);
+            if (lane >= off_l)
+                inc += y;
+        }
+        if (lane == kWave - 1)
+            partial[wave] = inc;
+        __syncthreads();
+        int32_t wave_base = 0;
+        for (int w = 0; w < wave; ++w)
+            wave_base += partial[w];
+        const int32_t carry = carry_s;
+        const int32_t excl = carry + wave_base + inc - x;
+        if (i < total) {
+            c[i] = excl;
+            if (i % nchunks == 0)
+                off[i / nchunks] = excl;
+        }
+        __syncthreads();
+        if (threadIdx.x == kScanThreads - 1)
+            carry_s = excl + x;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        off[nsb] = carry_s;
+}
+
+__global__ __launch_bounds__(256) void bucket_scatter_kernel(
+    const int32_t *__restrict__ groups, int64_t n, int K, int topk, int nchunks,
+    const int32_t *__restrict__ bases, int32_t *__restrict__ tokens,
+    int32_t *__restrict__ slot_entry)
+{
+    extern __shared__ int32_t run[];  // [kWavesPerBlock][nsb] running cursor
+    const int nsb = num_subbuckets(K);
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int h = blockIdx.y;
+    const int chunk = blockIdx.x * kWavesPerBlock + wave;
+    if (chunk >= nchunks)
+        return;  // whole wavefront leaves together; no block barrier below
+    int32_t *my = run + wave * nsb;
+    const int32_t *bh = bases + (int64_t)h * nsb * nchunks;
+    for (int i = lane; i < nsb; i += kWave)
+        my[i] = bh[(int64_t)i * nchunks + chunk];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+
+    const int32_t *gh = groups + (int64_t)h * n * topk;
+    int32_t *th = tokens + (int64_t)h * n * topk;
+    int32_t *sh = slot_entry + (int64_t)h * n * topk;
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int64_t t0 = (int64_t)chunk * kChunk;
+    for (int64_t tb = t0; tb < t0 + kChunk && tb < n; tb += kWave) {
+        const int64_t t = tb + lane;
+        const bool valid = t < n;
+        const int32_t *gt = gh + (valid ? t : tb) * topk;
+        int lo1 = K, lo2 = K;
+        if (valid)
+            two_lowest(gt, topk, K, lo1, lo2);
+        uint32_t pending = valid ? (topk >= 32 ? ~0u : ((1u << topk) - 1u)) : 0u;
+        // Each pass settles one sub-bucket key X: every lane holding an entry
+        // with key X takes rank (cursor[X] + number of lower lanes holding X).
+        // A token has at most one entry per key, so lane order is token order.
+        while (true) {
+            const uint64_t any = __ballot(pending != 0);
+            if (any == 0)
+                break;
+            const int leader = __ffsll((unsigned long long)any) - 1;
+            int my_key = -1;
+            if (pending != 0) {
+                const int s = __ffs(pending) - 1;
+                my_key = subbucket(gt[s], lo1, lo2, K);
+            }
+            const int X = __shfl(my_key, leader);
+            int sx = -1;
+            for (uint32_t p = pending; p != 0; p &= p - 1) {
+                const int s = __ffs(p) - 1;
+                if (subbucket(gt[s], lo1, lo2, K) == X)
+                    sx = s;
+            }
+            const uint64_t members = __ballot(sx >= 0);
+            const int32_t cursor = my[X];
+            if (sx >= 0) {
+                const int32_t e = cursor + __popcll(members & lanes_below);
+                th[e] = (int32_t)t;
+                sh[t * topk + sx] = e;
+                pending &= ~(1u << sx);
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (lane == leader)
+                my[X] = cursor + __popcll(members);
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        }
+    }
+}
+
+}  // namespace
+
+size_t bucket_workspace_bytes(int H, int64_t n, int K, int topk)
+{
+    (void)topk;
+    const int64_t nchunks = (n + kChunk - 1) / kChunk;
+    return align_up((size_t)H * num_subbuckets(K) * nchunks * sizeof(int32_t), 256);
+}
+
+hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int topk,
+                         int32_t *offsets, int32_t *tokens, int32_t *slot_entry, void *ws,
+                         hipStream_t s)
+{
+    const int nsb = num_subbuckets(K);
+    const int nchunks = (int)((n + kChunk - 1) / kChunk);
+    int32_t *counts = static_cast<int32_t *>(ws);
+    const dim3 grid((nchunks + kWavesPerBlock - 1) / kWavesPerBlock, H);
+    const size_t lds = sizeof(int32_t) * nsb * kWavesPerBlock;
+    hipLaunchKernelGGL(bucket_count_kernel, grid, dim3(kWave * kWavesPerBlock), lds, s,
+                       groups, n, K, topk, nchunks, counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(bucket_scan_kernel, dim3(H), dim3(kScanThreads), 0, s, counts, nsb,
+                       nchunks, offsets);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(bucket_scatter_kernel, grid, dim3(kWave * kWavesPerBlock), lds, s,
+                       groups, n, K, topk, nchunks, counts, tokens, slot_entry);
+    return hipGetLastError();
+}
+
+}  // namespace focus

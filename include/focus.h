@@ -1,0 +1,186 @@
+/*
+ * focus.h — C ABI of the Focus attention forward path on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Focus ("Why Attend to Everything? Focus is the Key", arXiv 2604.03260):
+ * each token is routed to the top-k of K learnable centroids by dot products
+ * of a 16-dimensional routing vector (gist.science Technical Summary,
+ * section 2, Learnable Centroids / Token Grouping / Inference Efficiency
+ * (Top-k); jindou-blog method bullets).  Query i then attends with exact
+ * softmax to the set
+ *     A(i) = { j <= i : i - j < w  or  G(i) and G(j) share a group }
+ * (Technical Summary, Gated Attention: Local Attention and Distant
+ * Attention).  The pages compute this with two library attention calls (a
+ * local-window call and a within-group causal call; Technical Summary,
+ * Key Contributions 5); this library computes the same set with its own
+ * kernels: route, bucket, gathered group attention, window attention and a
+ * log-sum-exp merge.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers owned by the caller, contiguous, at least
+ *    16-byte aligned.  The library keeps no pointer after a call returns and
+ *    allocates no device memory; scratch space is a caller-provided
+ *    workspace whose size the *_workspace_bytes queries return.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    legacy default stream).  Arguments are validated on the host before
+ *    anything is enqueued; on any error nothing is launched.  A fault inside
+ *    a kernel is reported by the caller's next synchronisation.
+ *  - Batch folds into heads: every head is an independent sequence.
+ *  - Routing is per key/value head (H_r == Hkv); query head h uses
+ *    key/value head h / (Hq / Hkv) and that head's routing.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef FOCUS_H
+#define FOCUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FOCUS_OK = 0,
+    FOCUS_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or range */
+    FOCUS_ERR_UNSUPPORTED = 2,      /* d not in {64,128}, d_g != 16, K > 32     */
+    FOCUS_ERR_WORKSPACE = 3,        /* workspace null or smaller than required  */
+    FOCUS_ERR_HIP = 4               /* a launch or runtime call failed          */
+} focus_status;
+
+typedef enum { FOCUS_F32 = 0, FOCUS_BF16 = 1 } focus_dtype;
+
+typedef void *focus_stream; /* hipStream_t */
+
+/* Parts of focus_attn_fwd, for callers that time or schedule them apart. */
+typedef enum {
+    FOCUS_PART_PREPARE = 1, /* gather keys/values into bucket order, plan tiles */
+    FOCUS_PART_GROUP = 2,   /* gathered within-group causal attention -> partials */
+    FOCUS_PART_WINDOW = 4,  /* sliding-window attention + log-sum-exp merge -> out */
+    FOCUS_PART_ALL = 7
+} focus_part;
+
+/* Human-readable name of a status; never NULL. */
+const char *focus_status_string(focus_status s);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char *focus_last_error(void);
+
+/* ABI revision of this header (incremented on any incompatible change). */
+int32_t focus_abi_version(void);
+
+/*
+ * focus_route — centroid scores and top-k group membership.
+ * Technical Summary, Token Grouping (projected state compared with each
+ * centroid) and Inference Efficiency (Top-k) (each token joins its k
+ * highest-scoring groups); jindou-blog: K centroids per layer, 16-d routing,
+ * dot-product assignment.
+ *
+ *   r          fp32 [H, n, d_g]   routing vectors (d_g must be 16)
+ *   centroids  fp32 [H, K, d_g]   centroids of each routing head
+ *   groups     int32 [H, n, topk] out: group ids, by score descending and,
+ *                                 on equal scores, by ascending index
+ *   gmask      uint32 [H, n]      out: bit g set iff g is among the groups
+ * Scores are fp32 products accumulated in index order 0..15 with no fused
+ * multiply-add, so the result is bit-reproducible on any IEEE machine.
+ * Errors: INVALID_ARGUMENT for n < 1, H < 1, K < 1, topk not in [1, K];
+ * UNSUPPORTED for d_g != 16 or K > 32.
+ */
+focus_status focus_route(const float *r, const float *centroids, int32_t H, int64_t n,
+                         int32_t d_g, int32_t K, int32_t topk, int32_t *groups,
+                         uint32_t *gmask, focus_stream stream);
+
+/*
+ * focus_bucket — per-head bucketing of the n*topk (token, group) entries for
+ * within-group causal attention (Technical Summary, Key Contributions 5:
+ * the sparse pattern splits into a local-window call and a within-group
+ * causal call; the pages leave the gathering itself open).
+ *
+ * A stable counting sort of the entries of each head by the key
+ * (group g, partner p), where the partner of token t in group g is its
+ * lowest group other than g (K when topk == 1).  Inside a (g, p)
+ * sub-bucket positions ascend.  Sub-bucket sb = g * (K + 1) + p.
+ *
+ *   groups      int32 [H, n, topk]      from focus_route
+ *   offsets     int32 [H, K*(K+1)+1]    out: first entry of each sub-bucket;
+ *                                        offsets[h][K*(K+1)] = n * topk
+ *   tokens      int32 [H, n*topk]       out: position of each entry
+ *   slot_entry  int32 [H, n, topk]      out: entry index of (t, groups[t][s])
+ *   workspace   >= focus_bucket_workspace_bytes(...) bytes of device memory
+ * Errors: INVALID_ARGUMENT for bad sizes or n*topk > INT32_MAX; UNSUPPORTED
+ * for K > 32; WORKSPACE if the workspace is missing or short.  Group ids
+ * outside [0, K) or repeated ids in a token's list are undefined input.
+ */
+size_t focus_bucket_workspace_bytes(int32_t H, int64_t n, int32_t K, int32_t topk);
+focus_status focus_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
+                          int32_t topk, int32_t *offsets, int32_t *tokens,
+                          int32_t *slot_entry, void *workspace, size_t workspace_bytes,
+                          focus_stream stream);
+
+/*
+ * focus_attn_fwd — exact softmax over A(i) for every query head and row
+ * (Technical Summary, Gated Attention: local window with exact softmax;
+ * distant tokens only when they share a group; Inference Efficiency
+ * (Top-k): sharing any one of the top-k groups suffices).
+ *
+ * Each surviving pair is evaluated exactly once: pairs with i - j < w by the
+ * window kernel, the others by the group kernel of the lowest group the two
+ * tokens share; the parts are joined by a log-sum-exp merge.
+ *
+ *   q           [Hq, n, d]  in dt (FOCUS_BF16 or FOCUS_F32)
+ *   k, v        [Hkv, n, d] in dt
+ *   gmask       uint32 [Hkv, n]  from focus_route
+ *   offsets, tokens, slot_entry  from focus_bucket (same groups)
+ *   window      w >= 0; w = 0 keeps only group pairs (a token always shares
+ *               its own groups, so every row keeps itself); w >= n is dense
+ *               causal attention
+ *   scale       logit scale (1/sqrt(d) for standard attention)
+ *   out         [Hq, n, d] in dt: softmax-weighted values, bf16 rounded to
+ *               nearest even
+ *   lse         fp32 [Hq, n]: natural log of sum_j exp(scale * q_i . k_j)
+ *   workspace   >= focus_attn_workspace_bytes(...) bytes
+ * Errors: INVALID_ARGUMENT for null pointers, n < 1, Hq % Hkv != 0,
+ * topk not in [1, K], window < 0, n*topk > INT32_MAX; UNSUPPORTED for
+ * d not in {64, 128} or K > 32; WORKSPACE if short.  Buckets that were not
+ * built from the routing that produced gmask are undefined input.
+ *
+ * focus_attn_fwd_part runs a subset of the same work (a focus_part bitmask);
+ * the parts must run in the order PREPARE, GROUP, WINDOW on the same
+ * workspace, and focus_attn_fwd equals focus_attn_fwd_part(..., FOCUS_PART_ALL).
+ */
+size_t focus_attn_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
+                                  int32_t d, int32_t K, int32_t topk);
+focus_status focus_attn_fwd(const void *q, const void *k, const void *v, focus_dtype dt,
+                            int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
+                            const uint32_t *gmask, const int32_t *offsets,
+                            const int32_t *tokens, const int32_t *slot_entry, int32_t K,
+                            int32_t topk, int64_t window, float scale, void *out,
+                            float *lse, void *workspace, size_t workspace_bytes,
+                            focus_stream stream);
+focus_status focus_attn_fwd_part(const void *q, const void *k, const void *v,
+                                 focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
+                                 int32_t d, const uint32_t *gmask, const int32_t *offsets,
+                                 const int32_t *tokens, const int32_t *slot_entry,
+                                 int32_t K, int32_t topk, int64_t window, float scale,
+                                 void *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, int32_t parts,
+                                 focus_stream stream);
+
+/*
+ * focus_dense_causal_fwd — plain causal attention (every j <= i) with the
+ * same window kernel and layouts; the dense baseline that Focus is compared
+ * against (thelatestinai.com Table 6 compares against full attention).
+ * Not part of the method.  Arguments as in focus_attn_fwd.
+ */
+size_t focus_dense_workspace_bytes(focus_dtype dt, int32_t Hkv, int64_t n, int32_t d);
+focus_status focus_dense_causal_fwd(const void *q, const void *k, const void *v,
+                                    focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
+                                    int32_t d, float scale, void *out, float *lse,
+                                    void *workspace, size_t workspace_bytes,
+                                    focus_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOCUS_H */

@@ -58,7 +58,7 @@ def _load():
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.oracle_route.argtypes = [P, P, i32, i64, i32, i32, i32, P, P]
     lib.oracle_bucket.argtypes = [P, i32, i64, i32, i32, P, P, P]
-    lib.oracle_attn_rows.argtypes = [P, P, P, i32, i32, i32, i64, i32, P, i32, i32,
+    lib.oracle_attn_rows.argtypes = [P, i32, P, P, i32, i32, i32, i64, i32, P, i32, i32,
                                      i64, f64, P, P, i64, P, P, P, i32]
     lib.oracle_pair_counts.argtypes = [P, i32, i64, i32, i32, i64, P]
     for f in (lib.oracle_route, lib.oracle_bucket, lib.oracle_attn_rows,
@@ -124,19 +124,27 @@ def _as_raw(x) -> tuple[np.ndarray, int]:
 
 
 def attn_rows(q, k, v, groups: np.ndarray, K: int, window: int, scale: float,
-              row_head: np.ndarray, row_pos: np.ndarray, nthreads: int = 0):
+              row_head: np.ndarray, row_pos: np.ndarray, nthreads: int = 0,
+              num_q_heads: int | None = None):
     """Exact softmax over A(i) for the listed (query head, row) pairs.
 
-    q: [Hq, n, d]; k, v: [Hkv, n, d] (float32, or uint16 holding bf16 bits);
-    groups: int32 [Hkv, n, topk].
+    q: [Hq, n, d], or [rows, d] holding just the listed rows' queries (then
+    pass num_q_heads); k, v: [Hkv, n, d] (float32, or uint16 holding bf16
+    bits); groups: int32 [Hkv, n, topk].
     Returns (o float64 [rows, d], lse float64 [rows], count int64 [rows]).
     """
     qa, qb = _as_raw(q)
     ka, kb = _as_raw(k)
     va, vb = _as_raw(v)
     assert qb == kb == vb
-    Hq, n, d = qa.shape
-    Hkv = ka.shape[0]
+    Hkv, n, d = ka.shape
+    q_per_row = qa.ndim == 2
+    if q_per_row:
+        assert num_q_heads is not None and qa.shape == (len(row_head), d)
+        Hq = int(num_q_heads)
+    else:
+        Hq = qa.shape[0]
+        assert qa.shape == (Hq, n, d)
     assert ka.shape == (Hkv, n, d) and va.shape == (Hkv, n, d)
     groups = np.ascontiguousarray(groups, dtype=np.int32)
     assert groups.shape[:2] == (Hkv, n)
@@ -147,7 +155,8 @@ def attn_rows(q, k, v, groups: np.ndarray, K: int, window: int, scale: float,
     o = np.empty((nrows, d), np.float64)
     lse = np.empty(nrows, np.float64)
     cnt = np.empty(nrows, np.int64)
-    _check(_load().oracle_attn_rows(_ptr(qa), _ptr(ka), _ptr(va), qb, Hq, Hkv, n, d,
+    _check(_load().oracle_attn_rows(_ptr(qa), int(q_per_row), _ptr(ka), _ptr(va), qb, Hq,
+                                    Hkv, n, d,
                                     _ptr(groups), K, topk, int(window), float(scale),
                                     _ptr(rh), _ptr(rp), nrows, _ptr(o), _ptr(lse),
                                     _ptr(cnt), int(nthreads)), "attn_rows")

@@ -192,10 +192,12 @@ static double widen(const void *base, int is_bf16, int64_t idx)
  * only when they share a group; Inference Efficiency (Top-k): sharing at
  * least one of the top-k groups is enough).  Evaluates the listed (head, row)
  * pairs.  Query head h reads key/value head h / (Hq/Hkv) and the routing of
- * that key/value head.  Outputs: o[row][d] (double), lse[row] (natural log of
- * the softmax denominator of the scaled scores), count[row] = |A(i)|. */
-int oracle_attn_rows(const void *q, const void *k, const void *v, int32_t is_bf16,
-                     int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
+ * that key/value head.  q is [Hq, n, d], or [nrows, d] (the query of each
+ * listed row) when q_per_row is set.  Outputs: o[row][d] (double), lse[row]
+ * (natural log of the softmax denominator of the scaled scores),
+ * count[row] = |A(i)|. */
+int oracle_attn_rows(const void *q, int32_t q_per_row, const void *k, const void *v,
+                     int32_t is_bf16, int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
                      const int32_t *groups, int32_t K, int32_t topk, int64_t w,
                      double scale, const int32_t *row_head, const int64_t *row_pos,
                      int64_t nrows, double *o, double *lse, int64_t *count,
@@ -238,8 +240,9 @@ int oracle_attn_rows(const void *q, const void *k, const void *v, int32_t is_bf1
             const int64_t i = row_pos[r];
             const int hk = h / ratio;
             const uint32_t *bk = bits + (int64_t)hk * n;
+            const int64_t qb = q_per_row ? r * d : ((int64_t)h * n + i) * d;
             for (int e = 0; e < d; ++e)
-                qi[e] = widen(q, is_bf16, ((int64_t)h * n + i) * d + e);
+                qi[e] = widen(q, is_bf16, qb + e);
             /* pass 1: scores of the attended keys and their maximum */
             double mx = -INFINITY;
             int64_t cnt = 0;

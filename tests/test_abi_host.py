@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/focus.h declares, and rejects bad arguments before
+anything is launched."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from centroid_gated_sparse_amd import focus as F
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = (ROOT / "include" / "focus.h").read_text()
+
+
+def declared_functions():
+    body = re.sub(r"/\*.*?\*/", "", HEADER, flags=re.S)
+    return sorted(set(re.findall(r"\b(focus_[a-z0-9_]+)\s*\(", body)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not F.LIB_PATH.exists():
+        from centroid_gated_sparse_amd.build import build
+        build()
+    return F.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 11
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(F.SYMBOLS)
+
+
+def test_status_strings_and_version(L):
+    assert L.focus_abi_version() == 1
+    for code, text in [(0, "FOCUS_OK"), (1, "FOCUS_ERR_INVALID_ARGUMENT"),
+                       (2, "FOCUS_ERR_UNSUPPORTED"), (3, "FOCUS_ERR_WORKSPACE"),
+                       (4, "FOCUS_ERR_HIP"), (99, "FOCUS_ERR_UNKNOWN")]:
+        assert F.status_string(code) == text
+
+
+def test_workspace_sizes(L):
+    # bucket: one int per (head, sub-bucket, 512-token chunk)
+    assert F.focus_bucket_workspace_bytes(8, 1 << 20, 8, 2) == 8 * 72 * 2048 * 4
+    assert F.focus_bucket_workspace_bytes(1, 10, 0, 1) == 0
+    # attention: at least the fp32 partials of every (query head, entry)
+    n, hq, hkv, d, K, k = 131072, 32, 8, 128, 4, 2
+    ws = F.focus_attn_workspace_bytes(F.FOCUS_BF16, hq, hkv, n, d, K, k)
+    assert ws >= hq * n * k * (d + 1) * 4
+    assert ws < 2 * hq * n * k * (d + 1) * 4 + 4 * hkv * n * k * d * 2
+    assert F.focus_attn_workspace_bytes(F.FOCUS_BF16, hq, hkv, n, 96, K, k) == 0
+    assert F.focus_attn_workspace_bytes(F.FOCUS_BF16, 6, 4, n, d, K, k) == 0
+    assert F.focus_dense_workspace_bytes(F.FOCUS_F32, 2, 512, 64) > 0
+
+
+# An aligned non-null address.  Every call below carries at least one invalid
+# argument, so the library returns before launching anything.  As a guard
+# against a validation regression turning one of them into a launch on a fake
+# address, these tests only run where no GPU is visible.
+FAKE = 1 << 20
+no_gpu = pytest.mark.skipif(
+    __import__("conftest").gpu_available(),
+    reason="fake-pointer validation tests run only where no GPU is visible")
+
+
+@no_gpu
+def test_route_rejects_bad_arguments(L):
+    call = lambda *a: L.focus_route(*a)
+    ok = (FAKE, FAKE, 2, 100, 16, 4, 2, FAKE, FAKE, None)
+    assert call(None, *ok[1:]) == 1
+    assert call(FAKE + 4, *ok[1:]) == 1            # misaligned
+    assert call(*ok[:4], 8, *ok[5:]) == 2          # d_g != 16
+    assert call(*ok[:5], 33, 2, *ok[7:]) == 2      # K > 32
+    assert call(*ok[:5], 4, 5, *ok[7:]) == 1       # topk > K
+    assert call(*ok[:3], 0, *ok[4:]) == 1          # n < 1
+    assert call(*ok[:5], 4, 0, *ok[7:]) == 1       # topk < 1
+    assert b"topk" in L.focus_last_error()
+
+
+@no_gpu
+def test_bucket_rejects_bad_arguments(L):
+    ok = [FAKE, 2, 100, 4, 2, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    bad = list(ok); bad[8] = None
+    assert L.focus_bucket(*bad) == 3               # missing workspace
+    bad = list(ok); bad[9] = 16
+    assert L.focus_bucket(*bad) == 3               # short workspace
+    bad = list(ok); bad[2] = 1 << 31
+    assert L.focus_bucket(*bad) == 1               # n * topk > INT32_MAX
+    bad = list(ok); bad[3] = 40
+    assert L.focus_bucket(*bad) == 2
+
+
+def _attn_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dt=F.FOCUS_BF16, Hq=8, Hkv=2, n=256, d=128, gmask=FAKE,
+             offsets=FAKE, tokens=FAKE, slot=FAKE, K=4, topk=2, window=16, scale=0.088,
+             out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 40, parts=7, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@no_gpu
+def test_attn_rejects_bad_arguments(L):
+    f = L.focus_attn_fwd_part
+    assert f(*_attn_args(Hq=7)) == 1               # Hq % Hkv
+    assert f(*_attn_args(d=96)) == 2
+    assert f(*_attn_args(window=-1)) == 1
+    assert f(*_attn_args(topk=5)) == 1
+    assert f(*_attn_args(K=33, topk=2)) == 2
+    assert f(*_attn_args(q=None)) == 1
+    assert f(*_attn_args(out=FAKE + 8)) == 1
+    assert f(*_attn_args(wsb=64)) == 3
+    assert f(*_attn_args(parts=0)) == 1
+    assert f(*_attn_args(parts=8)) == 1
+    assert f(*_attn_args(scale=0.0)) == 1
+    assert f(*_attn_args(dt=5)) == 1
+    d = L.focus_dense_causal_fwd
+    assert d(FAKE, FAKE, FAKE, 1, 8, 3, 256, 128, 0.1, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert d(FAKE, FAKE, FAKE, 1, 8, 2, 256, 64, 0.1, FAKE, FAKE, None, 0, None) == 3
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(F, "_lib", None)
+    monkeypatch.setattr(F, "LIB_PATH", tmp_path / "missing.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        F.lib()

@@ -1,0 +1,228 @@
+"""GPU parity: libfocus.so (through the C ABI binding) against the CPU oracle
+on the same seeded inputs.
+
+Bars: group ids and every bucket array bit-exact; attention outputs within
+max-abs 2e-2 (bf16 I/O) or 1e-4 (fp32 I/O), LSE within 1e-3; with q = 0 every
+logit is 0, so exp(LSE_i) must equal the oracle's exact |A(i)| (relative
+1e-5: one missing 64-key tile moves it by >= 64/|A(i)|).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from centroid_gated_sparse_amd import focus as F
+from centroid_gated_sparse_amd.workloads import (WORKLOADS, Workload, qkv_inputs,
+                                                 routing_inputs, sample_rows, seed_for,
+                                                 to_bf16_bits)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+O_TOL = {"f32": 1e-4, "bf16": 2e-2}
+LSE_TOL = 1e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def oracle_view(t):
+    if t.dtype == torch.bfloat16:
+        return to_bf16_bits(t)
+    return t.detach().cpu().contiguous().numpy()
+
+
+def gpu_forward(wl, c, r, q, k, v, window=None):
+    rt = torch.from_numpy(r).to(DEV)
+    ct = torch.from_numpy(c).to(DEV)
+    res = F.focus_forward(q, k, v, rt, ct, wl.topk, wl.window if window is None else window,
+                          wl.scale)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_rows(wl, res, q, k, v, groups_np, rh, rp, tag):
+    o_ref, lse_ref, cnt = oracle.attn_rows(oracle_view(q), oracle_view(k), oracle_view(v),
+                                           groups_np, wl.K, wl.window, wl.scale, rh, rp)
+    out = res["out"].float()[torch.from_numpy(rh).long().to(DEV),
+                             torch.from_numpy(rp).long().to(DEV)].cpu().double().numpy()
+    lse = res["lse"][torch.from_numpy(rh).long().to(DEV),
+                     torch.from_numpy(rp).long().to(DEV)].cpu().double().numpy()
+    err_o = np.abs(out - o_ref).max()
+    err_l = np.abs(lse - lse_ref).max()
+    rel_o = err_o / max(np.abs(o_ref).max(), 1e-30)
+    log(f"[{tag}] rows={len(rh)} max|dO|={err_o:.3e} (rel {rel_o:.3e}) max|dLSE|={err_l:.3e}")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert err_o <= O_TOL[wl.dtype], tag
+    assert err_l <= LSE_TOL, tag
+    return err_o, err_l
+
+
+# ----------------------------------------------------------------------------
+# routing and bucketing, bit-exact at every workload's full size
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_route_and_bucket_bitexact(name):
+    wl = WORKLOADS[name]
+    log(f"route/bucket {name}")
+    c, r, _ = routing_inputs(wl, seed_for(name))
+    g_ref, m_ref = oracle.route(r, c, wl.topk)
+    off_ref, tok_ref, se_ref = oracle.bucket(g_ref, wl.K)
+    groups, gmask = F.focus_route(torch.from_numpy(r).to(DEV), torch.from_numpy(c).to(DEV),
+                                  wl.topk)
+    offsets, tokens, slot_entry = F.focus_bucket(groups, wl.K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(groups.cpu().numpy(), g_ref)
+    np.testing.assert_array_equal(gmask.cpu().numpy().view(np.uint32), m_ref)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_ref)
+    np.testing.assert_array_equal(tokens.cpu().numpy(), tok_ref)
+    np.testing.assert_array_equal(slot_entry.cpu().numpy(), se_ref)
+
+
+@pytest.mark.parametrize("K,topk", [(1, 1), (3, 2), (8, 8), (32, 3), (32, 32), (5, 1)])
+def test_route_forced_ties(K, topk):
+    """r = 0 (all scores +-0), duplicated centroids and signed zeros: ties go
+    to the lower index on both sides."""
+    rng = np.random.default_rng(K * 31 + topk)
+    H, n = 3, 777
+    c = rng.standard_normal((H, K, 16)).astype(np.float32)
+    c[:, K // 2] = c[:, 0]
+    c[0, :] *= -1.0
+    r = rng.standard_normal((H, n, 16)).astype(np.float32)
+    r[:, ::3] = 0.0
+    r[:, 1::7] = -0.0
+    r[:, 2::11] = c[0, 0]
+    g_ref, m_ref = oracle.route(r, c, topk)
+    groups, gmask = F.focus_route(torch.from_numpy(r).to(DEV), torch.from_numpy(c).to(DEV), topk)
+    offsets, tokens, slot_entry = F.focus_bucket(groups, K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(groups.cpu().numpy(), g_ref)
+    np.testing.assert_array_equal(gmask.cpu().numpy().view(np.uint32), m_ref)
+    off_ref, tok_ref, se_ref = oracle.bucket(g_ref, K)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_ref)
+    np.testing.assert_array_equal(tokens.cpu().numpy(), tok_ref)
+    np.testing.assert_array_equal(slot_entry.cpu().numpy(), se_ref)
+
+
+# ----------------------------------------------------------------------------
+# attention, element by element on shapes the oracle evaluates in full
+
+def W(name, n, hq, hkv, d, K, topk, w, dtype, **kw):
+    std = 1.0 if dtype == "f32" else 1.0 / math.sqrt(d)
+    kw.setdefault("qkv_std", std)
+    return Workload(name, n, hq, hkv, d, K, topk, w, dtype, **kw)
+
+
+SMALL = [
+    W("f32_d64_mha_k1", 700, 2, 2, 64, 4, 1, 64, "f32"),
+    W("f32_d128_gqa", 333, 4, 2, 128, 4, 2, 40, "f32"),
+    W("bf16_d64_mha_k2", 1500, 3, 3, 64, 4, 2, 256, "bf16"),
+    W("bf16_d128_gqa4_skew", 1300, 8, 2, 128, 4, 2, 100, "bf16", z_probs=(0.4, 0.3, 0.2, 0.1)),
+    W("bf16_d128_gqa4_k8", 2000, 8, 2, 128, 8, 2, 64, "bf16"),
+    W("bf16_d128_top3_owner", 900, 4, 1, 128, 8, 3, 32, "bf16"),
+    W("bf16_d64_w0", 800, 2, 2, 64, 4, 2, 0, "bf16"),
+    W("bf16_d64_w_ge_n", 600, 2, 1, 64, 4, 2, 600, "bf16"),
+    W("bf16_d128_K1", 700, 4, 4, 128, 1, 1, 16, "bf16"),
+    W("bf16_d64_topk_eq_K", 500, 2, 2, 64, 4, 4, 8, "bf16"),
+    W("bf16_d128_gqa2", 650, 4, 2, 128, 4, 2, 50, "bf16"),
+    W("bf16_d64_gqa3", 450, 6, 2, 64, 4, 2, 30, "bf16"),
+    W("bf16_d128_gqa8", 520, 16, 2, 128, 4, 2, 70, "bf16"),
+    W("bf16_d64_empty_buckets", 900, 2, 2, 64, 8, 1, 20, "bf16",
+      z_probs=(0.5, 0.5, 0, 0, 0, 0, 0, 0), noise=0.05),
+    W("bf16_sharp_logits", 700, 2, 2, 64, 4, 2, 48, "bf16", qkv_std=1.0),
+    W("bf16_n1", 1, 2, 2, 64, 4, 2, 16, "bf16"),
+    W("bf16_n2", 2, 4, 1, 128, 4, 2, 1, "bf16"),
+    W("bf16_n63", 63, 2, 2, 64, 4, 2, 5, "bf16"),
+    W("bf16_n65", 65, 4, 4, 128, 4, 1, 70, "bf16"),
+    W("bf16_n257_w1", 257, 4, 4, 64, 4, 1, 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_attention_small_full_rows(wl):
+    log(f"attention {wl}")
+    seed = 77 + SMALL.index(wl)
+    c, r, _ = routing_inputs(wl, seed)
+    q, k, v = qkv_inputs(wl, seed, DEV)
+    res = gpu_forward(wl, c, r, q, k, v)
+    g_ref, _ = oracle.route(r, c, wl.topk)
+    np.testing.assert_array_equal(res["groups"].cpu().numpy(), g_ref)
+    rh = np.repeat(np.arange(wl.hq, dtype=np.int32), wl.n)
+    rp = np.tile(np.arange(wl.n, dtype=np.int64), wl.hq)
+    check_rows(wl, res, q, k, v, g_ref, rh, rp, wl.name)
+    # q = 0: exp(LSE) counts the attended keys exactly
+    res0 = gpu_forward(wl, c, r, torch.zeros_like(q), k, v)
+    cnt = oracle.pair_counts(g_ref, wl.K, wl.window)
+    hk = np.arange(wl.hq) // (wl.hq // wl.hkv)
+    got = np.exp(res0["lse"].cpu().double().numpy())
+    np.testing.assert_allclose(got, cnt[hk].astype(np.float64), rtol=1e-5)
+
+
+def test_dense_causal_baseline():
+    wl = W("dense", 1000, 8, 2, 128, 1, 1, 1000, "bf16")
+    q, k, v = qkv_inputs(wl, 5, DEV)
+    out, lse = F.focus_dense_causal_fwd(q, k, v, wl.scale)
+    torch.cuda.synchronize()
+    groups = np.zeros((wl.hkv, wl.n, 1), np.int32)
+    rh = np.repeat(np.arange(wl.hq, dtype=np.int32), wl.n)
+    rp = np.tile(np.arange(wl.n, dtype=np.int64), wl.hq)
+    check_rows(wl, dict(out=out, lse=lse), q, k, v, groups, rh, rp, "dense")
+
+
+def test_parts_and_determinism():
+    wl = W("parts", 3000, 8, 2, 128, 8, 2, 128, "bf16")
+    c, r, _ = routing_inputs(wl, 9)
+    q, k, v = qkv_inputs(wl, 9, DEV)
+    a = gpu_forward(wl, c, r, q, k, v)
+    b = gpu_forward(wl, c, r, q, k, v)
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["lse"], b["lse"])
+    ws = torch.empty(F.focus_attn_workspace_bytes(F.FOCUS_BF16, wl.hq, wl.hkv, wl.n, wl.d, wl.K,
+                                                  wl.topk), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty_like(a["lse"])
+    args = (q, k, v, a["gmask"], a["offsets"], a["tokens"], a["slot_entry"], wl.K, wl.window,
+            wl.scale, out, lse, ws)
+    for part in (F.PART_PREPARE, F.PART_GROUP, F.PART_WINDOW):
+        F.focus_attn_fwd_part(*args, parts=part)
+    torch.cuda.synchronize()
+    assert torch.equal(out, a["out"]) and torch.equal(lse, a["lse"])
+
+
+# ----------------------------------------------------------------------------
+# the workloads at full size: sampled rows against the oracle, every row
+# against the exact count
+
+SAMPLED_ROWS = {"tiny_fp32_n512": None, "gpt2_n8k": 2048, "gpt2_n64k": 4096,
+                "gqa7b_n128k_skew": 4096, "gqa7b_n1m_k8": 1024}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    wl = WORKLOADS[name]
+    seed = seed_for(name)
+    log(f"workload {name}: generating")
+    c, r, _ = routing_inputs(wl, seed)
+    q, k, v = qkv_inputs(wl, seed, DEV)
+    log(f"workload {name}: forward")
+    res = gpu_forward(wl, c, r, q, k, v)
+    g_ref, _ = oracle.route(r, c, wl.topk)
+    nrows = SAMPLED_ROWS[name]
+    if nrows is None:
+        rh = np.repeat(np.arange(wl.hq, dtype=np.int32), wl.n)
+        rp = np.tile(np.arange(wl.n, dtype=np.int64), wl.hq)
+    else:
+        rh, rp = sample_rows(wl, seed, nrows)
+    log(f"workload {name}: oracle on {len(rh)} rows")
+    check_rows(wl, res, q, k, v, g_ref, rh, rp, name)
+    del res
+    log(f"workload {name}: q = 0 count probe")
+    q.zero_()
+    res0 = gpu_forward(wl, c, r, q, k, v)
+    cnt = oracle.pair_counts(g_ref, wl.K, wl.window)
+    hk = np.arange(wl.hq) // (wl.hq // wl.hkv)
+    got = np.exp(res0["lse"].cpu().double().numpy())
+    rel = np.abs(got / cnt[hk] - 1.0).max()
+    log(f"[{name}] count probe max rel err {rel:.3e}")
+    assert rel < 1e-5
