@@ -42,8 +42,8 @@
 namespace focus {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = 256;  // kWaves * 64
+constexpr int kThreads = 512;  // 8 wavefronts, 2 per SIMD
+constexpr int kRowsPerBlock = 256;  // 8 wavefronts x 32 query rows
 constexpr int kKeyTile = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -64,6 +64,7 @@ struct Params {
     const int32_t *tokens;
     const int32_t *offsets;
     const uint32_t *gmask;
+    const uint32_t *egm;  // gmask of each bucket entry's token, [hkv][E]
     const int4 *tiles;
     const int32_t *ntiles;
     int max_tiles;
@@ -113,7 +114,7 @@ __device__ __forceinline__ int xcd_remap(int b, int total_padded)
 }
 
 // ---------------------------------------------------------------------------
-// per-dtype tile machinery
+// per-dtype tile machinery: one 32-row query block per wavefront
 
 template <int D, bool BF16>
 struct Tile;
@@ -123,31 +124,20 @@ struct Tile;
 template <int D>
 struct Tile<D, true> {
     using T = __bf16;
-    static constexpr int KS = D / 16;            // 32x32x16 steps over d
-    static constexpr int DB = D / 32;            // 32-row blocks of d in O^T
-    static constexpr int KCH = D / 8;            // 16-byte chunks per K row
+    static constexpr int KS = D / 16;  // 32x32x16 steps over d
+    static constexpr int DB = D / 32;  // 32-row blocks of d in O^T
+    static constexpr int KCH = D / 8;  // 16-byte chunks per K row
     static constexpr int K_BYTES = kKeyTile * D * 2;
     static constexpr int V_BYTES = D * kKeyTile * 2;
     static constexpr int LOADS = (K_BYTES / 16) / kThreads;  // per thread, K and V each
 
     struct QFrag {
-        bf16x8 v[2][KS];
+        bf16x8 v[KS];
     };
     struct Staged {};
-
-    __device__ static int kslot(int row, int c) { return row * KCH + (c ^ kswz(row)); }
-    __device__ static int vslot(int d, int c) { return d * 8 + (c ^ vswz(d)); }
-
-    __device__ static void load_q(QFrag &qf, const T *q, const int64_t (&row_off)[2], int h)
-    {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const bf16x8 *src = reinterpret_cast<const bf16x8 *>(q + row_off[b]);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf.v[b][ks] = src[ks * 2 + h];
-        }
-    }
+    struct PFrag {  // probabilities as the B operand of O^T += V^T P^T
+        bf16x8 v[2][2];
+    };
 
     __device__ static int kswz(int row)
     {
@@ -156,6 +146,16 @@ struct Tile<D, true> {
         return ((row & 3) | (((row >> 4) & 1) << 2)) ^ ((row >> 2) & 1);
     }
     __device__ static int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+    __device__ static int kslot(int row, int c) { return row * KCH + (c ^ kswz(row)); }
+    __device__ static int vslot(int d, int c) { return d * 8 + (c ^ vswz(d)); }
+
+    __device__ static void load_q(QFrag &qf, const T *q, int64_t row_off, int h)
+    {
+        const bf16x8 *src = reinterpret_cast<const bf16x8 *>(q + row_off);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf.v[ks] = src[ks * 2 + h];
+    }
 
     // Start the loads of one key tile straight into LDS: K rows row0.. of
     // kmat (clamped to its last row) and V^T columns row0.. of vmat.  Each
@@ -190,46 +190,59 @@ struct Tile<D, true> {
     }
     __device__ static void land(const Staged &, char *, char *) {}
 
-    // S^T[key][query] for the two 32-key blocks and two 32-query blocks.
-    __device__ static void qk(f32x16 (&s)[2][2], const QFrag &qf, const char *kl, int m, int h)
+    // S^T[key][query] for the two 32-key blocks of the tile.
+    __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const char *kl, int m, int h)
     {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        const int row0 = sigma(m), row1 = 32 + sigma(m);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[0][kb] = f32x16{};
-            s[1][kb] = f32x16{};
-            const int row = kb * 32 + sigma(m);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = reinterpret_cast<const bf16x8 *>(kl)[kslot(row, ks * 2 + h)];
-                s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.v[0][ks], s[0][kb], 0, 0, 0);
-                s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.v[1][ks], s[1][kb], 0, 0, 0);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a0 = reinterpret_cast<const bf16x8 *>(kl)[kslot(row0, ks * 2 + h)];
+            const bf16x8 a1 = reinterpret_cast<const bf16x8 *>(kl)[kslot(row1, ks * 2 + h)];
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf.v[ks], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf.v[ks], s[1], 0, 0, 0);
         }
     }
 
     // O^T[d][query] += V^T P^T.
-    __device__ static void pv(f32x16 (&o)[2][DB], const f32x16 (&s)[2][2], const char *vl, int m,
-                              int h)
+    __device__ static void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vl, int m, int h)
     {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 pb[2];
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pb[b][e] = (__bf16)s[b][kb][kk * 8 + e];
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const bf16x8 a = reinterpret_cast<const bf16x8 *>(
                         vl)[vslot(db * 32 + m, kb * 4 + h * 2 + kk)];
-                    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0], o[0][db], 0, 0, 0);
-                    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1], o[1][db], 0, 0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.v[kb][kk], o[db], 0, 0, 0);
                 }
-            }
-        }
+    }
+
+    // Exponentials of one tile -> bf16 P fragments; returns their fp32 sum.
+    // (The sum is taken before rounding: near-uniform rows round their
+    // probabilities the same way, and a sum of the rounded values would bias
+    // the log-sum-exp by up to ~1e-3.)
+    __device__ static float exp_tile(const f32x16 (&s)[2], float c, float mc, PFrag &pf)
+    {
+        float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float p0 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e], c, -mc));
+                    const float p1 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e + 1], c, -mc));
+                    l0 += p0;
+                    l1 += p1;
+                    pf.v[kb][kk][e] = (__bf16)p0;
+                    pf.v[kb][kk][e + 1] = (__bf16)p1;
+                }
+        return l0 + l1;
     }
 };
 
@@ -246,20 +259,21 @@ struct Tile<D, false> {
     static constexpr int LOADS = (kKeyTile * D / 4) / kThreads;  // float4 per thread
 
     struct QFrag {
-        float v[2][KS];
+        float v[KS];
     };
     struct Staged {
         float4 k[LOADS];
         float4 v[LOADS];
     };
+    struct PFrag {
+        f32x16 s[2];
+    };
 
-    __device__ static void load_q(QFrag &qf, const T *q, const int64_t (&row_off)[2], int h)
+    __device__ static void load_q(QFrag &qf, const T *q, int64_t row_off, int h)
     {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf.v[b][ks] = q[row_off[b] + ks * 2 + h];
+        for (int ks = 0; ks < KS; ++ks)
+            qf.v[ks] = q[row_off + ks * 2 + h];
     }
 
     __device__ static void prefetch(Staged &st, const Params &p, int kvh, int64_t row0, char *,
@@ -295,111 +309,96 @@ struct Tile<D, false> {
         }
     }
 
-    __device__ static void qk(f32x16 (&s)[2][2], const QFrag &qf, const char *kl, int m, int h)
+    __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const char *kl, int m, int h)
     {
         const float *kf = reinterpret_cast<const float *>(kl);
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        const float *k0 = kf + sigma(m) * KROW + h;
+        const float *k1 = kf + (32 + sigma(m)) * KROW + h;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[0][kb] = f32x16{};
-            s[1][kb] = f32x16{};
-            const float *krow = kf + (kb * 32 + sigma(m)) * KROW + h;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const float a = krow[ks * 2];
-                s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf.v[0][ks], s[0][kb], 0, 0, 0);
-                s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf.v[1][ks], s[1][kb], 0, 0, 0);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(k0[ks * 2], qf.v[ks], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(k1[ks * 2], qf.v[ks], s[1], 0, 0, 0);
         }
     }
 
-    __device__ static void pv(f32x16 (&o)[2][DB], const f32x16 (&s)[2][2], const char *vl, int m,
-                              int h)
+    __device__ static void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vl, int m, int h)
     {
         const float *vf = reinterpret_cast<const float *>(vl);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float *vrow = vf + (kb * 32 + h * 16 + r) * D + m;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const float a = vrow[db * 32];
-                    o[0][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[0][kb][r], o[0][db], 0, 0, 0);
-                    o[1][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[1][kb][r], o[1][db], 0, 0, 0);
-                }
+                for (int db = 0; db < DB; ++db)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[db * 32], pf.s[kb][r], o[db],
+                                                                 0, 0, 0);
             }
-        }
+    }
+
+    __device__ static float exp_tile(const f32x16 (&s)[2], float c, float mc, PFrag &pf)
+    {
+        float l = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+                pf.s[kb][r] = pr;
+                l += pr;
+            }
+        return l;
     }
 };
 
 // ---------------------------------------------------------------------------
-// online softmax state of one wavefront (two 32-row blocks; lane column =
-// query, both lane halves carry the same row statistics)
+// online softmax state of one wavefront: one query per lane column, both lane
+// halves carry the same row statistics and half of each row's keys
 
-template <int DB>
+template <class TL>
 struct Acc {
-    f32x16 o[2][DB];
-    float m[2];  // running max in the scaled log2 domain (may be -inf)
-    float l[2];  // this lane half's partial row sum
+    f32x16 o[TL::DB];
+    float m;  // running max in the scaled log2 domain (may be -inf)
+    float l;  // this lane half's partial row sum
 
     __device__ void init()
     {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                o[b][db] = f32x16{};
-            m[b] = -INFINITY;
-            l[b] = 0.f;
-        }
+        for (int db = 0; db < TL::DB; ++db)
+            o[db] = f32x16{};
+        m = -INFINITY;
+        l = 0.f;
     }
 
-    // Turn the raw logits s into probabilities (in place) and fold the tile
-    // into the running state.
-    __device__ void softmax(f32x16 (&s)[2][2], float c)
+    // Fold one tile of raw logits into the state; P receives the
+    // probabilities for the PV product.
+    __device__ void softmax(const f32x16 (&s)[2], float c, typename TL::PFrag &pf)
     {
-        float mx[2];
+        float t = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            float t = -INFINITY;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int r = 0; r < 16; ++r)
+                t = fmaxf(t, s[kb][r]);
+        const float mx = swap_halves_max(t) * c;
+        // Lazy rescale: the running max only moves when a row's max grew by
+        // more than 2^8, so P stays below 2^8 and O is rarely rescaled.
+        if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
+            const float m_new = fmaxf(m, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < TL::DB; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    t = fmaxf(t, s[b][kb][r]);
-            mx[b] = swap_halves_max(t) * c;
+                    o[db][r] *= alpha;
         }
-        // Lazy rescale: only when some row's max grew by more than 2^8.
-        const bool need = (mx[0] > m[0] + kLazyRescale) || (mx[1] > m[1] + kLazyRescale);
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const float m_new = fmaxf(m[b], mx[b]);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m[b] - m_use);
-                m[b] = m_new;
-                l[b] *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        o[b][db][r] *= alpha;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const float mc = (m[b] == -INFINITY) ? 0.f : m[b];
-            float sum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][kb][r], c, -mc));
-                    s[b][kb][r] = pr;
-                    sum += pr;
-                }
-            l[b] += sum;
-        }
+        const float mc = (m == -INFINITY) ? 0.f : m;
+        l += TL::exp_tile(s, c, mc, pf);
     }
 };
 
@@ -407,13 +406,14 @@ struct Acc {
 // the attention kernel: GROUP selects the gathered within-group pass
 
 template <int D, bool BF16, bool GROUP>
-__global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
+__global__ __launch_bounds__(kThreads) void attn_kernel(Params p)
 {
     using TL = Tile<D, BF16>;
     using T = typename TL::T;
     constexpr int DB = TL::DB;
     constexpr int STAGE = TL::K_BYTES + TL::V_BYTES + 2 * kKeyTile * 4;
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) char smem0[STAGE];
+    __shared__ __attribute__((aligned(16))) char smem1[STAGE];
     __shared__ int sub_start[kMaxGroups + 1];
     __shared__ int sub_count[kMaxGroups + 1];
     __shared__ int sub_owner[kMaxGroups + 1];
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
     const int h = lane / 32;
 
     // ---- which work item this block owns
-    int b_lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int b_lin = xcd_remap(blockIdx.x, gridDim.x);
     if (b_lin >= p.total_blocks)
         return;
     int kvh, hg, slot;
@@ -444,11 +444,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
     }
     const int rows_per_head = kRowsPerBlock / p.hpb;
     const int hsub = wave % p.hpb;
-    const int wrow0 = (wave / p.hpb) * 64;  // first row of this wavefront in the tile
+    const int wrow0 = (wave / p.hpb) * 32;  // first row of this wavefront in the tile
     const int hq = kvh * p.ratio + hg * p.hpb + hsub;
 
     // ---- rows of this block
-    int g = 0, mq = 0, e_start = 0, e_count = 0;
+    int g = 0, mq = 0, e_start = 0;
     int64_t p_start = 0;
     int tile_rows;
     if (GROUP) {
@@ -456,8 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
         g = t.x / (p.K + 1);
         mq = t.x % (p.K + 1);
         e_start = t.y;
-        e_count = t.z;
-        tile_rows = e_count;
+        tile_rows = t.z;
     } else {
         p_start = (int64_t)slot * rows_per_head;
         tile_rows = (int)min<int64_t>(rows_per_head, p.n - p_start);
@@ -465,44 +464,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
     const int32_t *tok = GROUP ? p.tokens + (int64_t)kvh * p.E : nullptr;
     const uint32_t *gmh = GROUP ? p.gmask + (int64_t)kvh * p.n : nullptr;
 
-    // query position and validity of the rows this lane carries (column m of
-    // each 32-row block)
-    int qpos[2];
-    bool qvalid[2];
-    int64_t qrow_off[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int r = wrow0 + b * 32 + m;
-        qvalid[b] = r < tile_rows;
-        const int rc = qvalid[b] ? r : 0;
-        qpos[b] = GROUP ? tok[e_start + rc] : (int)(p_start + rc);
-        qrow_off[b] = ((int64_t)hq * p.n + qpos[b]) * D;
-    }
+    // query row of this lane (column m of the wavefront's 32-row block)
+    const int qr = wrow0 + m;
+    const bool qvalid = qr < tile_rows;
+    const int qpos = GROUP ? tok[e_start + (qvalid ? qr : 0)] : (int)(p_start + (qvalid ? qr : 0));
     const bool wave_active = wrow0 < tile_rows;
-    // first and last query position of this wavefront / block
-    const int wave_last_row = min(wrow0 + 63, tile_rows - 1);
+    const int wave_last_row = min(wrow0 + 31, tile_rows - 1);
     const int wq_min = GROUP ? tok[e_start + (wave_active ? wrow0 : 0)] : (int)(p_start + wrow0);
     const int wq_max = GROUP ? tok[e_start + (wave_active ? wave_last_row : 0)]
                              : (int)(p_start + wave_last_row);
     const int bq_max = GROUP ? tok[e_start + tile_rows - 1] : (int)(p_start + tile_rows - 1);
 
     typename TL::QFrag qf;
-    TL::load_q(qf, static_cast<const T *>(p.q), qrow_off, h);
+    TL::load_q(qf, static_cast<const T *>(p.q), ((int64_t)hq * p.n + qpos) * D, h);
 
-    Acc<DB> acc;
+    Acc<TL> acc;
     acc.init();
 
     // ---- key tile schedule
     const int w = p.window;
-    uint32_t qlow[2] = {0u, 0u};
-    int n_sub = 0;
+    uint32_t qlow = 0u;
     int64_t j_first = 0;
     int n_tiles_total = 0;
     if (GROUP) {
-        const uint32_t low = (1u << g) - 1u;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-            qlow[b] = gmh[qpos[b]] & low;
+        qlow = gmh[qpos] & ((1u << g) - 1u);
         // wave 0 lanes find, per key sub-bucket, how many keys lie at or
         // before (last query position - w)
         if (wave == 0 && lane <= p.K) {
@@ -529,9 +514,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
             sub_owner[mk] = (p.topk >= 3) && (mq < g) && (mk < g) && (mk != mq);
         }
         __syncthreads();
-        n_sub = p.K + 1;
-        for (int i = 0; i < n_sub; ++i)
+        for (int i = 0; i <= p.K; ++i)
             n_tiles_total += (sub_count[i] + kKeyTile - 1) / kKeyTile;
+        n_tiles_total = __builtin_amdgcn_readfirstlane(n_tiles_total);
     } else {
         const int64_t lo = max<int64_t>(0, p_start - w + 1);
         j_first = (lo / kKeyTile) * kKeyTile;
@@ -541,15 +526,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
 
     // iterator over key tiles: (sub-bucket, tile) for the group pass
     int it_sub = 0, it_tile = 0;
+    // (values read from LDS are block-uniform: keep them in scalar registers)
+    auto uniform = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
     auto tile_origin = [&](int &valid, int &owner) -> int64_t {
         if (GROUP) {
-            while (it_tile * kKeyTile >= sub_count[it_sub]) {
+            while (it_tile * kKeyTile >= uniform(sub_count[it_sub])) {
                 ++it_sub;
                 it_tile = 0;
             }
-            valid = min(kKeyTile, sub_count[it_sub] - it_tile * kKeyTile);
-            owner = sub_owner[it_sub];
-            return (int64_t)sub_start[it_sub] + (int64_t)it_tile * kKeyTile;
+            valid = min(kKeyTile, uniform(sub_count[it_sub]) - it_tile * kKeyTile);
+            owner = uniform(sub_owner[it_sub]);
+            return (int64_t)uniform(sub_start[it_sub]) + (int64_t)it_tile * kKeyTile;
         } else {
             valid = kKeyTile;
             owner = 0;
@@ -558,51 +545,74 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
     };
 
     typename TL::Staged st;
-    // Positions (and, where an owner test is needed, group bits) of the keys
-    // of one tile go next to its K and V^T data.
-    auto stage_keys = [&](char *buf, int64_t origin, int valid, int owner) {
-        int *kpos = reinterpret_cast<int *>(buf + TL::K_BYTES + TL::V_BYTES);
-        uint32_t *kgm = reinterpret_cast<uint32_t *>(kpos + kKeyTile);
+    // Positions (and, where an owner test is needed, group bits) of a tile's
+    // keys live next to its K and V^T data.  They are read from global
+    // memory into registers when the tile's loads are issued and written to
+    // LDS only after the current tile's compute: writing them at once would
+    // make the wavefront wait for every load issued before them.
+    const uint32_t *egh = GROUP ? p.egm + (int64_t)kvh * p.E : nullptr;
+    auto load_keys = [&](int64_t origin, int valid, int owner, int &pos, uint32_t &gm) {
+        pos = 0;
+        gm = 0u;
         if (threadIdx.x < kKeyTile) {
             const int i = threadIdx.x;
             if (GROUP) {
-                const int pos = i < valid ? tok[origin + i] : 0x7fffffff;
-                kpos[i] = pos;
-                kgm[i] = (i < valid && owner) ? gmh[pos] : 0u;
+                pos = i < valid ? tok[origin + i] : 0x7fffffff;
+                gm = (i < valid && owner) ? egh[origin + i] : 0u;
             } else {
-                kpos[i] = (int)(origin + i);
+                pos = (int)(origin + i);
             }
+        }
+    };
+    auto store_keys = [&](char *buf, int pos, uint32_t gm) {
+        int *kpos = reinterpret_cast<int *>(buf + TL::K_BYTES + TL::V_BYTES);
+        uint32_t *kgm = reinterpret_cast<uint32_t *>(kpos + kKeyTile);
+        if (threadIdx.x < kKeyTile) {
+            kpos[threadIdx.x] = pos;
+            kgm[threadIdx.x] = gm;
         }
     };
     int cur_valid = 0, cur_owner = 0;
     if (n_tiles_total > 0) {
         const int64_t origin = tile_origin(cur_valid, cur_owner);
-        TL::prefetch(st, p, kvh, origin, smem, smem + TL::K_BYTES);
-        TL::land(st, smem, smem + TL::K_BYTES);
-        stage_keys(smem, origin, cur_valid, cur_owner);
+        int pos;
+        uint32_t gm;
+        load_keys(origin, cur_valid, cur_owner, pos, gm);
+        TL::prefetch(st, p, kvh, origin, smem0, smem0 + TL::K_BYTES);
+        TL::land(st, smem0, smem0 + TL::K_BYTES);
+        store_keys(smem0, pos, gm);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int t = 0; t < n_tiles_total; ++t) {
-        char *cur = smem + (t & 1) * STAGE;
-        char *nxt = smem + ((t + 1) & 1) * STAGE;
+    // One key tile: compute on `cur` while the next tile streams into `nxt`.
+    // The two LDS buffers are distinct arrays and the loop below is unrolled
+    // by two, so each LDS read names one buffer and each LDS-DMA write the
+    // other: the compiler can then see they do not overlap and does not wait
+    // for the in-flight loads before reading the current tile.
+    auto step = [&](int t, char *cur, char *nxt) {
         const int valid = cur_valid;
         const int owner = cur_owner;
         // start loading the next tile; it lands in the other buffer while
         // this one is computed
         const bool has_next = t + 1 < n_tiles_total;
+        int nx_pos = 0;
+        uint32_t nx_gm = 0u;
         if (has_next) {
             ++it_tile;
             const int64_t origin = tile_origin(cur_valid, cur_owner);
+            load_keys(origin, cur_valid, cur_owner, nx_pos, nx_gm);
             TL::prefetch(st, p, kvh, origin, nxt, nxt + TL::K_BYTES);
-            stage_keys(nxt, origin, cur_valid, cur_owner);
         }
 
         const int *kpos = reinterpret_cast<const int *>(cur + TL::K_BYTES + TL::V_BYTES);
         const uint32_t *kgm = reinterpret_cast<const uint32_t *>(kpos + kKeyTile);
-        if (wave_active) {
-            f32x16 s[2][2];
+        // Every wavefront computes, including one whose rows all lie past a
+        // ragged tile's end (its rows are masked and never stored): a branch
+        // here would split the accumulator's live range and cost a register
+        // copy of O per tile.
+        {
+            f32x16 s[2];
             TL::qk(s, qf, cur, m, h);
             // does any pair of this tile x wavefront need a mask?
             bool masked;
@@ -614,6 +624,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
                 masked = !((j0 + kKeyTile - 1 <= wq_min) && (j0 > (int64_t)wq_max - w));
             }
             if (masked) {
+                // kgm holds zero unless this sub-bucket pair needs the owner
+                // test, so the test below is a no-op elsewhere
+                const int64_t lim = (int64_t)qpos - w;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int4 *kp4 = reinterpret_cast<const int4 *>(kpos + kb * 32 + h * 16);
@@ -621,148 +634,136 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(Params p)
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int4 kp = kp4[r4];
+                        const uint4 kg = kg4[r4];
                         const int kv[4] = {kp.x, kp.y, kp.z, kp.w};
-                        uint32_t kgv[4] = {0u, 0u, 0u, 0u};
-                        if (GROUP && owner) {
-                            const uint4 kg = kg4[r4];
-                            kgv[0] = kg.x;
-                            kgv[1] = kg.y;
-                            kgv[2] = kg.z;
-                            kgv[3] = kg.w;
-                        }
+                        const uint32_t kgv[4] = {kg.x, kg.y, kg.z, kg.w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int r = r4 * 4 + e;
-#pragma unroll
-                            for (int b = 0; b < 2; ++b) {
-                                bool keep;
-                                if (GROUP)
-                                    keep = qvalid[b] && ((int64_t)kv[e] <= (int64_t)qpos[b] - w) &&
-                                           ((kgv[e] & qlow[b]) == 0u);
-                                else
-                                    keep = qvalid[b] && (kv[e] <= qpos[b]) &&
-                                           ((int64_t)kv[e] > (int64_t)qpos[b] - w);
-                                if (!keep)
-                                    s[b][kb][r] = -INFINITY;
-                            }
+                            bool keep;
+                            if (GROUP)
+                                keep = qvalid && ((int64_t)kv[e] <= lim) &&
+                                       ((kgv[e] & qlow) == 0u);
+                            else
+                                keep = qvalid && (kv[e] <= qpos) && ((int64_t)kv[e] > lim);
+                            s[kb][r4 * 4 + e] = keep ? s[kb][r4 * 4 + e] : -INFINITY;
                         }
                     }
                 }
             }
-            acc.softmax(s, p.c);
-            TL::pv(acc.o, s, cur + TL::K_BYTES, m, h);
+            typename TL::PFrag pf;
+            acc.softmax(s, p.c, pf);
+            TL::pv(acc.o, pf, cur + TL::K_BYTES, m, h);
         }
 
-        if (has_next)
+        if (has_next) {
             TL::land(st, nxt, nxt + TL::K_BYTES);
+            store_keys(nxt, nx_pos, nx_gm);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+    for (int t = 0; t < n_tiles_total; t += 2) {
+        step(t, smem0, smem1);
+        if (t + 1 < n_tiles_total)
+            step(t + 1, smem1, smem0);
     }
 
     if (!wave_active)
         return;
 
     // ---- epilogue
-    float l_tot[2], lse2[2];  // lse2: log2-domain log-sum-exp of the scaled logits
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        l_tot[b] = swap_halves_sum(acc.l[b]);
-        lse2[b] = (l_tot[b] > 0.f) ? acc.m[b] + __builtin_amdgcn_logf(l_tot[b]) : -INFINITY;
-    }
+    const float l_tot = swap_halves_sum(acc.l);
+    // log2-domain log-sum-exp of the scaled logits
+    const float lse2 = (l_tot > 0.f) ? acc.m + __builtin_amdgcn_logf(l_tot) : -INFINITY;
 
     if (GROUP) {
         // normalised partial O (fp32) and natural-log LSE at the query's entry
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (!qvalid[b])
-                continue;
-            const int64_t e = e_start + wrow0 + b * 32 + m;
-            const float inv = (l_tot[b] > 0.f) ? 1.f / l_tot[b] : 0.f;
-            float *po = p.part_o + ((int64_t)hq * p.E + e) * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    float4 v;
-                    v.x = acc.o[b][db][a * 4 + 0] * inv;
-                    v.y = acc.o[b][db][a * 4 + 1] * inv;
-                    v.z = acc.o[b][db][a * 4 + 2] * inv;
-                    v.w = acc.o[b][db][a * 4 + 3] * inv;
-                    *reinterpret_cast<float4 *>(po + db * 32 + a * 8 + h * 4) = v;
-                }
-            if (h == 0)
-                p.part_lse[(int64_t)hq * p.E + e] = lse2[b] * kLn2;
-        }
-        return;
-    }
-
-    // window pass: merge with the k group partials of the row, write O, LSE
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (!qvalid[b])
-            continue;
-        const int64_t i = qpos[b];
-        const int ns = p.merge ? p.topk : 0;
-        const int32_t *slots = p.slot_entry + ((int64_t)kvh * p.n + i) * p.topk;
-        const float *plse = p.part_lse + (int64_t)hq * p.E;
-        float M = lse2[b];
-        for (int s_ = 0; s_ < ns; ++s_)
-            M = fmaxf(M, plse[slots[s_]] * kLog2e);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        const float a_w = (l_tot[b] > 0.f) ? __builtin_amdgcn_exp2f(lse2[b] - Mu) / l_tot[b] : 0.f;
-        float wsum = (l_tot[b] > 0.f) ? __builtin_amdgcn_exp2f(lse2[b] - Mu) : 0.f;
-        float res[DB][16];
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                res[db][r] = acc.o[b][db][r] * a_w;
-        for (int s_ = 0; s_ < ns; ++s_) {
-            const int32_t ent = slots[s_];
-            const float a_s = __builtin_amdgcn_exp2f(plse[ent] * kLog2e - Mu);
-            if (a_s == 0.f)
-                continue;
-            wsum += a_s;
-            const float *po = p.part_o + ((int64_t)hq * p.E + ent) * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float4 v = *reinterpret_cast<const float4 *>(po + db * 32 + a * 8 + h * 4);
-                    res[db][a * 4 + 0] += a_s * v.x;
-                    res[db][a * 4 + 1] += a_s * v.y;
-                    res[db][a * 4 + 2] += a_s * v.z;
-                    res[db][a * 4 + 3] += a_s * v.w;
-                }
-        }
-        const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
-        T *orow = static_cast<T *>(p.out) + ((int64_t)hq * p.n + i) * D;
+        if (!qvalid)
+            return;
+        const int64_t e = e_start + qr;
+        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+        float *po = p.part_o + ((int64_t)hq * p.E + e) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                T *dst = orow + db * 32 + a * 8 + h * 4;
-                if (BF16) {
-                    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-                    bf16x4 v;
-                    v[0] = (__bf16)(res[db][a * 4 + 0] * inv);
-                    v[1] = (__bf16)(res[db][a * 4 + 1] * inv);
-                    v[2] = (__bf16)(res[db][a * 4 + 2] * inv);
-                    v[3] = (__bf16)(res[db][a * 4 + 3] * inv);
-                    *reinterpret_cast<bf16x4 *>(dst) = v;
-                } else {
-                    float4 v;
-                    v.x = res[db][a * 4 + 0] * inv;
-                    v.y = res[db][a * 4 + 1] * inv;
-                    v.z = res[db][a * 4 + 2] * inv;
-                    v.w = res[db][a * 4 + 3] * inv;
-                    *reinterpret_cast<float4 *>(dst) = v;
-                }
+                float4 v;
+                v.x = acc.o[db][a * 4 + 0] * inv;
+                v.y = acc.o[db][a * 4 + 1] * inv;
+                v.z = acc.o[db][a * 4 + 2] * inv;
+                v.w = acc.o[db][a * 4 + 3] * inv;
+                *reinterpret_cast<float4 *>(po + db * 32 + a * 8 + h * 4) = v;
             }
         if (h == 0)
-            p.lse[(int64_t)hq * p.n + i] = (wsum > 0.f) ? (Mu + __builtin_amdgcn_logf(wsum)) * kLn2
-                                                         : -INFINITY;
+            p.part_lse[(int64_t)hq * p.E + e] = lse2 * kLn2;
+        return;
     }
+
+    // window pass: merge with the k group partials of the row, write O, LSE
+    if (!qvalid)
+        return;
+    const int64_t i = qpos;
+    const int ns = p.merge ? p.topk : 0;
+    const int32_t *slots = p.slot_entry + ((int64_t)kvh * p.n + i) * p.topk;
+    const float *plse = p.part_lse + (int64_t)hq * p.E;
+    float M = lse2;
+    for (int s_ = 0; s_ < ns; ++s_)
+        M = fmaxf(M, plse[slots[s_]] * kLog2e);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    const float w_win = (l_tot > 0.f) ? __builtin_amdgcn_exp2f(lse2 - Mu) : 0.f;
+    const float a_w = (l_tot > 0.f) ? w_win / l_tot : 0.f;
+    float wsum = w_win;
+    float res[DB][16];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            res[db][r] = acc.o[db][r] * a_w;
+    for (int s_ = 0; s_ < ns; ++s_) {
+        const int32_t ent = slots[s_];
+        const float a_s = __builtin_amdgcn_exp2f(plse[ent] * kLog2e - Mu);
+        if (a_s == 0.f)
+            continue;
+        wsum += a_s;
+        const float *po = p.part_o + ((int64_t)hq * p.E + ent) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float4 v = *reinterpret_cast<const float4 *>(po + db * 32 + a * 8 + h * 4);
+                res[db][a * 4 + 0] += a_s * v.x;
+                res[db][a * 4 + 1] += a_s * v.y;
+                res[db][a * 4 + 2] += a_s * v.z;
+                res[db][a * 4 + 3] += a_s * v.w;
+            }
+    }
+    const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
+    T *orow = static_cast<T *>(p.out) + ((int64_t)hq * p.n + i) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            T *dst = orow + db * 32 + a * 8 + h * 4;
+            if (BF16) {
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                bf16x4 v;
+                v[0] = (__bf16)(res[db][a * 4 + 0] * inv);
+                v[1] = (__bf16)(res[db][a * 4 + 1] * inv);
+                v[2] = (__bf16)(res[db][a * 4 + 2] * inv);
+                v[3] = (__bf16)(res[db][a * 4 + 3] * inv);
+                *reinterpret_cast<bf16x4 *>(dst) = v;
+            } else {
+                float4 v;
+                v.x = res[db][a * 4 + 0] * inv;
+                v.y = res[db][a * 4 + 1] * inv;
+                v.z = res[db][a * 4 + 2] * inv;
+                v.w = res[db][a * 4 + 3] * inv;
+                *reinterpret_cast<float4 *>(dst) = v;
+            }
+        }
+    if (h == 0)
+        p.lse[(int64_t)hq * p.n + i] =
+            (wsum > 0.f) ? (Mu + __builtin_amdgcn_logf(wsum)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -830,6 +831,21 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(
     }
 }
 
+// egm[h][e] = gmask[h][tokens[h][e]]: the group bits of every bucket entry, in
+// bucket order, so a tile's owner test reads them without a dependent load.
+__global__ __launch_bounds__(256) void gather_gmask_kernel(const uint32_t *__restrict__ gmask,
+                                                           const int32_t *__restrict__ tokens,
+                                                           int64_t n, int64_t E, int H,
+                                                           uint32_t *__restrict__ egm)
+{
+    const int64_t total = (int64_t)H * E;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t h = i / E;
+        egm[i] = gmask[h * n + tokens[i]];
+    }
+}
+
 // Tile list of the group pass: for routing head h, every sub-bucket cut into
 // query tiles of `rows` entries, last tile (latest positions, most keys)
 // first.  tiles[h][i] = {sub-bucket, first entry, entry count, 0}.
@@ -868,7 +884,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
 struct Layout {
     int hpb, nhg, rows_group, max_tiles;
     int64_t E, e_pad, n_pad;
-    size_t kb, vb, vt, po, pl, tiles, ntiles, total;
+    size_t kb, vb, vt, egm, po, pl, tiles, ntiles, total;
 };
 
 int heads_per_block(int ratio)
@@ -901,6 +917,7 @@ Layout make_layout(const AttnShape &sh)
     L.kb = take((size_t)sh.hkv * L.e_pad * sh.d * es);
     L.vb = take((size_t)sh.hkv * L.e_pad * sh.d * es);
     L.vt = take(sh.dt == FOCUS_BF16 ? (size_t)sh.hkv * sh.d * L.n_pad * 2 : 0);
+    L.egm = take((size_t)sh.hkv * L.E * 4);
     L.po = take((size_t)sh.hq * L.E * sh.d * 4);
     L.pl = take((size_t)sh.hq * L.E * 4);
     L.tiles = take((size_t)sh.hkv * L.max_tiles * sizeof(int4));
@@ -1020,6 +1037,15 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
         }
         if (e != hipSuccess)
             return e;
+        {
+            const int64_t total = (int64_t)sh.hkv * L.E;
+            const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
+            hipLaunchKernelGGL(gather_gmask_kernel, dim3(blocks), dim3(256), 0, s, gmask, tokens,
+                               sh.n, L.E, sh.hkv, reinterpret_cast<uint32_t *>(w + L.egm));
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
         hipLaunchKernelGGL(plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets,
                            num_subbuckets(sh.K), L.rows_group, L.max_tiles, tiles, ntiles);
         e = hipGetLastError();
@@ -1032,6 +1058,7 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
     p.tokens = tokens;
     p.offsets = offsets;
     p.gmask = gmask;
+    p.egm = reinterpret_cast<const uint32_t *>(w + L.egm);
     p.part_o = reinterpret_cast<float *>(w + L.po);
     p.part_lse = reinterpret_cast<float *>(w + L.pl);
     p.slot_entry = slot_entry;
