@@ -118,6 +118,9 @@ def main() -> int:
                     help="seconds of oracle attention time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes three "
+                         "times (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -125,6 +128,15 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}))
+        return 0
 
     from centroid_gated_sparse_amd import focus as F
     from centroid_gated_sparse_amd.workloads import (WORKLOADS, qkv_inputs, routing_inputs,

@@ -36,14 +36,20 @@
 //     is only moved when a tile raises it by more than 2^8.
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace focus {
 namespace {
 
-constexpr int kThreads = 512;  // 8 wavefronts, 2 per SIMD
-constexpr int kRowsPerBlock = 256;  // 8 wavefronts x 32 query rows
+#ifndef FOCUS_ATTN_WAVES
+#define FOCUS_ATTN_WAVES 8
+#endif
+constexpr int kThreads = 64 * FOCUS_ATTN_WAVES;  // 32 query rows per wavefront
+constexpr int kRowsPerBlock = 32 * FOCUS_ATTN_WAVES;
+constexpr int kBlocksPerCU = 8 / FOCUS_ATTN_WAVES;  // two wavefronts per SIMD
+constexpr int kWavesPerRole = FOCUS_ATTN_WAVES / 2;  // ping-pong roles A and B
 constexpr int kKeyTile = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -64,7 +70,9 @@ struct Params {
     const int32_t *tokens;
     const int32_t *offsets;
     const uint32_t *gmask;
-    const uint32_t *egm;  // gmask of each bucket entry's token, [hkv][E]
+    const int32_t *etok;  // position of each bucket entry, [hkv][estride], INT_MAX padded
+    const uint32_t *egm;  // gmask of each bucket entry's token, [hkv][estride], 0 padded
+    int64_t estride;
     const int4 *tiles;
     const int32_t *ntiles;
     int max_tiles;
@@ -113,6 +121,51 @@ __device__ __forceinline__ int xcd_remap(int b, int total_padded)
     return (b % kXcds) * per + b / kXcds;
 }
 
+// (Take the LDS address of an array itself and add offsets to the 32-bit
+// result: converting "array + offset" back from a generic pointer costs a
+// null test and keeps the 64-bit generic pointer alive.)
+// LDS-DMA: each lane loads 16 (or 4) bytes from gbase + voff and the
+// wavefront's 64 results land contiguously at LDS byte address lds_addr (via
+// M0).  Issued from inline assembly so that the compiler neither tracks nor
+// waits for these loads: the kernel waits for them itself (vmcnt) before the
+// barrier that publishes a stage.  M0 is saved and restored around the load;
+// writing M0 needs one wait state before the load reads it.
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p);
+}
+
+// (Both the LDS address and the global base are wave-uniform; readfirstlane
+// puts them in the scalar registers the instruction reads them from.)
+__device__ __forceinline__ const void *uniform_ptr(const void *p)
+{
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void *)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_addr)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(gbase))
+                 : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t lds_addr)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(gbase))
+                 : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // per-dtype tile machinery: one 32-row query block per wavefront
 
@@ -134,7 +187,6 @@ struct Tile<D, true> {
     struct QFrag {
         bf16x8 v[KS];
     };
-    struct Staged {};
     struct PFrag {  // probabilities as the B operand of O^T += V^T P^T
         bf16x8 v[2][2];
     };
@@ -158,55 +210,92 @@ struct Tile<D, true> {
     }
 
     // Start the loads of one key tile straight into LDS: K rows row0.. of
-    // kmat (clamped to its last row) and V^T columns row0.. of vmat.  Each
-    // global_load_lds writes 64 consecutive 16-byte LDS slots (one per lane),
-    // so every lane fetches the chunk that the swizzled layout keeps in its
-    // slot.  Completion is awaited by the caller (vmcnt) before the barrier.
-    __device__ static void prefetch(Staged &, const Params &p, int kvh, int64_t row0, char *kl,
-                                    char *vl)
+    // kmat and V^T columns row0.. of vmat (both zero-padded past their last
+    // row, so no load needs a clamp).  Each global_load_lds writes 64
+    // consecutive 16-byte LDS slots (one per lane), so every lane fetches the
+    // chunk that the swizzled layout keeps in its slot.  Addresses are a
+    // block-uniform base (scalar registers) plus a fixed per-lane 32-bit
+    // offset.  Completion is awaited by the caller (vmcnt) before a barrier.
+    struct Staged {
+        uint32_t koff[LOADS];
+        uint32_t voff[LOADS];
+    };
+    __device__ static void init_staging(Staged &st, const Params &p)
     {
-        const T *km = static_cast<const T *>(p.kmat) + (int64_t)kvh * p.krows * D;
-        const T *vm = static_cast<const T *>(p.vmat) + (int64_t)kvh * D * p.vcols;
         const int lane = threadIdx.x % kWave;
         const int wave = threadIdx.x / kWave;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int inst = wave * LOADS + i;
-            const int P = inst * kWave + lane;
+            const int P = (wave * LOADS + i) * kWave + lane;
             const int row = P / KCH;
             const int c = (P % KCH) ^ kswz(row);
-            int64_t gr = row0 + row;
-            if (gr > p.krows - 1)
-                gr = p.krows - 1;
-            __builtin_amdgcn_global_load_lds(
-                km + gr * D + c * 8, (__attribute__((address_space(3))) void *)(kl + inst * 1024),
-                16, 0, 0);
+            st.koff[i] = (uint32_t)((row * D + c * 8) * 2);
             const int d = P / 8;
             const int vc = (P % 8) ^ vswz(d);
-            __builtin_amdgcn_global_load_lds(
-                vm + (int64_t)d * p.vcols + row0 + vc * 8,
-                (__attribute__((address_space(3))) void *)(vl + inst * 1024), 16, 0, 0);
+            st.voff[i] = (uint32_t)(((int64_t)d * p.vcols + vc * 8) * 2);
+        }
+    }
+    __device__ static void prefetch(Staged &st, const Params &p, int kvh, int64_t row0, char *kl,
+                                    char *vl)
+    {
+        const char *kb = static_cast<const char *>(p.kmat) + ((int64_t)kvh * p.krows + row0) * D * 2;
+        const char *vb = static_cast<const char *>(p.vmat) + ((int64_t)kvh * D * p.vcols + row0) * 2;
+        const int wave = threadIdx.x / kWave;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int inst = wave * LOADS + i;
+            dma16(kb, st.koff[i], lds_address(kl) + inst * 1024);
+            dma16(vb, st.voff[i], lds_address(vl) + inst * 1024);
         }
     }
     __device__ static void land(const Staged &, char *, char *) {}
 
+    // Per-lane byte offsets of this lane's MFMA operand fragments inside a K
+    // tile (one per 16-wide step over d) and a V^T tile (one per 8-key
+    // column group); the 32-row blocks of the tile add fixed offsets.
+    struct LdsOff {
+        uint32_t k[KS];
+        uint32_t v[4];
+    };
+    __device__ static void init_lds_off(LdsOff &o, int m, int h)
+    {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            o.k[ks] = (uint32_t)kslot(sigma(m), ks * 2 + h) * 16u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)  // j = kb * 2 + kk
+            o.v[j] = (uint32_t)vslot(m, (j >> 1) * 4 + h * 2 + (j & 1)) * 16u;
+    }
+    // Hide the offsets' values from the optimiser at the start of each
+    // compute phase: it then adds each stage's (constant) LDS address in the
+    // instruction's immediate field instead of keeping a precomputed address
+    // per stage live across the loop.
+    __device__ static void refresh(LdsOff &o)
+    {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            asm volatile("" : "+v"(o.k[ks]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            asm volatile("" : "+v"(o.v[j]));
+    }
+
     // S^T[key][query] for the two 32-key blocks of the tile.
-    __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const char *kl, int m, int h)
+    __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const char *kl, const LdsOff &o)
     {
         s[0] = f32x16{};
         s[1] = f32x16{};
-        const int row0 = sigma(m), row1 = 32 + sigma(m);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a0 = reinterpret_cast<const bf16x8 *>(kl)[kslot(row0, ks * 2 + h)];
-            const bf16x8 a1 = reinterpret_cast<const bf16x8 *>(kl)[kslot(row1, ks * 2 + h)];
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kl + o.k[ks]);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kl + o.k[ks] + 32 * D * 2);
             s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf.v[ks], s[0], 0, 0, 0);
             s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf.v[ks], s[1], 0, 0, 0);
         }
     }
 
     // O^T[d][query] += V^T P^T.
-    __device__ static void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vl, int m, int h)
+    __device__ static void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vl, const LdsOff &lo)
     {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -214,8 +303,8 @@ struct Tile<D, true> {
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x8 a = reinterpret_cast<const bf16x8 *>(
-                        vl)[vslot(db * 32 + m, kb * 4 + h * 2 + kk)];
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vl + lo.v[kb * 2 + kk] +
+                                                                        db * 32 * 64 * 2);
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.v[kb][kk], o[db], 0, 0, 0);
                 }
     }
@@ -268,6 +357,7 @@ struct Tile<D, false> {
     struct PFrag {
         f32x16 s[2];
     };
+    __device__ static void init_staging(Staged &, const Params &) {}
 
     __device__ static void load_q(QFrag &qf, const T *q, int64_t row_off, int h)
     {
@@ -309,8 +399,19 @@ struct Tile<D, false> {
         }
     }
 
-    __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const char *kl, int m, int h)
+    struct LdsOff {
+        int m, h;
+    };
+    __device__ static void init_lds_off(LdsOff &o, int m, int h)
     {
+        o.m = m;
+        o.h = h;
+    }
+    __device__ static void refresh(LdsOff &) {}
+
+    __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const char *kl, const LdsOff &lo)
+    {
+        const int m = lo.m, h = lo.h;
         const float *kf = reinterpret_cast<const float *>(kl);
         s[0] = f32x16{};
         s[1] = f32x16{};
@@ -323,8 +424,9 @@ struct Tile<D, false> {
         }
     }
 
-    __device__ static void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vl, int m, int h)
+    __device__ static void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vl, const LdsOff &lo)
     {
+        const int m = lo.m, h = lo.h;
         const float *vf = reinterpret_cast<const float *>(vl);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -406,14 +508,54 @@ struct Acc {
 // the attention kernel: GROUP selects the gathered within-group pass
 
 template <int D, bool BF16, bool GROUP>
-__global__ __launch_bounds__(kThreads) void attn_kernel(Params p)
+__global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
 {
     using TL = Tile<D, BF16>;
     using T = typename TL::T;
     constexpr int DB = TL::DB;
-    constexpr int STAGE = TL::K_BYTES + TL::V_BYTES + 2 * kKeyTile * 4;
-    __shared__ __attribute__((aligned(16))) char smem0[STAGE];
-    __shared__ __attribute__((aligned(16))) char smem1[STAGE];
+    // A stage holds one key tile: K, V^T, and the keys' positions, group bits
+    // and the tile's valid-key count and owner-test flag.  bf16 runs the
+    // staggered two-role schedule over four stages (loads two tiles ahead),
+    // fp32 the plain double-buffered one.  Each part of each stage is its own LDS array, so
+    // the compiler can tell an LDS-DMA write into one stage from a read of
+    // another, and the K stages sit low enough for one lane offset plus an
+    // immediate to address all of them.
+    constexpr int NSTAGE = BF16 ? 4 : 2;
+    constexpr int KEYS = 2 * kKeyTile + 4;
+    constexpr int KB3 = NSTAGE >= 3 ? TL::K_BYTES : 16, VB3 = NSTAGE >= 3 ? TL::V_BYTES : 16;
+    constexpr int KB4 = NSTAGE >= 4 ? TL::K_BYTES : 16, VB4 = NSTAGE >= 4 ? TL::V_BYTES : 16;
+    __shared__ __attribute__((aligned(16))) char k_lds0[TL::K_BYTES];
+    __shared__ __attribute__((aligned(16))) char k_lds1[TL::K_BYTES];
+    __shared__ __attribute__((aligned(16))) char k_lds2[KB3];
+    __shared__ __attribute__((aligned(16))) char k_lds3[KB4];
+    __shared__ __attribute__((aligned(16))) char v_lds0[TL::V_BYTES];
+    __shared__ __attribute__((aligned(16))) char v_lds1[TL::V_BYTES];
+    __shared__ __attribute__((aligned(16))) char v_lds2[VB3];
+    __shared__ __attribute__((aligned(16))) char v_lds3[VB4];
+    __shared__ __attribute__((aligned(16))) int key_lds0[KEYS];
+    __shared__ __attribute__((aligned(16))) int key_lds1[KEYS];
+    __shared__ __attribute__((aligned(16))) int key_lds2[KEYS];
+    __shared__ __attribute__((aligned(16))) int key_lds3[KEYS];
+    // Stage<I> names the arrays of stage I at compile time.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    struct Stage {
+        char *k;
+        char *v;
+        int *key;
+    };
+    auto stage = [&](auto I) -> Stage {
+        if constexpr (decltype(I)::value == 0)
+            return Stage{k_lds0, v_lds0, key_lds0};
+        else if constexpr (decltype(I)::value == 1)
+            return Stage{k_lds1, v_lds1, key_lds1};
+        else if constexpr (decltype(I)::value == 2)
+            return Stage{k_lds2, v_lds2, key_lds2};
+        else
+            return Stage{k_lds3, v_lds3, key_lds3};
+    };
     __shared__ int sub_start[kMaxGroups + 1];
     __shared__ int sub_count[kMaxGroups + 1];
     __shared__ int sub_owner[kMaxGroups + 1];
@@ -545,127 +687,285 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p)
     };
 
     typename TL::Staged st;
+    TL::init_staging(st, p);
+    typename TL::LdsOff lo;
+    TL::init_lds_off(lo, m, h);
     // Positions (and, where an owner test is needed, group bits) of a tile's
     // keys live next to its K and V^T data.  They are read from global
     // memory into registers when the tile's loads are issued and written to
     // LDS only after the current tile's compute: writing them at once would
     // make the wavefront wait for every load issued before them.
-    const uint32_t *egh = GROUP ? p.egm + (int64_t)kvh * p.E : nullptr;
+    const int32_t *etk = GROUP ? p.etok + (int64_t)kvh * p.estride : nullptr;
+    const uint32_t *egh = GROUP ? p.egm + (int64_t)kvh * p.estride : nullptr;
     auto load_keys = [&](int64_t origin, int valid, int owner, int &pos, uint32_t &gm) {
         pos = 0;
         gm = 0u;
         if (threadIdx.x < kKeyTile) {
             const int i = threadIdx.x;
             if (GROUP) {
-                pos = i < valid ? tok[origin + i] : 0x7fffffff;
+                pos = i < valid ? etk[origin + i] : 0x7fffffff;
                 gm = (i < valid && owner) ? egh[origin + i] : 0u;
             } else {
                 pos = (int)(origin + i);
             }
         }
     };
-    auto store_keys = [&](char *buf, int pos, uint32_t gm) {
-        int *kpos = reinterpret_cast<int *>(buf + TL::K_BYTES + TL::V_BYTES);
+    auto store_keys = [&](auto I, int pos, uint32_t gm, int valid, int owner) {
+        int *kpos = stage(I).key;
         uint32_t *kgm = reinterpret_cast<uint32_t *>(kpos + kKeyTile);
         if (threadIdx.x < kKeyTile) {
             kpos[threadIdx.x] = pos;
             kgm[threadIdx.x] = gm;
         }
+        if (threadIdx.x == 0) {
+            kpos[2 * kKeyTile] = valid;
+            kpos[2 * kKeyTile + 1] = owner;
+        }
+    };
+    auto stage_meta = [&](auto I, int &valid, int &owner) {
+        const int *meta = stage(I).key + 2 * kKeyTile;
+        valid = __builtin_amdgcn_readfirstlane(meta[0]);
+        owner = __builtin_amdgcn_readfirstlane(meta[1]);
     };
     int cur_valid = 0, cur_owner = 0;
-    if (n_tiles_total > 0) {
-        const int64_t origin = tile_origin(cur_valid, cur_owner);
-        int pos;
-        uint32_t gm;
-        load_keys(origin, cur_valid, cur_owner, pos, gm);
-        TL::prefetch(st, p, kvh, origin, smem0, smem0 + TL::K_BYTES);
-        TL::land(st, smem0, smem0 + TL::K_BYTES);
-        store_keys(smem0, pos, gm);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // One key tile: compute on `cur` while the next tile streams into `nxt`.
-    // The two LDS buffers are distinct arrays and the loop below is unrolled
-    // by two, so each LDS read names one buffer and each LDS-DMA write the
-    // other: the compiler can then see they do not overlap and does not wait
-    // for the in-flight loads before reading the current tile.
-    auto step = [&](int t, char *cur, char *nxt) {
-        const int valid = cur_valid;
-        const int owner = cur_owner;
-        // start loading the next tile; it lands in the other buffer while
-        // this one is computed
-        const bool has_next = t + 1 < n_tiles_total;
-        int nx_pos = 0;
-        uint32_t nx_gm = 0u;
-        if (has_next) {
-            ++it_tile;
+    if constexpr (!BF16) {
+        if (n_tiles_total > 0) {
             const int64_t origin = tile_origin(cur_valid, cur_owner);
-            load_keys(origin, cur_valid, cur_owner, nx_pos, nx_gm);
-            TL::prefetch(st, p, kvh, origin, nxt, nxt + TL::K_BYTES);
-        }
-
-        const int *kpos = reinterpret_cast<const int *>(cur + TL::K_BYTES + TL::V_BYTES);
-        const uint32_t *kgm = reinterpret_cast<const uint32_t *>(kpos + kKeyTile);
-        // Every wavefront computes, including one whose rows all lie past a
-        // ragged tile's end (its rows are masked and never stored): a branch
-        // here would split the accumulator's live range and cost a register
-        // copy of O per tile.
-        {
-            f32x16 s[2];
-            TL::qk(s, qf, cur, m, h);
-            // does any pair of this tile x wavefront need a mask?
-            bool masked;
-            if (GROUP) {
-                const int last_key = kpos[valid - 1];
-                masked = (valid < kKeyTile) || owner || ((int64_t)last_key > (int64_t)wq_min - w);
-            } else {
-                const int64_t j0 = kpos[0];
-                masked = !((j0 + kKeyTile - 1 <= wq_min) && (j0 > (int64_t)wq_max - w));
-            }
-            if (masked) {
-                // kgm holds zero unless this sub-bucket pair needs the owner
-                // test, so the test below is a no-op elsewhere
-                const int64_t lim = (int64_t)qpos - w;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int4 *kp4 = reinterpret_cast<const int4 *>(kpos + kb * 32 + h * 16);
-                    const uint4 *kg4 = reinterpret_cast<const uint4 *>(kgm + kb * 32 + h * 16);
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int4 kp = kp4[r4];
-                        const uint4 kg = kg4[r4];
-                        const int kv[4] = {kp.x, kp.y, kp.z, kp.w};
-                        const uint32_t kgv[4] = {kg.x, kg.y, kg.z, kg.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            bool keep;
-                            if (GROUP)
-                                keep = qvalid && ((int64_t)kv[e] <= lim) &&
-                                       ((kgv[e] & qlow) == 0u);
-                            else
-                                keep = qvalid && (kv[e] <= qpos) && ((int64_t)kv[e] > lim);
-                            s[kb][r4 * 4 + e] = keep ? s[kb][r4 * 4 + e] : -INFINITY;
-                        }
-                    }
-                }
-            }
-            typename TL::PFrag pf;
-            acc.softmax(s, p.c, pf);
-            TL::pv(acc.o, pf, cur + TL::K_BYTES, m, h);
-        }
-
-        if (has_next) {
-            TL::land(st, nxt, nxt + TL::K_BYTES);
-            store_keys(nxt, nx_pos, nx_gm);
+            int pos;
+            uint32_t gm;
+            load_keys(origin, cur_valid, cur_owner, pos, gm);
+            TL::prefetch(st, p, kvh, origin, stage(I0{}).k, stage(I0{}).v);
+            TL::land(st, stage(I0{}).k, stage(I0{}).v);
+            store_keys(I0{}, pos, gm, cur_valid, cur_owner);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    }
+
+    // Raw logits of one tile for this wavefront, masked where a pair falls
+    // outside the pass: QK^T on the tile's K rows, then (only on tiles that
+    // need it) the window / causal / owner tests on key positions in LDS.
+    auto scores = [&](f32x16 (&s)[2], auto I, int valid, int owner) {
+        const int *kpos = stage(I).key;
+        const uint32_t *kgm = reinterpret_cast<const uint32_t *>(kpos + kKeyTile);
+        TL::qk(s, qf, stage(I).k, lo);
+            // does any pair of this tile x wavefront need a mask?
+        bool masked;
+        if (GROUP) {
+            const int last_key = kpos[valid - 1];
+            masked = (valid < kKeyTile) || owner || (last_key > wq_min - w);
+        } else {
+            const int j0 = kpos[0];
+            masked = !((j0 + kKeyTile - 1 <= wq_min) && (j0 > wq_max - w));
+        }
+        if (masked) {
+            // Register r of lane half h holds key index kb*32 + h*16 + r of
+            // the tile; compare that against per-lane bounds shifted by h*16.
+            const int hshift = h * 16;
+            int lo, hi;  // kept key indices: lo <= index <= hi
+            if (GROUP) {
+                // positions ascend inside a sub-bucket, so keys inside the
+                // causal / window bound are a prefix of the tile's first
+                // `valid` keys: count them with a binary search
+                const int lim = qpos - w;
+                int cnt = 0;  // ends at min(count, 63); the last probe covers 64
+#pragma unroll
+                for (int step = kKeyTile / 2; step >= 1; step >>= 1)
+                    if (cnt + step - 1 < valid && kpos[cnt + step - 1] <= lim)
+                        cnt += step;
+                if (cnt < valid && kpos[cnt] <= lim)
+                    ++cnt;
+                lo = 0;
+                hi = cnt - 1;
+            } else {
+                // window pass: key index i is position j0 + i
+                const int j0 = kpos[0];
+                lo = qpos - w + 1 - j0;
+                hi = qpos - j0;
+            }
+            if (!qvalid)
+                hi = lo - 1;
+            // owner test (top-k >= 3 only): bit i of ok is set when key i
+            // shares no group below g with this lane's query.  A compact loop
+            // over broadcast reads keeps this rare path light on registers.
+            uint64_t ok = ~0ull;
+            if (GROUP && owner) {
+                ok = 0ull;
+#pragma unroll 1
+                for (int c = 0; c < kKeyTile / 4; ++c) {
+                    const uint4 kg = reinterpret_cast<const uint4 *>(kgm)[c];
+                    const uint32_t bits = ((kg.x & qlow) == 0u ? 1u : 0u) |
+                                          ((kg.y & qlow) == 0u ? 2u : 0u) |
+                                          ((kg.z & qlow) == 0u ? 4u : 0u) |
+                                          ((kg.w & qlow) == 0u ? 8u : 0u);
+                    ok |= (uint64_t)bits << (4 * c);
+                }
+            }
+            const uint32_t ok_lo = (uint32_t)(ok >> hshift);          // keys h*16 + 0..31
+            const uint32_t ok_hi = (uint32_t)(ok >> (32 + hshift));   // keys 32 + h*16 + 0..31
+            lo -= hshift;
+            hi -= hshift;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint32_t okb = kb ? ok_hi : ok_lo;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int idx = kb * 32 + r;
+                    const bool keep = idx >= lo && idx <= hi && ((okb >> r) & 1u);
+                    s[kb][r] = keep ? s[kb][r] : -INFINITY;
+                }
+            }
+        }
     };
-    for (int t = 0; t < n_tiles_total; t += 2) {
-        step(t, smem0, smem1);
-        if (t + 1 < n_tiles_total)
-            step(t + 1, smem1, smem0);
+
+    if constexpr (!BF16) {
+        // Plain schedule: compute on `cur` while the next tile streams into
+        // `nxt`; one barrier per tile.  The two LDS buffers are distinct
+        // arrays and the loop is unrolled by two, so each LDS read names one
+        // buffer and each LDS write the other.
+        auto step = [&](int t, auto CUR, auto NXT) {
+            const int valid = cur_valid;
+            const int owner = cur_owner;
+            const bool has_next = t + 1 < n_tiles_total;
+            int nx_pos = 0;
+            uint32_t nx_gm = 0u;
+            if (has_next) {
+                ++it_tile;
+                const int64_t origin = tile_origin(cur_valid, cur_owner);
+                load_keys(origin, cur_valid, cur_owner, nx_pos, nx_gm);
+                TL::prefetch(st, p, kvh, origin, stage(NXT).k, stage(NXT).v);
+            }
+            // Every wavefront computes, including one whose rows all lie past
+            // a ragged tile's end (its rows are masked and never stored): a
+            // branch here would split the accumulator's live range and cost
+            // a register copy of O per tile.
+            f32x16 s[2];
+            TL::refresh(lo);
+            scores(s, CUR, valid, owner);
+            typename TL::PFrag pf;
+            acc.softmax(s, p.c, pf);
+            TL::pv(acc.o, pf, stage(CUR).v, lo);
+            if (has_next) {
+                TL::land(st, stage(NXT).k, stage(NXT).v);
+                store_keys(NXT, nx_pos, nx_gm, cur_valid, cur_owner);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+        for (int t = 0; t < n_tiles_total; t += 2) {
+            step(t, I0{}, I1{});
+            if (t + 1 < n_tiles_total)
+                step(t + 1, I1{}, I0{});
+        }
+    } else {
+        // Two-role (staggered) schedule.  Each SIMD runs one wavefront of
+        // role A (waves 0-3) and one of role B (waves 4-7); one block barrier
+        // closes each tile interval u:
+        //     A: QK(u), softmax(u), PV(u)
+        //     B: softmax(u-1), PV(u-1), QK(u)
+        // so within an interval A starts on the matrix cores while B starts
+        // on the vector ALUs, and the SIMD overlaps the two.  B finishes the
+        // last tile in one extra interval.  Tile u lives in stage u % 4; its
+        // loads (K, V^T, key positions and group bits, all LDS-DMA) are
+        // issued at the start of interval u - 2 and awaited at the end of
+        // interval u - 1, two intervals of latency cover.  Both roles pass
+        // exactly one barrier per interval.
+        const int T = n_tiles_total;
+        // LDS-DMA loads each wavefront issues per tile (waited on by count)
+        constexpr int DMA_KV = 2 * TL::LOADS;
+        const bool key_wave = GROUP && __builtin_amdgcn_readfirstlane(wave) == 0;
+        auto issue = [&](auto I) {
+            int nv, no;
+            const int64_t origin = tile_origin(nv, no);
+            TL::prefetch(st, p, kvh, origin, stage(I).k, stage(I).v);
+            int *kp = stage(I).key;
+            if (GROUP) {
+                if (key_wave) {
+                    dma4(etk + origin, (uint32_t)lane * 4u, lds_address(kp));
+                    dma4(egh + origin, (uint32_t)lane * 4u, lds_address(kp) + kKeyTile * 4);
+                }
+            } else if (threadIdx.x < kKeyTile) {
+                kp[threadIdx.x] = (int)(origin + threadIdx.x);
+            }
+            if (threadIdx.x == 0) {
+                kp[2 * kKeyTile] = nv;
+                kp[2 * kKeyTile + 1] = no;
+            }
+        };
+        // end of an interval: everything but the newest tile's loads landed,
+        // this interval's LDS traffic done, then the block barrier
+        // (s_waitcnt immediates on gfx950: vmcnt in bits 3:0, expcnt 6:4,
+        // lgkmcnt 11:8; 0x70 | n = "vmcnt(n) lgkmcnt(0)", expcnt untouched.
+        // The builtin, unlike inline asm, is visible to the compiler's own
+        // wait tracking, so it adds no waits of its own for these loads.)
+        auto close_interval = [&](bool newest_in_flight) {
+            if (!newest_in_flight)
+                __builtin_amdgcn_s_waitcnt(0x70);
+            else if (key_wave)
+                __builtin_amdgcn_s_waitcnt(0x70 | (DMA_KV + 2));
+            else
+                __builtin_amdgcn_s_waitcnt(0x70 | DMA_KV);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        static_assert(!BF16 || TL::LOADS == 1 || TL::LOADS == 2, "vmcnt counts assume 1-2 loads");
+
+        // prologue: tiles 0 and 1 (tile 0's iterator position is current)
+        if (T > 0)
+            issue(I0{});
+        if (T > 1) {
+            ++it_tile;
+            issue(I1{});
+        }
+        __builtin_amdgcn_s_waitcnt(0x70);
+        __syncthreads();
+
+        auto run = [&](auto role_tag) {
+            constexpr bool ROLE_A = decltype(role_tag)::value;
+            f32x16 s[2];
+            typename TL::PFrag pf;
+            auto interval = [&](int u, auto PREV, auto CUR, auto AHEAD) {
+                const bool ahead = u + 2 < T;
+                if (ahead) {
+                    ++it_tile;
+                    issue(AHEAD);
+                }
+                TL::refresh(lo);
+                if (ROLE_A) {
+                    if (u < T) {
+                        int valid, owner;
+                        stage_meta(CUR, valid, owner);
+                        scores(s, CUR, valid, owner);
+                        acc.softmax(s, p.c, pf);
+                        TL::pv(acc.o, pf, stage(CUR).v, lo);
+                    }
+                } else {
+                    if (u >= 1) {
+                        acc.softmax(s, p.c, pf);
+                        TL::pv(acc.o, pf, stage(PREV).v, lo);
+                    }
+                    if (u < T) {
+                        int valid, owner;
+                        stage_meta(CUR, valid, owner);
+                        scores(s, CUR, valid, owner);
+                    }
+                }
+                close_interval(ahead);
+            };
+            for (int u = 0; u <= T; u += 4) {
+                interval(u, I3{}, I0{}, I2{});
+                if (u + 1 <= T)
+                    interval(u + 1, I0{}, I1{}, I3{});
+                if (u + 2 <= T)
+                    interval(u + 2, I1{}, I2{}, I0{});
+                if (u + 3 <= T)
+                    interval(u + 3, I2{}, I3{}, I1{});
+            }
+        };
+        if (__builtin_amdgcn_readfirstlane(wave) < kWavesPerRole)
+            run(std::true_type{});
+        else
+            run(std::false_type{});
     }
 
     if (!wave_active)
@@ -831,18 +1131,29 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(
     }
 }
 
-// egm[h][e] = gmask[h][tokens[h][e]]: the group bits of every bucket entry, in
-// bucket order, so a tile's owner test reads them without a dependent load.
-__global__ __launch_bounds__(256) void gather_gmask_kernel(const uint32_t *__restrict__ gmask,
-                                                           const int32_t *__restrict__ tokens,
-                                                           int64_t n, int64_t E, int H,
-                                                           uint32_t *__restrict__ egm)
+// Bucket-order copies padded to a whole extra key tile: etok[h][e] =
+// tokens[h][e] and egm[h][e] = gmask[h][tokens[h][e]] (the group bits of every
+// entry), with INT_MAX / 0 past the last entry, so a key tile's positions and
+// group bits load as one contiguous block that never leaves the array.
+__global__ __launch_bounds__(256) void gather_entries_kernel(const uint32_t *__restrict__ gmask,
+                                                             const int32_t *__restrict__ tokens,
+                                                             int64_t n, int64_t E, int64_t estride,
+                                                             int H, int32_t *__restrict__ etok,
+                                                             uint32_t *__restrict__ egm)
 {
-    const int64_t total = (int64_t)H * E;
+    const int64_t total = (int64_t)H * estride;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t h = i / E;
-        egm[i] = gmask[h * n + tokens[i]];
+        const int64_t h = i / estride;
+        const int64_t e = i % estride;
+        if (e < E) {
+            const int32_t t = tokens[h * E + e];
+            etok[i] = t;
+            egm[i] = gmask[h * n + t];
+        } else {
+            etok[i] = 0x7fffffff;
+            egm[i] = 0u;
+        }
     }
 }
 
@@ -884,7 +1195,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
 struct Layout {
     int hpb, nhg, rows_group, max_tiles;
     int64_t E, e_pad, n_pad;
-    size_t kb, vb, vt, egm, po, pl, tiles, ntiles, total;
+    size_t kb, vb, kp, vt, etok, egm, po, pl, tiles, ntiles, total;
 };
 
 int heads_per_block(int ratio)
@@ -916,8 +1227,10 @@ Layout make_layout(const AttnShape &sh)
     };
     L.kb = take((size_t)sh.hkv * L.e_pad * sh.d * es);
     L.vb = take((size_t)sh.hkv * L.e_pad * sh.d * es);
+    L.kp = take(sh.dt == FOCUS_BF16 ? (size_t)sh.hkv * L.n_pad * sh.d * 2 : 0);
     L.vt = take(sh.dt == FOCUS_BF16 ? (size_t)sh.hkv * sh.d * L.n_pad * 2 : 0);
-    L.egm = take((size_t)sh.hkv * L.E * 4);
+    L.etok = take((size_t)sh.hkv * L.e_pad * 4);
+    L.egm = take((size_t)sh.hkv * L.e_pad * 4);
     L.po = take((size_t)sh.hq * L.E * sh.d * 4);
     L.pl = take((size_t)sh.hq * L.E * 4);
     L.tiles = take((size_t)sh.hkv * L.max_tiles * sizeof(int4));
@@ -999,7 +1312,8 @@ size_t dense_workspace_bytes(const AttnShape &sh)
     if (sh.dt != FOCUS_BF16)
         return 256;
     const int64_t n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
-    return align_up((size_t)sh.hkv * sh.d * n_pad * 2, 256);
+    // transposed values and a zero-padded copy of the keys
+    return 2 * align_up((size_t)sh.hkv * sh.d * n_pad * 2, 256);
 }
 
 hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const void *v,
@@ -1026,6 +1340,9 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
             if (e == hipSuccess)
                 e = launch_transpose(sh.d, V, nullptr, sh.n, sh.n, L.n_pad, sh.hkv,
                                      reinterpret_cast<__bf16 *>(w + L.vt), s);
+            if (e == hipSuccess)
+                e = launch_gather(sh.d, K, (const int32_t *)nullptr, sh.n, sh.n, L.n_pad, sh.hkv,
+                                  reinterpret_cast<__bf16 *>(w + L.kp), s);
         } else {
             auto K = static_cast<const float *>(k);
             auto V = static_cast<const float *>(v);
@@ -1038,10 +1355,11 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
         if (e != hipSuccess)
             return e;
         {
-            const int64_t total = (int64_t)sh.hkv * L.E;
+            const int64_t total = (int64_t)sh.hkv * L.e_pad;
             const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
-            hipLaunchKernelGGL(gather_gmask_kernel, dim3(blocks), dim3(256), 0, s, gmask, tokens,
-                               sh.n, L.E, sh.hkv, reinterpret_cast<uint32_t *>(w + L.egm));
+            hipLaunchKernelGGL(gather_entries_kernel, dim3(blocks), dim3(256), 0, s, gmask, tokens,
+                               sh.n, L.E, L.e_pad, sh.hkv, reinterpret_cast<int32_t *>(w + L.etok),
+                               reinterpret_cast<uint32_t *>(w + L.egm));
             e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
@@ -1058,7 +1376,9 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
     p.tokens = tokens;
     p.offsets = offsets;
     p.gmask = gmask;
+    p.etok = reinterpret_cast<const int32_t *>(w + L.etok);
     p.egm = reinterpret_cast<const uint32_t *>(w + L.egm);
+    p.estride = L.e_pad;
     p.part_o = reinterpret_cast<float *>(w + L.po);
     p.part_lse = reinterpret_cast<float *>(w + L.pl);
     p.slot_entry = slot_entry;
@@ -1081,9 +1401,9 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
     }
     if (parts & FOCUS_PART_WINDOW) {
         Params wp = p;
-        wp.kmat = k;
+        wp.kmat = bf16 ? (const void *)(w + L.kp) : k;
         wp.vmat = bf16 ? (const void *)(w + L.vt) : v;
-        wp.krows = sh.n;
+        wp.krows = bf16 ? L.n_pad : sh.n;
         wp.vcols = L.n_pad;
         wp.merge = 1;
         wp.row_tiles = (int)((sh.n + (kRowsPerBlock / L.hpb) - 1) / (kRowsPerBlock / L.hpb));
@@ -1104,17 +1424,23 @@ hipError_t launch_dense(const AttnShape &sh, const void *q, const void *k, const
     const bool bf16 = sh.dt == FOCUS_BF16;
     const int64_t n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
     hipError_t e = hipSuccess;
+    const size_t half = align_up((size_t)sh.hkv * sh.d * n_pad * 2, 256);
+    __bf16 *vt = static_cast<__bf16 *>(ws);
+    __bf16 *kp = reinterpret_cast<__bf16 *>(static_cast<char *>(ws) + half);
     if (bf16) {
-        e = launch_transpose(sh.d, static_cast<const __bf16 *>(v), nullptr, sh.n, sh.n,
-                             n_pad, sh.hkv, static_cast<__bf16 *>(ws), s);
+        e = launch_transpose(sh.d, static_cast<const __bf16 *>(v), nullptr, sh.n, sh.n, n_pad,
+                             sh.hkv, vt, s);
+        if (e == hipSuccess)
+            e = launch_gather(sh.d, static_cast<const __bf16 *>(k), (const int32_t *)nullptr,
+                              sh.n, sh.n, n_pad, sh.hkv, kp, s);
         if (e != hipSuccess)
             return e;
     }
     Params p = base_params(d, L);
     p.q = q;
-    p.kmat = k;
-    p.vmat = bf16 ? ws : v;
-    p.krows = sh.n;
+    p.kmat = bf16 ? (const void *)kp : k;
+    p.vmat = bf16 ? (const void *)vt : v;
+    p.krows = bf16 ? n_pad : sh.n;
     p.vcols = n_pad;
     p.merge = 0;
     p.out = out;
