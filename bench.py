@@ -16,16 +16,40 @@ length of the pages' headline speedup.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
+from pathlib import Path
 
 import numpy as np
 
 METRIC = "Focus attn fwd tokens/s + % bf16 MFMA peak at 128K–1M tokens, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
+
+
+ROOT = Path(__file__).resolve().parent
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per group-kernel launch from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE, copy-calibrated),
+    or None when there is none or the kernel source changed since."""
+    path = ROOT / "profiles" / f"attn_{workload}.md"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    m_hash = re.search(r"sha256: `([0-9a-f]{64})`", text)
+    m_bytes = re.search(r"group_kernel_traffic_bytes_per_launch: ([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes:
+        return None
+    h = hashlib.sha256()
+    for name in ("attn.hip", "common.hpp"):
+        h.update((ROOT / "centroid_gated_sparse_amd" / "csrc" / name).read_bytes())
+    return float(m_bytes.group(1)) if h.hexdigest() == m_hash.group(1) else None
 
 
 def log(msg: str) -> None:
@@ -232,7 +256,8 @@ def main() -> int:
                    "head_dim": wl.d, "centroids": K, "topk": topk, "window": wl.window,
                    "batch": 1, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": recorded_traffic(wl.name),
                      "kernel": "attn_kernel group pass (focus_attn_fwd part GROUP)"},
         "detail": {
             "part_ms": part_ms,
