@@ -32,6 +32,8 @@ PEAK_F32_TFLOPS = 157.3
 
 
 ROOT = Path(__file__).resolve().parent
+# sources of the attention kernels (their hash keys the recorded counters)
+ATTN_SOURCES = ("attn.hip", "attn_common.hpp", "common.hpp")
 
 
 def recorded_traffic(workload: str):
@@ -47,7 +49,7 @@ def recorded_traffic(workload: str):
     if not m_hash or not m_bytes:
         return None
     h = hashlib.sha256()
-    for name in ("attn.hip", "common.hpp"):
+    for name in ATTN_SOURCES:
         h.update((ROOT / "centroid_gated_sparse_amd" / "csrc" / name).read_bytes())
     return float(m_bytes.group(1)) if h.hexdigest() == m_hash.group(1) else None
 
