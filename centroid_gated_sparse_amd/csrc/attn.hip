@@ -165,33 +165,62 @@ struct Tile<D, true> {
             asm volatile("" : "+v"(o.v[j]));
     }
 
+    // The LDS reads of both products run ahead of the MFMAs that consume
+    // them (two k-steps for S^T, one 16-key step for O^T), the order pinned
+    // by scheduling fences: left alone, the scheduler issues each read just
+    // before its use and the LDS latency stalls the matrix core.
+    // (fence mask: VALU 0x2, SALU 0x4 and transcendental 0x400
+    // instructions may cross, so the softmax still interleaves with the
+    // MFMAs; LDS reads and MFMAs keep their order)
+    static constexpr int kQkAhead = 2;
+    static constexpr int kFence = 0x406;
     // S^T[key][query] for the two 32-key blocks of the tile.
     __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const char *kl, const LdsOff &o)
     {
+        constexpr int AHEAD = kQkAhead < KS ? kQkAhead : KS;
         s[0] = f32x16{};
         s[1] = f32x16{};
+        bf16x8 f[AHEAD + 1][2];
+        auto load = [&](bf16x8 (&g)[2], int ks) {
+            g[0] = *reinterpret_cast<const bf16x8 *>(kl + o.k[ks]);
+            g[1] = *reinterpret_cast<const bf16x8 *>(kl + o.k[ks] + 32 * D * 2);
+        };
+#pragma unroll
+        for (int ks = 0; ks < AHEAD; ++ks)
+            load(f[ks], ks);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kl + o.k[ks]);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kl + o.k[ks] + 32 * D * 2);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf.v[ks], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf.v[ks], s[1], 0, 0, 0);
+            if (ks + AHEAD < KS)
+                load(f[(ks + AHEAD) % (AHEAD + 1)], ks + AHEAD);
+            __builtin_amdgcn_sched_barrier(kFence);
+            const bf16x8(&g)[2] = f[ks % (AHEAD + 1)];
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[0], qf.v[ks], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g[1], qf.v[ks], s[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(kFence);
         }
     }
 
-    // O^T[d][query] += V^T P^T.
+    // O^T[d][query] += V^T P^T, one 16-key step j = kb * 2 + kk at a time.
     __device__ static void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vl, const LdsOff &lo)
     {
+        bf16x8 f[2][DB];
+        auto load = [&](bf16x8 (&g)[DB], int j) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int db = 0; db < DB; ++db)
+                g[db] = *reinterpret_cast<const bf16x8 *>(vl + lo.v[j] + db * 32 * 64 * 2);
+        };
+        load(f[0], 0);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+        for (int j = 0; j < 4; ++j) {
+            if (j + 1 < 4)
+                load(f[(j + 1) % 2], j + 1);
+            __builtin_amdgcn_sched_barrier(kFence);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vl + lo.v[kb * 2 + kk] +
-                                                                        db * 32 * 64 * 2);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.v[kb][kk], o[db], 0, 0, 0);
-                }
+            for (int db = 0; db < DB; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[j % 2][db], pf.v[j >> 1][j & 1],
+                                                                o[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(kFence);
+        }
     }
 
     // Exponentials of one tile -> bf16 P fragments; returns their fp32 sum.
