@@ -16,8 +16,11 @@
 //     the row by log-sum-exp.
 //
 // Kernel design (gfx950, CDNA4):
-//   * 256 threads = 4 wavefronts; each wavefront owns 64 query rows as two
-//     32-row blocks and holds Q in registers for the whole key loop.
+//   * 512 threads = 8 wavefronts, two per SIMD; each wavefront owns 32
+//     query rows and holds Q in registers for the whole key loop.  The
+//     softmax's vector work is spread over both wavefronts of a SIMD: one
+//     wavefront alone issues vector instructions at about half the SIMD's
+//     rate.
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16 (fp32 inputs:
 //     v_mfma_f32_32x32x2f32).  Computing the transposes puts one query per
 //     lane column, so row max / row sum need one cross-half exchange per tile
@@ -26,10 +29,13 @@
 //     register r of the S^T accumulator is key h*16 + r: the P fragment for
 //     one 32x32x16 step is then 8 consecutive keys, matching one 16-byte read
 //     of the V^T tile.
-//   * K and V^T tiles of 64 keys are staged through LDS (XOR-swizzled, double
-//     buffered, one barrier per tile).  Keys and values are first gathered
-//     into bucket order (and V transposed) by a prepare pass, so every tile
-//     load in the hot loop is contiguous.
+//   * K and V^T tiles of 64 keys are staged through LDS (XOR-swizzled), loaded
+//     straight into LDS two tiles ahead over four stages (bf16; the fp32 path
+//     double-buffers through registers); one barrier per tile.  Keys and
+//     values are first gathered into bucket order (and V transposed) by a
+//     prepare pass, so every tile load in the hot loop is contiguous.
+//   * bf16: the two wavefronts of a SIMD run staggered roles (see the key
+//     loop), so one wavefront's vector work overlaps the other's MFMAs.
 //   * Grouped-query heads sharing a key/value head are packed into one block
 //     (up to 4 heads x 64 rows), sharing every K/V tile and mask.
 //   * Online softmax in the exp2 domain with lazy rescaling: the running max
