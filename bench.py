@@ -134,6 +134,128 @@ def cpu_baseline(wl, seed, q, k, v, groups_np, r, c, budget_s: float):
     }
 
 
+def make_step(F, wl, q, k, v, rt, ct):
+    """Buffers of one workload and its step: route -> bucket -> attention
+    (prepare, group, window + merge), each part bracketed by optional
+    events."""
+    import torch
+
+    dev = q.device
+    H, n, K, topk = wl.hkv, wl.n, wl.K, wl.topk
+    i32 = dict(dtype=torch.int32, device=dev)
+    b = {
+        "groups": torch.empty((H, n, topk), **i32),
+        "gmask": torch.empty((H, n), **i32),
+        "offsets": torch.empty((H, K * (K + 1) + 1), **i32),
+        "tokens": torch.empty((H, n * topk), **i32),
+        "slot_entry": torch.empty((H, n, topk), **i32),
+        "bws": torch.empty(max(F.focus_bucket_workspace_bytes(H, n, K, topk), 16),
+                           dtype=torch.uint8, device=dev),
+        "out": torch.empty_like(q),
+        "lse": torch.empty((wl.hq, n), dtype=torch.float32, device=dev),
+    }
+    dt_code = F.FOCUS_BF16 if wl.dtype == "bf16" else F.FOCUS_F32
+    b["aws"] = torch.empty(F.focus_attn_workspace_bytes(dt_code, wl.hq, H, n, wl.d, K, topk),
+                           dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        F.focus_route(rt, ct, topk, b["groups"], b["gmask"])
+        mark(1)
+        F.focus_bucket(b["groups"], K, b["offsets"], b["tokens"], b["slot_entry"], b["bws"])
+        mark(2)
+        args_ = (q, k, v, b["gmask"], b["offsets"], b["tokens"], b["slot_entry"], K, wl.window,
+                 wl.scale, b["out"], b["lse"], b["aws"])
+        F.focus_attn_fwd_part(*args_, parts=F.PART_PREPARE)
+        mark(3)
+        F.focus_attn_fwd_part(*args_, parts=F.PART_GROUP)
+        mark(4)
+        F.focus_attn_fwd_part(*args_, parts=F.PART_WINDOW)
+        mark(5)
+
+    return step, b
+
+
+def timed_ms(fn, warmup: int, steps: int) -> float:
+    """Median time of fn() over `steps` runs after `warmup`, by events on
+    the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+# Speed against full attention that the pages report in Table 6 (H100,
+# FlashAttention on both sides; shape and window not stated): context
+# only, printed next to this sweep's own ratio.
+TABLE6_PAGES = {4: (0.2, 0.5, 1.5, 2.2, 3.0, 4.0, 4.1), 8: (0.2, 0.6, 1.8, 3.1, 4.7, 7.6, 8.6)}
+
+
+def run_sweep(steps: int, warmup: int) -> int:
+    """Focus step against our dense causal kernel over the Table 6 context
+    lengths and group counts (top-1, 7B-style GQA layer, w = 1024); one
+    JSON object with a row per (K, n)."""
+    import torch
+
+    from centroid_gated_sparse_amd import focus as F
+    from centroid_gated_sparse_amd.workloads import (TABLE6_CONTEXTS, TABLE6_GROUPS,
+                                                     qkv_inputs, routing_inputs, seed_for,
+                                                     table6_workload)
+
+    F.lib()
+    rows = []
+    for i, n in enumerate(TABLE6_CONTEXTS):
+        base = table6_workload(n, TABLE6_GROUPS[0])
+        q, k, v = qkv_inputs(base, seed_for(base.name), "cuda")
+        dws = torch.empty(max(F.focus_dense_workspace_bytes(F.FOCUS_BF16, base.hkv, n, base.d),
+                              16), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+        lse = torch.empty((base.hq, n), dtype=torch.float32, device="cuda")
+        dense_ms = timed_ms(lambda: F.focus_dense_causal_fwd(q, k, v, base.scale, out, lse, dws),
+                            1, max(1, min(steps, 2) if n > 300000 else steps))
+        del dws, out, lse
+        for K in TABLE6_GROUPS:
+            wl = table6_workload(n, K)
+            c, r, _ = routing_inputs(wl, seed_for(wl.name))
+            rt = torch.from_numpy(r).cuda()
+            ct = torch.from_numpy(c).cuda()
+            step, b = make_step(F, wl, q, k, v, rt, ct)
+            focus_ms = timed_ms(step, warmup, steps)
+            surv = int(surviving_pairs(b["groups"].cpu().numpy(), K, wl.window).sum()) * (
+                wl.hq // wl.hkv)
+            dense_pairs = wl.hq * n * (n + 1) // 2
+            rows.append({
+                "n": n, "K": K, "topk": wl.topk, "window": wl.window,
+                "focus_ms": focus_ms, "dense_ms": dense_ms,
+                "speedup_vs_dense": dense_ms / focus_ms,
+                "focus_tokens_per_s": n / (focus_ms / 1e3),
+                "pairs_kept_vs_dense": surv / dense_pairs,
+                "focus_tflops_surviving": 4.0 * wl.d * surv / (focus_ms / 1e3) / 1e12,
+                "dense_tflops": 4.0 * wl.d * dense_pairs / (dense_ms / 1e3) / 1e12,
+                "pages_table6_speedup_h100": TABLE6_PAGES[K][i],
+            })
+            log(f"sweep: n={n} K={K} focus {focus_ms:.2f} ms dense {dense_ms:.2f} ms "
+                f"-> {dense_ms / focus_ms:.2f}x")
+            del step, b, rt, ct
+        del q, k, v
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "table6_contexts", "model": "gqa7b 32/8 heads d128 bf16",
+                      "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +266,8 @@ def main() -> int:
                     help="seconds of oracle attention time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the Table 6 context sweep (Focus vs our dense kernel)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three "
                          "times (scales the HBM byte counters)")
@@ -164,6 +288,9 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}))
         return 0
 
+    if args.sweep:
+        return run_sweep(args.steps, args.warmup)
+
     from centroid_gated_sparse_amd import focus as F
     from centroid_gated_sparse_amd.workloads import (WORKLOADS, qkv_inputs, routing_inputs,
                                                      seed_for)
@@ -177,41 +304,13 @@ def main() -> int:
     rt = torch.from_numpy(r).to(dev)
     ct = torch.from_numpy(c).to(dev)
     q, k, v = qkv_inputs(wl, seed, dev)
+    step, bufs = make_step(F, wl, q, k, v, rt, ct)
+    groups, aws = bufs["groups"], bufs["aws"]
     H, n, K, topk = wl.hkv, wl.n, wl.K, wl.topk
-    i32 = dict(dtype=torch.int32, device=dev)
-    groups = torch.empty((H, n, topk), **i32)
-    gmask = torch.empty((H, n), **i32)
-    offsets = torch.empty((H, K * (K + 1) + 1), **i32)
-    tokens = torch.empty((H, n * topk), **i32)
-    slot_entry = torch.empty((H, n, topk), **i32)
-    bws = torch.empty(max(F.focus_bucket_workspace_bytes(H, n, K, topk), 16),
-                      dtype=torch.uint8, device=dev)
     dt_code = F.FOCUS_BF16 if wl.dtype == "bf16" else F.FOCUS_F32
-    aws = torch.empty(F.focus_attn_workspace_bytes(dt_code, wl.hq, H, n, wl.d, K, topk),
-                      dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((wl.hq, n), dtype=torch.float32, device=dev)
+    out, lse = bufs["out"], bufs["lse"]
     log(f"bench: workspace {aws.numel() / 2**30:.2f} GiB")
-
     names = ["route", "bucket", "prepare", "group", "window"]
-
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record()
-        mark(0)
-        F.focus_route(rt, ct, topk, groups, gmask)
-        mark(1)
-        F.focus_bucket(groups, K, offsets, tokens, slot_entry, bws)
-        mark(2)
-        args_ = (q, k, v, gmask, offsets, tokens, slot_entry, K, wl.window, wl.scale, out, lse,
-                 aws)
-        F.focus_attn_fwd_part(*args_, parts=F.PART_PREPARE)
-        mark(3)
-        F.focus_attn_fwd_part(*args_, parts=F.PART_GROUP)
-        mark(4)
-        F.focus_attn_fwd_part(*args_, parts=F.PART_WINDOW)
-        mark(5)
 
     for i in range(args.warmup):
         step()
@@ -294,7 +393,7 @@ def main() -> int:
         log(f"bench: dense causal {dense_ms:.1f} ms")
 
     if not args.no_cpu_baseline:
-        del aws
+        del aws, out, lse, bufs, step
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(wl, seed, q, k, v, groups.cpu().numpy(), r, c,
                                               args.cpu_budget)

@@ -70,8 +70,28 @@ WORKLOADS = {
 WORKLOAD_ORDER = list(WORKLOADS)
 
 
+# Context-length sweep in the shape of Table 6 (speed against full attention
+# from 1K to 1M tokens, K = 4 and K = 8 centroid groups).  The pages give
+# neither the model nor the window there; the sweep uses the 7B-style
+# grouped-query layer above, top-1 membership (the O(n^2/K + n*w) reading)
+# and w = 1024.
+TABLE6_CONTEXTS = (1024, 4096, 16384, 32768, 65536, 262144, 1048576)
+TABLE6_GROUPS = (4, 8)
+
+
+def table6_workload(n: int, K: int) -> Workload:
+    return Workload(f"table6_gqa7b_n{n}_k{K}", n, 32, 8, 128, K, 1, 1024, "bf16",
+                    qkv_std=1.0 / math.sqrt(128))
+
+
 def seed_for(name: str) -> int:
-    return 1000 + WORKLOAD_ORDER.index(name) if name in WORKLOAD_ORDER else 4242
+    if name in WORKLOAD_ORDER:
+        return 1000 + WORKLOAD_ORDER.index(name)
+    for i, n in enumerate(TABLE6_CONTEXTS):
+        for j, K in enumerate(TABLE6_GROUPS):
+            if name == f"table6_gqa7b_n{n}_k{K}":
+                return 2000 + 10 * i + j
+    return 4242
 
 
 def _streams(seed: int):

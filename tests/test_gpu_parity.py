@@ -226,3 +226,41 @@ def test_workload_full_size(name):
     rel = np.abs(got / cnt[hk] - 1.0).max()
     log(f"[{name}] count probe max rel err {rel:.3e}")
     assert rel < 1e-5
+
+
+# ----------------------------------------------------------------------------
+# the context sweep in the shape of Table 6 (top-1, K = 4 / 8, 7B GQA layer,
+# w = 1024): every row at 1K, sampled rows beyond, plus the count probe
+
+TABLE6_CASES = [(1024, 4, None), (1024, 8, None), (16384, 4, 1024), (16384, 8, 1024),
+                (1048576, 8, 256)]
+
+
+@pytest.mark.parametrize("n,K,nrows", TABLE6_CASES,
+                         ids=[f"n{n}_k{K}" for n, K, _ in TABLE6_CASES])
+def test_table6_sweep_shapes(n, K, nrows):
+    from centroid_gated_sparse_amd.workloads import table6_workload
+
+    wl = table6_workload(n, K)
+    seed = seed_for(wl.name)
+    log(f"sweep {wl.name}: generating")
+    c, r, _ = routing_inputs(wl, seed)
+    q, k, v = qkv_inputs(wl, seed, DEV)
+    res = gpu_forward(wl, c, r, q, k, v)
+    g_ref, _ = oracle.route(r, c, wl.topk)
+    assert np.array_equal(res["groups"].cpu().numpy(), g_ref)
+    if nrows is None:
+        rh = np.repeat(np.arange(wl.hq, dtype=np.int32), wl.n)
+        rp = np.tile(np.arange(wl.n, dtype=np.int64), wl.hq)
+    else:
+        rh, rp = sample_rows(wl, seed, nrows)
+    check_rows(wl, res, q, k, v, g_ref, rh, rp, wl.name)
+    del res
+    q.zero_()
+    res0 = gpu_forward(wl, c, r, q, k, v)
+    cnt = oracle.pair_counts(g_ref, wl.K, wl.window)
+    hk = np.arange(wl.hq) // (wl.hq // wl.hkv)
+    got = np.exp(res0["lse"].cpu().double().numpy())
+    rel = np.abs(got / cnt[hk] - 1.0).max()
+    log(f"[{wl.name}] count probe max rel err {rel:.3e}")
+    assert rel < 1e-5
