@@ -61,8 +61,9 @@ def _load():
     lib.oracle_attn_rows.argtypes = [P, i32, P, P, i32, i32, i32, i64, i32, P, i32, i32,
                                      i64, f64, P, P, i64, P, P, P, i32]
     lib.oracle_pair_counts.argtypes = [P, i32, i64, i32, i32, i64, P]
+    lib.oracle_project.argtypes = [P, i32, i64, i32, P, P]
     for f in (lib.oracle_route, lib.oracle_bucket, lib.oracle_attn_rows,
-              lib.oracle_pair_counts):
+              lib.oracle_pair_counts, lib.oracle_project):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -94,6 +95,34 @@ def route(r: np.ndarray, centroids: np.ndarray, topk: int):
     _check(_load().oracle_route(_ptr(r), _ptr(c), H, n, dg, K, topk,
                                 _ptr(groups), _ptr(gmask)), "route")
     return groups, gmask
+
+
+def project(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Routing projection r = W x of every token, in the fixed fp32 order.
+
+    x: [n, d_model] float32, or uint16 bf16 bit patterns; W: float32 [16, d_model].
+    Returns r float32 [n, 16].
+    """
+    is_bf16 = x.dtype == np.uint16
+    x = np.ascontiguousarray(x)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    n, dm = x.shape
+    assert W.shape == (16, dm)
+    r = np.empty((n, 16), np.float32)
+    _check(_load().oracle_project(_ptr(x), int(is_bf16), n, dm, _ptr(W), _ptr(r)), "project")
+    return r
+
+
+def route_project(x: np.ndarray, W: np.ndarray, centroids: np.ndarray, topk: int):
+    """Projection shared by all routing heads, then each head's top-k.
+
+    Returns (r float32 [n, 16], groups int32 [H, n, topk], gmask uint32 [H, n]).
+    """
+    r = project(x, W)
+    H = centroids.shape[0]
+    rh = np.ascontiguousarray(np.broadcast_to(r, (H,) + r.shape))
+    groups, gmask = route(rh, centroids, topk)
+    return r, groups, gmask
 
 
 def bucket(groups: np.ndarray, K: int):

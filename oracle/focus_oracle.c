@@ -103,6 +103,47 @@ int oracle_route(const float *r, const float *centroids, int32_t H, int64_t n,
     return ORACLE_OK;
 }
 
+/* One input element as fp32 (bf16 bit patterns widen exactly). */
+static float load_as_f32(const void *base, int is_bf16, int64_t idx)
+{
+    if (is_bf16) {
+        uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return f;
+    }
+    return ((const float *)base)[idx];
+}
+
+/* Routing projection (Technical Summary, Core Architecture, Token Grouping:
+ * a token's hidden state is projected into the 16-dimensional centroid
+ * space before it is scored; the parameter counts of the thelatestinai.com
+ * Tables 2 and 3, 148K on GPT-2 124M and 2.1M on a 7B model, match one
+ * d_model x 16 matrix plus the centroids per layer):
+ *     r[t][j] = sum over e = 0 .. dm-1 of W[j][e] * x[t][e]
+ * fp32 products of W and x (bf16 x widened exactly), added in index order
+ * starting from 0, no fused multiply-add: the same convention as the score,
+ * so the projected vectors are bit-reproducible.  W is [16][dm], x [n][dm],
+ * r [n][16]. */
+int oracle_project(const void *x, int32_t is_bf16, int64_t n, int32_t dm,
+                   const float *W, float *r)
+{
+    if (!x || !W || !r || n < 1 || dm < 1)
+        return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        for (int j = 0; j < 16; ++j) {
+            float s = 0.0f;
+            for (int e = 0; e < dm; ++e) {
+                float p = W[(int64_t)j * dm + e] * load_as_f32(x, is_bf16, t * dm + e);
+                s = s + p;
+            }
+            r[t * 16 + j] = s;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Partner of token t inside group g: its lowest group other than g, or K when
  * it belongs to g alone (top-1). */
 static int partner_of(const int32_t *gt, int topk, int g, int K)

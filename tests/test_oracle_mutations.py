@@ -29,6 +29,12 @@ MUTATIONS = {
     "count_far_edge": ("int64_t far_end = i - w;", "int64_t far_end = i - w + 1;"),
     "value_index": ("acc[e] += p * widen(v, is_bf16, vb + e);",
                     "acc[e] += p * widen(v, is_bf16, kb_unused(vb) + e);"),
+    "project_fma": ("float p = W[(int64_t)j * dm + e] * load_as_f32(x, is_bf16, t * dm + e);\n"
+                    "                s = s + p;",
+                    "s = fmaf(W[(int64_t)j * dm + e], load_as_f32(x, is_bf16, t * dm + e), s);"),
+    "project_w_transposed": ("W[(int64_t)j * dm + e]", "W[(int64_t)e * 16 + j]"),
+    "project_reverse_order": ("for (int e = 0; e < dm; ++e) {\n                float p = W",
+                              "for (int e = dm - 1; e >= 0; --e) {\n                float p = W"),
 }
 
 

@@ -343,3 +343,62 @@ def test_attn_bf16_inputs_widen_exactly():
     b = _run(*f32, groups, K, 4, 0.25)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ----------------------------------------------------------------------------
+# routing projection r = W x (Technical Summary, Token Grouping; one d_model x
+# 16 matrix per layer, as the parameter counts of Tables 2 and 3 imply)
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values that bf16 represents exactly -> their bf16 bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0), "value not representable in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def test_project_integer_exact():
+    # small integers: every product and partial sum is exact in fp32, so the
+    # result must equal integer matrix arithmetic (a transposed or shifted W
+    # index cannot pass)
+    rng = np.random.default_rng(11)
+    n, dm = 37, 96
+    x = rng.integers(-8, 9, (n, dm)).astype(np.float32)
+    W = rng.integers(-5, 6, (16, dm)).astype(np.float32)
+    want = (x.astype(np.int64) @ W.T.astype(np.int64)).astype(np.float32)
+    assert np.array_equal(oracle.project(x, W), want)
+    assert np.array_equal(oracle.project(_bf16_bits(x), W), want)
+
+
+def test_project_order_and_no_fma():
+    # Hand-derived rounding cases that fix the arithmetic reading (fp32,
+    # index order from 0, separate multiply and add).
+    # (a) W0 = 1 + 2^-20, W1 = -W0, x = (1 + 2^-7, 1 + 2^-7): each product
+    #     rounds to 1 + 2^-7 + 2^-20 (the 2^-27 term is below half an ulp), so
+    #     the sum is exactly 0; a fused multiply-add would keep -2^-27.
+    W = np.zeros((16, 2), np.float32)
+    W[0] = [1 + 2.0**-20, -(1 + 2.0**-20)]
+    x = np.array([[1 + 2.0**-7, 1 + 2.0**-7]], np.float32)
+    r = oracle.project(_bf16_bits(x), W)
+    assert r[0, 0] == 0.0
+    # (b) x = (1, 2^-24 x 15), W = 1: in index order every 1 + 2^-24 rounds to
+    #     even, back to 1; summing the small terms first would give 1 + 2^-20.
+    x = np.array([[1.0] + [2.0**-24] * 15], np.float32)
+    W = np.ones((16, 16), np.float32)
+    r = oracle.project(_bf16_bits(x), W)
+    assert np.all(r[0] == 1.0)
+
+
+def test_route_project_identity_reduces_to_route():
+    # W = [I_16 | 0]: the projected vector is the first 16 hidden components,
+    # so the groups are the (pinned) routing of those components
+    rng = np.random.default_rng(12)
+    n, dm, H, K, topk = 300, 40, 3, 8, 2
+    x = rng.standard_normal((n, dm)).astype(np.float32)
+    W = np.zeros((16, dm), np.float32)
+    W[:, :16] = np.eye(16, dtype=np.float32)
+    c = rng.standard_normal((H, K, 16)).astype(np.float32)
+    r, g, m = oracle.route_project(x, W, c, topk)
+    assert np.array_equal(r, x[:, :16])
+    g_ref, m_ref = oracle.route(np.ascontiguousarray(np.broadcast_to(x[:, :16], (H, n, 16))),
+                                c, topk)
+    assert np.array_equal(g, g_ref) and np.array_equal(m, m_ref)
