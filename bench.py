@@ -256,6 +256,53 @@ def run_sweep(steps: int, warmup: int) -> int:
     return 0
 
 
+# fp32 vector rate of one MI355X without packed or fused forms: 256 CUs x
+# 4 SIMDs x 16 lanes, one operation per lane per clock at 2.4 GHz.
+PEAK_F32_VALU_TFLOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+PEAK_HBM_GBS = 8000.0
+
+
+def run_project(steps: int, warmup: int) -> int:
+    """The fused routing projection (focus_route_project) at each projection
+    workload: one JSON object with a row per workload, each with its vector
+    ALU roofline (a separate multiply and add per weight, 32 * d_model
+    operations per token, plus 31 per centroid score)."""
+    import torch
+
+    from centroid_gated_sparse_amd import focus as F
+    from centroid_gated_sparse_amd.workloads import (PROJECTION_WORKLOADS, projection_inputs,
+                                                     seed_for)
+
+    F.lib()
+    rows = []
+    for pw in PROJECTION_WORKLOADS.values():
+        x, W, c = projection_inputs(pw, seed_for(pw.name), "cuda")
+        Wt = torch.from_numpy(np.ascontiguousarray(W.T)).cuda()
+        ct = torch.from_numpy(c).cuda()
+        groups = torch.empty((pw.heads, pw.n, pw.topk), dtype=torch.int32, device="cuda")
+        gmask = torch.empty((pw.heads, pw.n), dtype=torch.int32, device="cuda")
+        ms = timed_ms(lambda: F.focus_route_project(x, Wt, ct, pw.topk, groups, gmask),
+                      warmup, steps)
+        ops = pw.n * (32.0 * pw.d_model + 31.0 * pw.heads * pw.K)
+        hbm = pw.n * (pw.d_model * x.element_size() + pw.heads * 4 * (pw.topk + 1))
+        achieved = ops / (ms / 1e3) / 1e12
+        rows.append({
+            "workload": pw.name, "n": pw.n, "d_model": pw.d_model, "heads": pw.heads,
+            "centroids": pw.K, "topk": pw.topk, "dtype": pw.dtype, "ms": ms,
+            "tokens_per_s": pw.n / (ms / 1e3),
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_F32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_F32_VALU_TFLOPS},
+            "hbm_gbs": hbm / (ms / 1e3) / 1e9,
+            "hbm_frac": hbm / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        })
+        log(f"project: {pw.name} {ms:.3f} ms, {achieved:.2f} TFLOP/s "
+            f"({achieved / PEAK_F32_VALU_TFLOPS:.1%} of the vector ALU rate)")
+        del x, Wt, ct, groups, gmask
+        torch.cuda.empty_cache()
+    print(json.dumps({"bench": "route_project", "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +315,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the Table 6 context sweep (Focus vs our dense kernel)")
+    ap.add_argument("--project", action="store_true",
+                    help="only time the fused routing projection (focus_route_project)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes three "
                          "times (scales the HBM byte counters)")
@@ -290,6 +339,8 @@ def main() -> int:
 
     if args.sweep:
         return run_sweep(args.steps, args.warmup)
+    if args.project:
+        return run_project(max(args.steps, 5), args.warmup)
 
     from centroid_gated_sparse_amd import focus as F
     from centroid_gated_sparse_amd.workloads import (WORKLOADS, qkv_inputs, routing_inputs,

@@ -125,6 +125,34 @@ focus_status focus_route(const float *r, const float *centroids, int32_t H, int6
     return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_route launch");
 }
 
+focus_status focus_route_project(const void *x, focus_dtype xdt, int64_t n, int32_t d_model,
+                                 const float *Wt, const float *centroids, int32_t H,
+                                 int32_t d_g, int32_t K, int32_t topk, int32_t *groups,
+                                 uint32_t *gmask, float *r, focus_stream stream)
+{
+    g_last_error[0] = 0;
+    FOCUS_PTR(x);
+    FOCUS_PTR(Wt);
+    FOCUS_PTR(centroids);
+    FOCUS_PTR(groups);
+    FOCUS_PTR(gmask);
+    if (r != nullptr && !aligned16(r))
+        return invalid("pointer r is not 16-byte aligned");
+    FOCUS_REQUIRE(xdt == FOCUS_F32 || xdt == FOCUS_BF16, "dtype %d", (int)xdt);
+    FOCUS_REQUIRE(H >= 1 && n >= 1 && K >= 1, "H=%d n=%lld K=%d", H, (long long)n, K);
+    FOCUS_REQUIRE(n <= INT32_MAX, "n=%lld", (long long)n);
+    FOCUS_REQUIRE(d_model >= 1, "d_model=%d", d_model);
+    if (d_g != kRouteDim)
+        return unsupported("routing dimension must be 16");
+    if (K > kMaxGroups)
+        return unsupported("at most 32 centroids");
+    FOCUS_REQUIRE(topk >= 1 && topk <= K, "topk=%d K=%d", topk, K);
+    hipError_t e = launch_route_project(x, xdt == FOCUS_BF16, n, d_model, Wt, centroids, H, K,
+                                        topk, groups, gmask, r,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_route_project launch");
+}
+
 size_t focus_bucket_workspace_bytes(int32_t H, int64_t n, int32_t K, int32_t topk)
 {
     if (H < 1 || n < 1 || K < 1 || K > kMaxGroups || topk < 1 || topk > K)

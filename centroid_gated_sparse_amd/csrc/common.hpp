@@ -34,6 +34,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---- route.hip
 hipError_t launch_route(const float *r, const float *centroids, int H, int64_t n, int K,
                         int topk, int32_t *groups, uint32_t *gmask, hipStream_t s);
+hipError_t launch_route_project(const void *x, bool bf16, int64_t n, int dm, const float *Wt,
+                                const float *centroids, int H, int K, int topk,
+                                int32_t *groups, uint32_t *gmask, float *r_out, hipStream_t s);
 
 // ---- bucket.hip
 size_t bucket_workspace_bytes(int H, int64_t n, int K, int topk);

@@ -108,6 +108,238 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ r,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused projection + routing: r_t = W x_t, then every routing head's top-k
+// from r_t (Technical Summary, Core Architecture / Token Grouping: each
+// hidden state is projected to the 16-dimensional centroid space; the
+// projection is one d_model x 16 matrix per layer, the parameter counts of
+// the thelatestinai.com Tables 2 and 3).
+//
+// The work is plain fp32 vector arithmetic: r_t[j] starts at +0 and adds
+// Wt[e][j] * x_t[e] for e = 0, 1, ... with a separate multiply and add (no
+// fused multiply-add), so it is reproducible bit for bit.  Each lane owns
+// TPL tokens and their 16 sums.  Wt (d_model rows of 16 weights) is the
+// same for every lane: one row is a single 64-byte scalar load whose values
+// enter the vector instructions as scalar operands, all rows of a chunk
+// addressed from one base by constant offsets.  Hidden states stream through
+// 16-byte loads, a chunk of 8 elements ahead of the arithmetic.  At 2 * 16
+// vector operations per element the kernel is bound by the fp32 vector
+// rate, not by HBM.
+
+constexpr int kProjBlock = 256;  // threads per block
+constexpr int kProjChunk = 8;    // hidden-state elements per load
+
+template <bool BF16>
+struct XChunk;
+
+// Eight bf16 hidden-state values (one 16-byte load), widened exactly.
+template <>
+struct XChunk<true> {
+    uint4 raw;
+    __device__ __forceinline__ void load(const char *row, int e0)
+    {
+        raw = *reinterpret_cast<const uint4 *>(row + (size_t)e0 * 2);
+    }
+    __device__ __forceinline__ float at(int u) const
+    {
+        const uint32_t w = u < 2 ? raw.x : u < 4 ? raw.y : u < 6 ? raw.z : raw.w;
+        return __uint_as_float((u & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+// Eight fp32 hidden-state values (two 16-byte loads).
+template <>
+struct XChunk<false> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const char *row, int e0)
+    {
+        const float4 *p = reinterpret_cast<const float4 *>(row + (size_t)e0 * 4);
+        a = p[0];
+        b = p[1];
+    }
+    __device__ __forceinline__ float at(int u) const
+    {
+        const float4 &h = u < 4 ? a : b;
+        const int k = u & 3;
+        return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+    }
+};
+
+__device__ __forceinline__ float load_one(const char *row, bool bf16, int e)
+{
+    if (bf16)
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(row)[e] << 16);
+    return reinterpret_cast<const float *>(row)[e];
+}
+
+// Score of a routing vector against one centroid: the same order as score16.
+__device__ __forceinline__ float score_r(const float (&r)[16], const float *__restrict__ c)
+{
+#pragma clang fp contract(off)
+    float s = r[0] * c[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) {
+        float p = r[e] * c[e];
+        s = s + p;
+    }
+    return s;
+}
+
+// Routing of one token for every head: selection of the k best groups,
+// scanning upward and taking a group only on a strictly larger score, so
+// equal scores go to the lower index.
+__device__ __forceinline__ void route_token(const float (&r)[16], int64_t t, int64_t n,
+                                            const float *__restrict__ centroids, int H, int K,
+                                            int topk, int32_t *__restrict__ groups,
+                                            uint32_t *__restrict__ gmask)
+{
+    for (int h = 0; h < H; ++h) {
+        const float *ch = centroids + (int64_t)h * K * kRouteDim;
+        float s[kMaxGroups];
+#pragma unroll
+        for (int g = 0; g < kMaxGroups; ++g)
+            s[g] = g < K ? score_r(r, ch + g * kRouteDim) : 0.f;
+        uint32_t taken = 0;
+        int32_t *gt = groups + ((int64_t)h * n + t) * topk;
+        for (int sel = 0; sel < topk; ++sel) {
+            int best = -1;
+            float bs = 0.f;
+#pragma unroll
+            for (int g = 0; g < kMaxGroups; ++g) {
+                if (g < K && !((taken >> g) & 1u) && (best < 0 || s[g] > bs)) {
+                    best = g;
+                    bs = s[g];
+                }
+            }
+            taken |= 1u << best;
+            gt[sel] = best;
+        }
+        gmask[(int64_t)h * n + t] = taken;
+    }
+}
+
+// Adds one chunk of 8 elements to the sums, element by element in order.
+template <bool BF16, int TPL>
+__device__ __forceinline__ void project_chunk(float (&acc)[TPL][16], const XChunk<BF16> (&xc)[TPL],
+                                              const float *__restrict__ wt)
+{
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int u = 0; u < kProjChunk; ++u) {
+        float xv[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            xv[i] = xc[i].at(u);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float w = wt[u * kRouteDim + j];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const float p = w * xv[i];
+                acc[i][j] = acc[i][j] + p;
+            }
+        }
+    }
+}
+
+// VEC: d_model is a multiple of 8, so rows are 16-byte aligned and the
+// hidden states move in 8-element chunks; otherwise one element at a time.
+// Lane l of wave v owns tokens (v * TPL + i) * 64 + l, i < TPL.
+template <bool BF16, bool VEC, int TPL>
+__global__ __launch_bounds__(kProjBlock) void route_project_kernel(
+    const void *__restrict__ x, int64_t n, int dm, const float *__restrict__ Wt,
+    const float *__restrict__ centroids, int H, int K, int topk,
+    int32_t *__restrict__ groups, uint32_t *__restrict__ gmask, float *__restrict__ r_out)
+{
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = ((int64_t)blockIdx.x * kProjBlock + threadIdx.x) / kWave;
+    constexpr size_t esize = BF16 ? 2 : 4;
+    int64_t tok[TPL];
+    const char *row[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+        tok[i] = (wave * TPL + i) * kWave + lane;
+        const int64_t tl = tok[i] < n ? tok[i] : n - 1;  // tail lanes repeat the last row
+        row[i] = static_cast<const char *>(x) + (size_t)tl * dm * esize;
+    }
+
+    float acc[TPL][16];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            acc[i][j] = 0.f;
+
+    if constexpr (VEC) {
+        // two chunk buffers: the loads of one chunk are in flight while the
+        // other is summed
+        XChunk<BF16> xa[TPL], xb[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            xa[i].load(row[i], 0);
+        const int chunks = dm / kProjChunk;
+        int c = 0;
+        for (; c + 2 <= chunks; c += 2) {
+#pragma unroll
+            for (int i = 0; i < TPL; ++i)
+                xb[i].load(row[i], (c + 1) * kProjChunk);
+            project_chunk<BF16, TPL>(acc, xa, Wt + (size_t)c * kProjChunk * kRouteDim);
+            const int cn = c + 2 < chunks ? c + 2 : c + 1;  // past the end: reload a valid chunk
+#pragma unroll
+            for (int i = 0; i < TPL; ++i)
+                xa[i].load(row[i], cn * kProjChunk);
+            project_chunk<BF16, TPL>(acc, xb, Wt + (size_t)(c + 1) * kProjChunk * kRouteDim);
+        }
+        if (c < chunks)  // odd chunk count: xa holds the last chunk
+            project_chunk<BF16, TPL>(acc, xa, Wt + (size_t)c * kProjChunk * kRouteDim);
+    } else {
+        for (int e = 0; e < dm; ++e) {
+            float xv[TPL];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i)
+                xv[i] = load_one(row[i], BF16, e);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float w = Wt[(size_t)e * kRouteDim + j];
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    const float p = w * xv[i];
+                    acc[i][j] = acc[i][j] + p;
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+        if (tok[i] >= n)
+            continue;
+        if (r_out != nullptr) {
+            float4 *ro = reinterpret_cast<float4 *>(r_out + tok[i] * kRouteDim);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                ro[q4] = make_float4(acc[i][4 * q4], acc[i][4 * q4 + 1], acc[i][4 * q4 + 2],
+                                     acc[i][4 * q4 + 3]);
+        }
+        route_token(acc[i], tok[i], n, centroids, H, K, topk, groups, gmask);
+    }
+}
+
+template <bool BF16, int TPL>
+hipError_t launch_project_tpl(const void *x, int64_t n, int dm, const float *Wt,
+                              const float *centroids, int H, int K, int topk, int32_t *groups,
+                              uint32_t *gmask, float *r_out, hipStream_t s)
+{
+    const int64_t tokens_per_block = (int64_t)kProjBlock * TPL;
+    const int64_t blocks = (n + tokens_per_block - 1) / tokens_per_block;
+    auto kern = dm % kProjChunk == 0 ? route_project_kernel<BF16, true, TPL>
+                                     : route_project_kernel<BF16, false, TPL>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kProjBlock), 0, s, x, n, dm, Wt,
+                       centroids, H, K, topk, groups, gmask, r_out);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_route(const float *r, const float *centroids, int H, int64_t n, int K,
@@ -124,6 +356,35 @@ hipError_t launch_route(const float *r, const float *centroids, int H, int64_t n
     hipLaunchKernelGGL(route_kernel, grid, dim3(256), 0, s, r, centroids, n, K, kp_log2,
                        topk, groups, gmask);
     return hipGetLastError();
+}
+
+hipError_t launch_route_project(const void *x, bool bf16, int64_t n, int dm, const float *Wt,
+                                const float *centroids, int H, int K, int topk,
+                                int32_t *groups, uint32_t *gmask, float *r_out, hipStream_t s)
+{
+    // Tokens per lane: more tokens share each scalar weight load, fewer
+    // tokens per lane keep every SIMD busy at short contexts (256 CUs x 4
+    // SIMDs x 4 waves = 4096 waves fill the chip).
+    const int64_t waves_at_4 = (n + 4 * kWave - 1) / (4 * kWave);
+    const int64_t waves_at_2 = (n + 2 * kWave - 1) / (2 * kWave);
+    if (bf16) {
+        if (waves_at_4 >= 4096)
+            return launch_project_tpl<true, 4>(x, n, dm, Wt, centroids, H, K, topk, groups,
+                                               gmask, r_out, s);
+        if (waves_at_2 >= 4096)
+            return launch_project_tpl<true, 2>(x, n, dm, Wt, centroids, H, K, topk, groups,
+                                               gmask, r_out, s);
+        return launch_project_tpl<true, 1>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
+                                           r_out, s);
+    }
+    if (waves_at_4 >= 4096)
+        return launch_project_tpl<false, 4>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
+                                            r_out, s);
+    if (waves_at_2 >= 4096)
+        return launch_project_tpl<false, 2>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
+                                            r_out, s);
+    return launch_project_tpl<false, 1>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
+                                        r_out, s);
 }
 
 }  // namespace focus

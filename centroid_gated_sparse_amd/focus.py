@@ -3,8 +3,8 @@ torch tensors.  Argument marshalling only — every step of the path runs in
 the library's HIP kernels.  Raises if the library has not been built or a
 call returns an error status.
 
-The call names match the C ABI: focus_route, focus_bucket, focus_attn_fwd
-(+ focus_attn_fwd_part), focus_dense_causal_fwd.  ``focus_forward`` chains
+The call names match the C ABI: focus_route, focus_route_project,
+focus_bucket, focus_attn_fwd (+ focus_attn_fwd_part), focus_dense_causal_fwd.  ``focus_forward`` chains
 the three calls and allocates outputs and workspaces with torch.
 """
 from __future__ import annotations
@@ -24,7 +24,7 @@ PART_ALL = 7
 # exported symbols (all declared in include/focus.h)
 SYMBOLS = (
     "focus_status_string", "focus_last_error", "focus_abi_version",
-    "focus_route", "focus_bucket_workspace_bytes", "focus_bucket",
+    "focus_route", "focus_route_project", "focus_bucket_workspace_bytes", "focus_bucket",
     "focus_attn_workspace_bytes", "focus_attn_fwd", "focus_attn_fwd_part",
     "focus_dense_workspace_bytes", "focus_dense_causal_fwd",
 )
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
     L.focus_abi_version.argtypes = []
     L.focus_abi_version.restype = i32
     L.focus_route.argtypes = [P, P, i32, i64, i32, i32, i32, P, P, P]
+    L.focus_route_project.argtypes = [P, ctypes.c_int, i64, i32, P, P, i32, i32, i32, i32,
+                                      P, P, P, P]
     L.focus_bucket_workspace_bytes.argtypes = [i32, i64, i32, i32]
     L.focus_bucket_workspace_bytes.restype = sz
     L.focus_bucket.argtypes = [P, i32, i64, i32, i32, P, P, P, P, sz, P]
@@ -69,8 +71,8 @@ def lib() -> ctypes.CDLL:
     L.focus_dense_workspace_bytes.restype = sz
     L.focus_dense_causal_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i32, i64, i32, f32,
                                          P, P, P, sz, P]
-    for name in ("focus_route", "focus_bucket", "focus_attn_fwd", "focus_attn_fwd_part",
-                 "focus_dense_causal_fwd"):
+    for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_attn_fwd",
+                 "focus_attn_fwd_part", "focus_dense_causal_fwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -104,7 +106,7 @@ def _dtype_code(t) -> int:
         return FOCUS_BF16
     if t.dtype == torch.float32:
         return FOCUS_F32
-    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
 
 
 def _need(cond: bool, msg: str) -> None:
@@ -129,6 +131,29 @@ def focus_route(r, centroids, topk: int, groups=None, gmask=None, stream=None):
     _check("focus_route", lib().focus_route(_ptr(r), _ptr(centroids), H, n, dg, K, topk,
                                             _ptr(groups), _ptr(gmask), _stream(stream)))
     return groups, gmask
+
+
+def focus_route_project(x, Wt, centroids, topk: int, groups=None, gmask=None, r=None,
+                        want_r: bool = False, stream=None):
+    """x [n, d_model] (bf16 or fp32), Wt fp32 [d_model, 16] (row e: the 16 weights of
+    hidden feature e), centroids fp32 [H, K, 16]
+    -> (groups int32 [H, n, topk], gmask int32 [H, n], r fp32 [n, 16] or None).
+    r is written when given or when want_r is set."""
+    import torch
+
+    n, dm = x.shape
+    H, K, dg = centroids.shape
+    _need(tuple(Wt.shape) == (dm, dg), f"Wt must be [{dm}, {dg}], got {tuple(Wt.shape)}")
+    if groups is None:
+        groups = torch.empty((H, n, topk), dtype=torch.int32, device=x.device)
+    if gmask is None:
+        gmask = torch.empty((H, n), dtype=torch.int32, device=x.device)
+    if r is None and want_r:
+        r = torch.empty((n, dg), dtype=torch.float32, device=x.device)
+    _check("focus_route_project", lib().focus_route_project(
+        _ptr(x), _dtype_code(x), n, dm, _ptr(Wt), _ptr(centroids), H, dg, K, topk,
+        _ptr(groups), _ptr(gmask), _ptr(r), _stream(stream)))
+    return groups, gmask, r
 
 
 def focus_bucket_workspace_bytes(H: int, n: int, K: int, topk: int) -> int:

@@ -154,3 +154,53 @@ def to_bf16_bits(t) -> np.ndarray:
     import torch
 
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# Routing projection inputs (the step before routing: r_t = W x_t maps a
+# d_model hidden state to the 16-dimensional routing space, one W per layer
+# shared by its routing heads; 12 x 768 x 16 = 148K parameters for GPT-2 and
+# 32 x 4096 x 16 = 2.1M for Mistral-7B, Tables 2 and 3).
+@dataclass(frozen=True)
+class ProjectionWorkload:
+    name: str
+    n: int          # tokens
+    d_model: int    # hidden size
+    heads: int      # routing heads (each with its own centroids)
+    K: int
+    topk: int
+    dtype: str      # hidden-state dtype: "bf16" or "f32"
+
+
+PROJECTION_WORKLOADS = {
+    "gpt2_proj_n64k": ProjectionWorkload("gpt2_proj_n64k", 65536, 768, 12, 4, 2, "bf16"),
+    "gqa7b_proj_n1m_k8": ProjectionWorkload("gqa7b_proj_n1m_k8", 1048576, 4096, 8, 8, 2,
+                                            "bf16"),
+}
+
+
+def projection_inputs(pw: ProjectionWorkload, seed: int, device="cpu"):
+    """(x torch [n, d_model] in pw.dtype on `device`, W float32 [16, d_model],
+    centroids float32 [heads, K, 16]).
+
+    x: standard normal hidden states; W: normal(0, 1/d_model) so that each
+    routing coordinate has unit variance; centroids: standard normal rows
+    scaled to unit length, drawn per routing head."""
+    import torch
+
+    s_c, s_w, s_x, _, _ = _streams(seed)
+    c = np.random.default_rng(s_c).standard_normal((pw.heads, pw.K, D_ROUTE),
+                                                   dtype=np.float32)
+    c /= np.linalg.norm(c, axis=2, keepdims=True).astype(np.float32)
+    W = (np.random.default_rng(s_w).standard_normal((D_ROUTE, pw.d_model), dtype=np.float32)
+         * np.float32(1.0 / math.sqrt(pw.d_model))).astype(np.float32)
+    torch_seed = int(s_x.generate_state(1, np.uint64)[0] & 0x7FFFFFFFFFFFFFFF)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(torch_seed)
+    dt = torch.float32 if pw.dtype == "f32" else torch.bfloat16
+    x = torch.empty((pw.n, pw.d_model), dtype=dt, device=device)
+    rows = max(1, (1 << 26) // pw.d_model)   # float32 staging of at most 256 MiB
+    for a in range(0, pw.n, rows):
+        b = min(pw.n, a + rows)
+        x[a:b] = torch.randn((b - a, pw.d_model), generator=gen, device=device,
+                             dtype=torch.float32).to(dt)
+    return x, np.ascontiguousarray(W), np.ascontiguousarray(c)

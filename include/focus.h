@@ -91,6 +91,40 @@ focus_status focus_route(const float *r, const float *centroids, int32_t H, int6
                          uint32_t *gmask, focus_stream stream);
 
 /*
+ * focus_route_project — the routing projection fused with focus_route.
+ * Technical Summary, Core Architecture and Token Grouping (each hidden state
+ * is projected into the 16-dimensional centroid space before it is compared
+ * with the centroids); thelatestinai.com Tables 2 and 3 (one d_model x 16
+ * projection per layer: 12 x 768 x 16 = 148K parameters for GPT-2,
+ * 32 x 4096 x 16 = 2.1M for Mistral-7B), so every routing head of a layer
+ * routes the same r_t against its own centroids.
+ *
+ *   x          [n, d_model] in xdt (FOCUS_BF16 or FOCUS_F32): hidden states
+ *   Wt         fp32 [d_model, d_g]  the projection, one row of d_g weights
+ *                                   per hidden feature:
+ *                                   r_t[j] = sum_e Wt[e][j] * x_t[e]
+ *                                   (a torch Linear(d_model, 16) weight,
+ *                                   transposed)
+ *   centroids  fp32 [H, K, d_g]
+ *   groups     int32 [H, n, topk]   out, as focus_route
+ *   gmask      uint32 [H, n]        out, as focus_route
+ *   r          fp32 [n, d_g]        out, optional (NULL: not written)
+ * Each r_t[j] starts at +0 and adds the fp32 products Wt[e][j] * x_t[e] for
+ * e = 0, 1, ..., d_model - 1, each product rounded before its add (no fused
+ * multiply-add); bf16 inputs widen exactly.  The scores and the top-k then
+ * follow focus_route exactly, so focus_route on the returned r (broadcast to
+ * the H heads) gives the same groups.  Any d_model >= 1 works; multiples of
+ * 8 take the vectorised loads.
+ * Errors: INVALID_ARGUMENT for null or misaligned pointers, n < 1, H < 1,
+ * d_model < 1, K < 1, topk not in [1, K]; UNSUPPORTED for d_g != 16 or
+ * K > 32.
+ */
+focus_status focus_route_project(const void *x, focus_dtype xdt, int64_t n, int32_t d_model,
+                                 const float *Wt, const float *centroids, int32_t H,
+                                 int32_t d_g, int32_t K, int32_t topk, int32_t *groups,
+                                 uint32_t *gmask, float *r, focus_stream stream);
+
+/*
  * focus_bucket — per-head bucketing of the n*topk (token, group) entries for
  * within-group causal attention (Technical Summary, Key Contributions 5:
  * the sparse pattern splits into a local-window call and a within-group

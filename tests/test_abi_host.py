@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(F.SYMBOLS)
@@ -77,6 +77,32 @@ def test_route_rejects_bad_arguments(L):
     assert call(*ok[:5], 4, 5, *ok[7:]) == 1       # topk > K
     assert call(*ok[:3], 0, *ok[4:]) == 1          # n < 1
     assert call(*ok[:5], 4, 0, *ok[7:]) == 1       # topk < 1
+    assert b"topk" in L.focus_last_error()
+
+
+@no_gpu
+def test_route_project_rejects_bad_arguments(L):
+    f = L.focus_route_project
+    # x, xdt, n, d_model, Wt, centroids, H, d_g, K, topk, groups, gmask, r, stream
+    ok = [FAKE, F.FOCUS_BF16, 100, 768, FAKE, FAKE, 4, 16, 8, 2, FAKE, FAKE, None, None]
+
+    def call(**over):
+        a = list(ok)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == 1                      # x null
+    assert call(a4=FAKE + 4) == 1                  # Wt misaligned
+    assert call(a12=FAKE + 8) == 1                 # r given but misaligned
+    assert call(a1=3) == 1                         # dtype
+    assert call(a2=0) == 1                         # n < 1
+    assert call(a3=0) == 1                         # d_model < 1
+    assert call(a6=0) == 1                         # H < 1
+    assert call(a7=8) == 2                         # d_g != 16
+    assert call(a8=33) == 2                        # K > 32
+    assert call(a9=9) == 1                         # topk > K
+    assert call(a9=0) == 1
     assert b"topk" in L.focus_last_error()
 
 
