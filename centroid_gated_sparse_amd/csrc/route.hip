@@ -117,17 +117,20 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ r,
 //
 // The work is plain fp32 vector arithmetic: r_t[j] starts at +0 and adds
 // Wt[e][j] * x_t[e] for e = 0, 1, ... with a separate multiply and add (no
-// fused multiply-add), so it is reproducible bit for bit.  Each lane owns
-// TPL tokens and their 16 sums.  Wt (d_model rows of 16 weights) is the
-// same for every lane: one row is a single 64-byte scalar load whose values
-// enter the vector instructions as scalar operands, all rows of a chunk
-// addressed from one base by constant offsets.  Hidden states stream through
-// 16-byte loads, a chunk of 8 elements ahead of the arithmetic.  At 2 * 16
-// vector operations per element the kernel is bound by the fp32 vector
-// rate, not by HBM.
+// fused multiply-add), so it is reproducible bit for bit.  One lane owns one
+// token and its 16 sums (more tokens per lane measured slower: fewer waves
+// hide less latency).  Wt (d_model rows of 16 weights) is the same for every
+// lane: a row is one 64-byte scalar load whose values enter the vector
+// instructions as scalar operands.  The rows come through a ring of
+// kProjAhead + 1 SGPR rows, fetched kProjAhead rows ahead of their use, with
+// scheduling fences so the compiler keeps the loads early.  Hidden states
+// stream through 16-byte loads, one 8-element chunk ahead.  At 2 * 16
+// vector operations per element the kernel is bound by the fp32 vector rate,
+// not by HBM.
 
 constexpr int kProjBlock = 256;  // threads per block
 constexpr int kProjChunk = 8;    // hidden-state elements per load
+constexpr int kProjAhead = 3;    // weight rows in flight ahead of the arithmetic
 
 template <bool BF16>
 struct XChunk;
@@ -219,125 +222,107 @@ __device__ __forceinline__ void route_token(const float (&r)[16], int64_t t, int
 }
 
 // Adds one chunk of 8 elements to the sums, element by element in order.
-template <bool BF16, int TPL>
-__device__ __forceinline__ void project_chunk(float (&acc)[TPL][16], const XChunk<BF16> (&xc)[TPL],
-                                              const float *__restrict__ wt)
+// On entry ring[16 * a + j] holds weight row e0 + a (a < kProjAhead); `next`
+// points at the chunk after this one (rows e0 + 8, ...), or at any valid
+// chunk when this is the last.
+template <bool BF16>
+__device__ __forceinline__ void project_chunk(float (&acc)[16], const XChunk<BF16> &xc,
+                                              float (&ring)[16 * kProjAhead],
+                                              const float *__restrict__ wt,
+                                              const float *__restrict__ next)
 {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int u = 0; u < kProjChunk; ++u) {
-        float xv[TPL];
+        const float xv = xc.at(u);
+        const float *src = u + kProjAhead < kProjChunk
+                               ? wt + (u + kProjAhead) * kRouteDim
+                               : next + (u + kProjAhead - kProjChunk) * kRouteDim;
+        float fetched[16];
 #pragma unroll
-        for (int i = 0; i < TPL; ++i)
-            xv[i] = xc[i].at(u);
+        for (int j = 0; j < 16; ++j)
+            fetched[j] = src[j];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float w = wt[u * kRouteDim + j];
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const float p = w * xv[i];
-                acc[i][j] = acc[i][j] + p;
-            }
+            const float p = ring[j] * xv;
+            acc[j] = acc[j] + p;
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a + 1 < kProjAhead; ++a)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                ring[16 * a + j] = ring[16 * (a + 1) + j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            ring[16 * (kProjAhead - 1) + j] = fetched[j];
     }
 }
 
 // VEC: d_model is a multiple of 8, so rows are 16-byte aligned and the
 // hidden states move in 8-element chunks; otherwise one element at a time.
-// Lane l of wave v owns tokens (v * TPL + i) * 64 + l, i < TPL.
-template <bool BF16, bool VEC, int TPL>
+// Thread g of the grid owns token g.
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kProjBlock) void route_project_kernel(
     const void *__restrict__ x, int64_t n, int dm, const float *__restrict__ Wt,
     const float *__restrict__ centroids, int H, int K, int topk,
     int32_t *__restrict__ groups, uint32_t *__restrict__ gmask, float *__restrict__ r_out)
 {
 #pragma clang fp contract(off)
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = ((int64_t)blockIdx.x * kProjBlock + threadIdx.x) / kWave;
     constexpr size_t esize = BF16 ? 2 : 4;
-    int64_t tok[TPL];
-    const char *row[TPL];
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-        tok[i] = (wave * TPL + i) * kWave + lane;
-        const int64_t tl = tok[i] < n ? tok[i] : n - 1;  // tail lanes repeat the last row
-        row[i] = static_cast<const char *>(x) + (size_t)tl * dm * esize;
-    }
+    const int64_t t = (int64_t)blockIdx.x * kProjBlock + threadIdx.x;
+    const int64_t tl = t < n ? t : n - 1;  // tail lanes repeat the last row
+    const char *row = static_cast<const char *>(x) + (size_t)tl * dm * esize;
 
-    float acc[TPL][16];
+    float acc[16];
 #pragma unroll
-    for (int i = 0; i < TPL; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            acc[i][j] = 0.f;
+    for (int j = 0; j < 16; ++j)
+        acc[j] = 0.f;
 
     if constexpr (VEC) {
+        const int chunks = dm / kProjChunk;
+        const float *last = Wt + (size_t)(chunks - 1) * kProjChunk * kRouteDim;
+        auto chunk_w = [&](int c) {
+            return c < chunks ? Wt + (size_t)c * kProjChunk * kRouteDim : last;
+        };
+        float ring[16 * kProjAhead];
+#pragma unroll
+        for (int a = 0; a < 16 * kProjAhead; ++a)
+            ring[a] = Wt[a];  // rows 0 .. kProjAhead-1 (d_model >= 8)
         // two chunk buffers: the loads of one chunk are in flight while the
         // other is summed
-        XChunk<BF16> xa[TPL], xb[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i)
-            xa[i].load(row[i], 0);
-        const int chunks = dm / kProjChunk;
+        XChunk<BF16> xa, xb;
+        xa.load(row, 0);
         int c = 0;
         for (; c + 2 <= chunks; c += 2) {
-#pragma unroll
-            for (int i = 0; i < TPL; ++i)
-                xb[i].load(row[i], (c + 1) * kProjChunk);
-            project_chunk<BF16, TPL>(acc, xa, Wt + (size_t)c * kProjChunk * kRouteDim);
-            const int cn = c + 2 < chunks ? c + 2 : c + 1;  // past the end: reload a valid chunk
-#pragma unroll
-            for (int i = 0; i < TPL; ++i)
-                xa[i].load(row[i], cn * kProjChunk);
-            project_chunk<BF16, TPL>(acc, xb, Wt + (size_t)(c + 1) * kProjChunk * kRouteDim);
+            xb.load(row, (c + 1) * kProjChunk);
+            project_chunk<BF16>(acc, xa, ring, chunk_w(c), chunk_w(c + 1));
+            xa.load(row, (c + 2 < chunks ? c + 2 : c + 1) * kProjChunk);
+            project_chunk<BF16>(acc, xb, ring, chunk_w(c + 1), chunk_w(c + 2));
         }
         if (c < chunks)  // odd chunk count: xa holds the last chunk
-            project_chunk<BF16, TPL>(acc, xa, Wt + (size_t)c * kProjChunk * kRouteDim);
+            project_chunk<BF16>(acc, xa, ring, chunk_w(c), chunk_w(c + 1));
     } else {
         for (int e = 0; e < dm; ++e) {
-            float xv[TPL];
-#pragma unroll
-            for (int i = 0; i < TPL; ++i)
-                xv[i] = load_one(row[i], BF16, e);
+            const float xv = load_one(row, BF16, e);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float w = Wt[(size_t)e * kRouteDim + j];
-#pragma unroll
-                for (int i = 0; i < TPL; ++i) {
-                    const float p = w * xv[i];
-                    acc[i][j] = acc[i][j] + p;
-                }
+                const float p = Wt[(size_t)e * kRouteDim + j] * xv;
+                acc[j] = acc[j] + p;
             }
         }
     }
 
+    if (t >= n)
+        return;
+    if (r_out != nullptr) {
+        float4 *ro = reinterpret_cast<float4 *>(r_out + t * kRouteDim);
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-        if (tok[i] >= n)
-            continue;
-        if (r_out != nullptr) {
-            float4 *ro = reinterpret_cast<float4 *>(r_out + tok[i] * kRouteDim);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                ro[q4] = make_float4(acc[i][4 * q4], acc[i][4 * q4 + 1], acc[i][4 * q4 + 2],
-                                     acc[i][4 * q4 + 3]);
-        }
-        route_token(acc[i], tok[i], n, centroids, H, K, topk, groups, gmask);
+        for (int q4 = 0; q4 < 4; ++q4)
+            ro[q4] = make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
     }
-}
-
-template <bool BF16, int TPL>
-hipError_t launch_project_tpl(const void *x, int64_t n, int dm, const float *Wt,
-                              const float *centroids, int H, int K, int topk, int32_t *groups,
-                              uint32_t *gmask, float *r_out, hipStream_t s)
-{
-    const int64_t tokens_per_block = (int64_t)kProjBlock * TPL;
-    const int64_t blocks = (n + tokens_per_block - 1) / tokens_per_block;
-    auto kern = dm % kProjChunk == 0 ? route_project_kernel<BF16, true, TPL>
-                                     : route_project_kernel<BF16, false, TPL>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kProjBlock), 0, s, x, n, dm, Wt,
-                       centroids, H, K, topk, groups, gmask, r_out);
-    return hipGetLastError();
+    route_token(acc, t, n, centroids, H, K, topk, groups, gmask);
 }
 
 }  // namespace
@@ -362,29 +347,14 @@ hipError_t launch_route_project(const void *x, bool bf16, int64_t n, int dm, con
                                 const float *centroids, int H, int K, int topk,
                                 int32_t *groups, uint32_t *gmask, float *r_out, hipStream_t s)
 {
-    // Tokens per lane: more tokens share each scalar weight load, fewer
-    // tokens per lane keep every SIMD busy at short contexts (256 CUs x 4
-    // SIMDs x 4 waves = 4096 waves fill the chip).
-    const int64_t waves_at_4 = (n + 4 * kWave - 1) / (4 * kWave);
-    const int64_t waves_at_2 = (n + 2 * kWave - 1) / (2 * kWave);
-    if (bf16) {
-        if (waves_at_4 >= 4096)
-            return launch_project_tpl<true, 4>(x, n, dm, Wt, centroids, H, K, topk, groups,
-                                               gmask, r_out, s);
-        if (waves_at_2 >= 4096)
-            return launch_project_tpl<true, 2>(x, n, dm, Wt, centroids, H, K, topk, groups,
-                                               gmask, r_out, s);
-        return launch_project_tpl<true, 1>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
-                                           r_out, s);
-    }
-    if (waves_at_4 >= 4096)
-        return launch_project_tpl<false, 4>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
-                                            r_out, s);
-    if (waves_at_2 >= 4096)
-        return launch_project_tpl<false, 2>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
-                                            r_out, s);
-    return launch_project_tpl<false, 1>(x, n, dm, Wt, centroids, H, K, topk, groups, gmask,
-                                        r_out, s);
+    const int64_t blocks = (n + kProjBlock - 1) / kProjBlock;
+    const bool vec = dm % kProjChunk == 0;
+    auto kern = bf16 ? (vec ? route_project_kernel<true, true> : route_project_kernel<true, false>)
+                     : (vec ? route_project_kernel<false, true>
+                            : route_project_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kProjBlock), 0, s, x, n, dm, Wt,
+                       centroids, H, K, topk, groups, gmask, r_out);
+    return hipGetLastError();
 }
 
 }  // namespace focus

@@ -103,7 +103,7 @@ def routing_inputs(wl: Workload, seed: int):
     s_c, s_z, s_noise, _, _ = _streams(seed)
     c = np.random.default_rng(s_c).standard_normal((wl.K, D_ROUTE), dtype=np.float32)
     c /= np.linalg.norm(c, axis=1, keepdims=True).astype(np.float32)
-    centroids = np.ascontiguousarray(np.broadcast_to(c, (wl.hkv, wl.K, D_ROUTE)))
+    centroids = np.broadcast_to(c, (wl.hkv, wl.K, D_ROUTE)).copy()  # writable, contiguous
     p = None if wl.z_probs is None else np.asarray(wl.z_probs, np.float64)
     z = np.random.default_rng(s_z).choice(wl.K, size=(wl.hkv, wl.n), p=p)
     noise = np.random.default_rng(s_noise).standard_normal(

@@ -21,11 +21,17 @@
  *           and the output is the exact softmax over A(i).
  *   bucket: the (token, group) entries sorted by group, then by the token's
  *           lowest other group ("partner"), then by position.
+ *   project: r_t = W x_t, the hidden state projected into the routing space
+ *           by one 16 x d_model matrix per layer (Technical Summary, Core
+ *           Architecture and Token Grouping; the thelatestinai.com Tables 2
+ *           and 3 give its parameter count).
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of the repository):
  *   - score arithmetic: fp32, products and sums in index order 0..d_g-1,
  *     no fused multiply-add (build with -ffp-contract=off);
+ *   - projection arithmetic: the same rule, each sum starting at +0 and
+ *     adding the rounded products in feature order 0..d_model-1;
  *   - ties in the top-k: the lower group index wins; -0.0 equals +0.0;
  *   - window: i - j < w (w keys including the query itself);
  *   - softmax scale is an argument (1/sqrt(d) in every workload);
