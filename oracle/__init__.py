@@ -62,8 +62,13 @@ def _load():
                                      i64, f64, P, P, i64, P, P, P, i32]
     lib.oracle_pair_counts.argtypes = [P, i32, i64, i32, i32, i64, P]
     lib.oracle_project.argtypes = [P, i32, i64, i32, P, P]
+    lib.oracle_attn_bwd_rows.argtypes = [P, P, P, P, i32, i32, i32, i64, i32, P, i32, i32,
+                                         i64, f64, P, P, i64, P, i32]
+    lib.oracle_attn_bwd.argtypes = [P, P, P, P, i32, i32, i32, i64, i32, P, i32, i32, i64,
+                                    f64, P, P, P, i32]
     for f in (lib.oracle_route, lib.oracle_bucket, lib.oracle_attn_rows,
-              lib.oracle_pair_counts, lib.oracle_project):
+              lib.oracle_pair_counts, lib.oracle_project, lib.oracle_attn_bwd_rows,
+              lib.oracle_attn_bwd):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -211,3 +216,50 @@ def pair_counts(groups: np.ndarray, K: int, window: int) -> np.ndarray:
     _check(_load().oracle_pair_counts(_ptr(groups), H, n, K, topk, int(window),
                                       _ptr(out)), "pair_counts")
     return out
+
+
+def attn_bwd(q, k, v, dout, groups: np.ndarray, K: int, window: int, scale: float,
+             nthreads: int = 0):
+    """Gradients of the exact softmax over A(i) with respect to q, k and v,
+    given the output gradient dout [Hq, n, d] (same dtype convention as q).
+    Returns (dq [Hq, n, d], dk [Hkv, n, d], dv [Hkv, n, d]), float64."""
+    qa, qb = _as_raw(q)
+    ka, kb = _as_raw(k)
+    va, vb = _as_raw(v)
+    da, db = _as_raw(dout)
+    assert qb == kb == vb == db
+    Hq, n, d = qa.shape
+    Hkv = ka.shape[0]
+    assert ka.shape == va.shape == (Hkv, n, d) and da.shape == qa.shape
+    groups = np.ascontiguousarray(groups, dtype=np.int32)
+    assert groups.shape[:2] == (Hkv, n)
+    topk = groups.shape[2]
+    dq = np.empty((Hq, n, d), np.float64)
+    dk = np.empty((Hkv, n, d), np.float64)
+    dv = np.empty((Hkv, n, d), np.float64)
+    _check(_load().oracle_attn_bwd(_ptr(qa), _ptr(ka), _ptr(va), _ptr(da), qb, Hq, Hkv, n,
+                                   d, _ptr(groups), K, topk, int(window), float(scale),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads)), "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_rows(q, k, v, dout, groups: np.ndarray, K: int, window: int, scale: float,
+                  row_head: np.ndarray, row_pos: np.ndarray, nthreads: int = 0):
+    """dq of the listed (query head, position) rows: float64 [rows, d]."""
+    qa, qb = _as_raw(q)
+    ka, kb = _as_raw(k)
+    va, vb = _as_raw(v)
+    da, db = _as_raw(dout)
+    assert qb == kb == vb == db
+    Hq, n, d = qa.shape
+    Hkv = ka.shape[0]
+    groups = np.ascontiguousarray(groups, dtype=np.int32)
+    topk = groups.shape[2]
+    rh = np.ascontiguousarray(row_head, dtype=np.int32)
+    rp = np.ascontiguousarray(row_pos, dtype=np.int64)
+    dq = np.empty((rh.shape[0], d), np.float64)
+    _check(_load().oracle_attn_bwd_rows(_ptr(qa), _ptr(ka), _ptr(va), _ptr(da), qb, Hq, Hkv,
+                                        n, d, _ptr(groups), K, topk, int(window),
+                                        float(scale), _ptr(rh), _ptr(rp), rh.shape[0],
+                                        _ptr(dq), int(nthreads)), "attn_bwd_rows")
+    return dq

@@ -391,3 +391,248 @@ int oracle_pair_counts(const int32_t *groups, int32_t H, int64_t n, int32_t K,
     free(cnt);
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the exact softmax over A(i): the gradients of the forward
+ * above with respect to q, k and v, for the hard set (no gradient reaches the
+ * routing).  Needed to fine-tune or train through Focus attention
+ * (thelatestinai.com Table 5, all parameters fine-tuned; Technical Summary,
+ * results: from-scratch training at 124M and 7B).  With
+ *     s_ij = scale * q_i.k_j,   P_ij = exp(s_ij - L_i) on A(i),
+ *     O_i = sum_j P_ij v_j,     D_i = dO_i . O_i,
+ *     dP_ij = dO_i . v_j,       dS_ij = P_ij (dP_ij - D_i),
+ * the chain rule gives
+ *     dq_i = scale sum_{j in A(i)} dS_ij k_j
+ *     dk_j = scale sum_{(h,i): j in A(i)} dS_ij q_i
+ *     dv_j = sum_{(h,i): j in A(i)} P_ij dO_i
+ * where the sums for dk and dv run over every query head h that reads the
+ * key/value head of j.  All arithmetic is in double from the widened inputs;
+ * O and L are the oracle's own (not a GPU result).
+ * ------------------------------------------------------------------------ */
+
+/* Softmax statistics of one row: L_i, and D_i = dO_i . O_i.  sc must hold n
+ * doubles; qi is the widened query.  Returns |A(i)|. */
+static int64_t row_stats(const double *qi, const void *k, const void *v, const void *dout,
+                         int is_bf16, const uint32_t *bk, int64_t n, int d, int64_t w,
+                         double scale, int64_t hk, int64_t dob, int64_t i, double *sc,
+                         double *acc, double *L, double *D)
+{
+    double mx = -INFINITY;
+    int64_t cnt = 0;
+    for (int64_t j = 0; j <= i; ++j) {
+        if (!((i - j) < w || (bk[i] & bk[j]) != 0)) {
+            sc[j] = NAN;
+            continue;
+        }
+        double s = 0.0;
+        const int64_t kb = (hk * n + j) * d;
+        for (int e = 0; e < d; ++e)
+            s += qi[e] * widen(k, is_bf16, kb + e);
+        sc[j] = s * scale;
+        if (sc[j] > mx)
+            mx = sc[j];
+        ++cnt;
+    }
+    double l = 0.0;
+    for (int e = 0; e < d; ++e)
+        acc[e] = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+        if (isnan(sc[j]))
+            continue;
+        double p = exp(sc[j] - mx);
+        l += p;
+        const int64_t vb = (hk * n + j) * d;
+        for (int e = 0; e < d; ++e)
+            acc[e] += p * widen(v, is_bf16, vb + e);
+    }
+    double dd = 0.0;
+    for (int e = 0; e < d; ++e)
+        dd += widen(dout, is_bf16, dob + e) * (acc[e] / l);
+    *L = mx + log(l);
+    *D = dd;
+    return cnt;
+}
+
+/* dq of the listed (query head, position) rows: each row needs only its own
+ * attended set.  dq is [nrows][d] (double). */
+int oracle_attn_bwd_rows(const void *q, const void *k, const void *v, const void *dout,
+                         int32_t is_bf16, int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
+                         const int32_t *groups, int32_t K, int32_t topk, int64_t w,
+                         double scale, const int32_t *row_head, const int64_t *row_pos,
+                         int64_t nrows, double *dq, int32_t nthreads)
+{
+    if (!q || !k || !v || !dout || !groups || !row_head || !row_pos || !dq || Hq < 1 ||
+        Hkv < 1 || Hq % Hkv || n < 1 || d < 1 || K < 1 || K > 32 || topk < 1 ||
+        topk > K || w < 0 || nrows < 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (row_head[r] < 0 || row_head[r] >= Hq || row_pos[r] < 0 || row_pos[r] >= n)
+            return ORACLE_BAD_ARG;
+    uint32_t *bits = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(Hkv * n));
+    if (!bits)
+        return ORACLE_NO_MEMORY;
+    for (int64_t ht = 0; ht < (int64_t)Hkv * n; ++ht)
+        bits[ht] = group_bits(groups + ht * topk, topk);
+    const int ratio = Hq / Hkv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)n);
+        double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!sc || !qi || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (failed)
+                continue;
+            const int h = row_head[r];
+            const int64_t i = row_pos[r];
+            const int64_t hk = h / ratio;
+            const uint32_t *bk = bits + hk * n;
+            const int64_t rowb = ((int64_t)h * n + i) * d;
+            for (int e = 0; e < d; ++e)
+                qi[e] = widen(q, is_bf16, rowb + e);
+            double L, D;
+            row_stats(qi, k, v, dout, is_bf16, bk, n, d, w, scale, hk, rowb, i, sc, acc, &L,
+                      &D);
+            for (int e = 0; e < d; ++e)
+                acc[e] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                if (isnan(sc[j]))
+                    continue;
+                const double p = exp(sc[j] - L);
+                double dp = 0.0;
+                const int64_t vb = (hk * n + j) * d;
+                for (int e = 0; e < d; ++e)
+                    dp += widen(dout, is_bf16, rowb + e) * widen(v, is_bf16, vb + e);
+                const double ds = p * (dp - D);
+                const int64_t kb = (hk * n + j) * d;
+                for (int e = 0; e < d; ++e)
+                    acc[e] += ds * widen(k, is_bf16, kb + e);
+            }
+            for (int e = 0; e < d; ++e)
+                dq[r * d + e] = scale * acc[e];
+        }
+        free(sc);
+        free(qi);
+        free(acc);
+    }
+    free(bits);
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Full gradients.  dq [Hq, n, d], dk and dv [Hkv, n, d], all double.  The
+ * first sweep takes every query row (its L_i, D_i and dq_i); the second takes
+ * every key row j of every key/value head and sums over the queries that
+ * attend to it, so no two threads write the same output. */
+int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
+                    int32_t is_bf16, int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
+                    const int32_t *groups, int32_t K, int32_t topk, int64_t w,
+                    double scale, double *dq, double *dk, double *dv, int32_t nthreads)
+{
+    if (!q || !k || !v || !dout || !groups || !dq || !dk || !dv || Hq < 1 || Hkv < 1 ||
+        Hq % Hkv || n < 1 || d < 1 || K < 1 || K > 32 || topk < 1 || topk > K || w < 0)
+        return ORACLE_BAD_ARG;
+    const int64_t rows = (int64_t)Hq * n;
+    int32_t *rh = (int32_t *)malloc(sizeof(int32_t) * (size_t)rows);
+    int64_t *rp = (int64_t *)malloc(sizeof(int64_t) * (size_t)rows);
+    double *Ls = (double *)malloc(sizeof(double) * (size_t)rows);
+    double *Ds = (double *)malloc(sizeof(double) * (size_t)rows);
+    uint32_t *bits = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(Hkv * n));
+    if (!rh || !rp || !Ls || !Ds || !bits) {
+        free(rh);
+        free(rp);
+        free(Ls);
+        free(Ds);
+        free(bits);
+        return ORACLE_NO_MEMORY;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        rh[r] = (int32_t)(r / n);
+        rp[r] = r % n;
+    }
+    int rc = oracle_attn_bwd_rows(q, k, v, dout, is_bf16, Hq, Hkv, n, d, groups, K, topk, w,
+                                  scale, rh, rp, rows, dq, nthreads);
+    if (rc != ORACLE_OK)
+        goto done;
+    for (int64_t ht = 0; ht < (int64_t)Hkv * n; ++ht)
+        bits[ht] = group_bits(groups + ht * topk, topk);
+    const int ratio = Hq / Hkv;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)n);
+        double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!sc || !qi || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        /* softmax statistics of every row */
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; ++r) {
+            if (failed)
+                continue;
+            const int h = (int)(r / n);
+            const int64_t i = r % n;
+            const int64_t hk = h / ratio;
+            const int64_t rowb = r * d;
+            for (int e = 0; e < d; ++e)
+                qi[e] = widen(q, is_bf16, rowb + e);
+            row_stats(qi, k, v, dout, is_bf16, bits + hk * n, n, d, w, scale, hk, rowb, i,
+                      sc, acc, &Ls[r], &Ds[r]);
+        }
+        /* key rows: sum over the queries that attend to each key */
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t kr = 0; kr < (int64_t)Hkv * n; ++kr) {
+            if (failed)
+                continue;
+            const int64_t hk = kr / n;
+            const int64_t j = kr % n;
+            const uint32_t *bk = bits + hk * n;
+            double *dkj = dk + kr * d;
+            double *dvj = dv + kr * d;
+            for (int e = 0; e < d; ++e)
+                dkj[e] = dvj[e] = 0.0;
+            for (int h = (int)hk * ratio; h < (int)(hk + 1) * ratio; ++h) {
+                for (int64_t i = j; i < n; ++i) {
+                    if (!((i - j) < w || (bk[i] & bk[j]) != 0))
+                        continue;
+                    const int64_t rowb = ((int64_t)h * n + i) * d;
+                    double s = 0.0, dp = 0.0;
+                    for (int e = 0; e < d; ++e) {
+                        s += widen(q, is_bf16, rowb + e) * widen(k, is_bf16, kr * d + e);
+                        dp += widen(dout, is_bf16, rowb + e) * widen(v, is_bf16, kr * d + e);
+                    }
+                    const double p = exp(s * scale - Ls[(int64_t)h * n + i]);
+                    const double ds = p * (dp - Ds[(int64_t)h * n + i]);
+                    for (int e = 0; e < d; ++e) {
+                        dkj[e] += scale * ds * widen(q, is_bf16, rowb + e);
+                        dvj[e] += p * widen(dout, is_bf16, rowb + e);
+                    }
+                }
+            }
+        }
+        free(sc);
+        free(qi);
+        free(acc);
+    }
+    if (failed)
+        rc = ORACLE_NO_MEMORY;
+done:
+    free(rh);
+    free(rp);
+    free(Ls);
+    free(Ds);
+    free(bits);
+    return rc;
+}

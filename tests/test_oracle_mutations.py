@@ -35,6 +35,16 @@ MUTATIONS = {
     "project_w_transposed": ("W[(int64_t)j * dm + e]", "W[(int64_t)e * 16 + j]"),
     "project_reverse_order": ("for (int e = 0; e < dm; ++e) {\n                float p = W",
                               "for (int e = dm - 1; e >= 0; --e) {\n                float p = W"),
+    "bwd_dq_drop_d": ("const double ds = p * (dp - D);", "const double ds = p * dp;"),
+    "bwd_dk_drop_d": ("const double ds = p * (dp - Ds[(int64_t)h * n + i]);",
+                      "const double ds = p * dp;"),
+    "bwd_dk_no_scale": ("dkj[e] += scale * ds * widen(q", "dkj[e] += ds * widen(q"),
+    "bwd_dv_uses_ds": ("dvj[e] += p * widen(dout", "dvj[e] += ds * widen(dout"),
+    "bwd_gqa_first_head_only": ("h < (int)(hk + 1) * ratio; ++h)", "h < (int)hk * ratio + 1; ++h)"),
+    "bwd_window_le": ("if (!((i - j) < w || (bk[i] & bk[j]) != 0))",
+                      "if (!((i - j) <= w || (bk[i] & bk[j]) != 0))"),
+    "bwd_d_unnormalised": ("dd += widen(dout, is_bf16, dob + e) * (acc[e] / l);",
+                           "dd += widen(dout, is_bf16, dob + e) * acc[e];"),
 }
 
 

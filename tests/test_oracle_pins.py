@@ -402,3 +402,138 @@ def test_route_project_identity_reduces_to_route():
     g_ref, m_ref = oracle.route(np.ascontiguousarray(np.broadcast_to(x[:, :16], (H, n, 16))),
                                 c, topk)
     assert np.array_equal(g, g_ref) and np.array_equal(m, m_ref)
+
+
+# ----------------------------------------------------------------------------
+# backward: gradients of the exact softmax over A(i) with respect to q, k, v
+
+def _library_grads(q, k, v, dout, scale, mask):
+    """torch autograd (float64, CPU) through a plain masked softmax attention
+    with Hq/Hkv head sharing: the gradients of sum(dout * O)."""
+    hq = q.shape[0]
+    qt = torch.from_numpy(q).double().requires_grad_(True)
+    kt = torch.from_numpy(k).double().requires_grad_(True)
+    vt = torch.from_numpy(v).double().requires_grad_(True)
+    ke = kt.repeat_interleave(hq // k.shape[0], dim=0)
+    ve = vt.repeat_interleave(hq // v.shape[0], dim=0)
+    s = torch.matmul(qt, ke.transpose(-1, -2)) * scale
+    s = s.masked_fill(~torch.from_numpy(np.ascontiguousarray(mask)), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), ve)
+    (o * torch.from_numpy(dout).double()).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def _set_mask(groups, w):
+    """Boolean [Hkv, n, n] mask of A(i), from its definition."""
+    hkv, n, topk = groups.shape
+    gm = np.zeros((hkv, n), np.int64)
+    for s in range(topk):
+        gm |= 1 << groups[..., s].astype(np.int64)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return (j <= i)[None] & (((i - j) < w)[None] | ((gm[:, :, None] & gm[:, None, :]) != 0))
+
+
+def _assert_grads(got, want, tol=1e-10):
+    for g, r, name in zip(got, want, ("dq", "dk", "dv")):
+        np.testing.assert_allclose(g, r, atol=tol, rtol=0, err_msg=name)
+
+
+def test_attn_bwd_finite_differences():
+    """The gradients equal central differences of the pinned forward:
+    d/dx sum(dout * O) for sampled elements of q, k and v."""
+    rng = np.random.default_rng(21)
+    hq, hkv, n, d, K, w, scale = 2, 1, 48, 8, 3, 4, 0.5
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    dout = rng.standard_normal((hq, n, d)).astype(np.float32)
+    groups = _random_groups(rng, hkv, n, K, 2)
+    grads = oracle.attn_bwd(q, k, v, dout, groups, K, w, scale)
+
+    def loss(qq, kk, vv):
+        o, _, _ = _run(qq, kk, vv, groups, K, w, scale)
+        return float((o * dout.astype(np.float64)).sum())
+
+    h = np.float32(2.0 ** -10)
+    for which, arr in enumerate((q, k, v)):
+        for _ in range(12):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] = arr[idx] + h
+            minus[idx] = arr[idx] - h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = plus, minus
+            fd = (loss(*args_p) - loss(*args_m)) / (float(plus[idx]) - float(minus[idx]))
+            an = grads[which][idx]
+            assert abs(fd - an) <= 2e-5 + 1e-4 * abs(an), (which, idx, fd, an)
+
+
+@pytest.mark.parametrize("case", ["K1", "window_ge_n"])
+def test_attn_bwd_reduces_to_dense_causal(case):
+    rng = np.random.default_rng(22 + len(case))
+    hq, hkv, n, d = 4, 2, 90, 16
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    dout = rng.standard_normal((hq, n, d)).astype(np.float32)
+    if case == "K1":
+        K, w, groups = 1, 5, np.zeros((hkv, n, 1), np.int32)
+    else:
+        K, w, groups = 4, n, _random_groups(rng, hkv, n, 4, 1)
+    got = oracle.attn_bwd(q, k, v, dout, groups, K, w, 0.3)
+    causal = np.broadcast_to(np.tril(np.ones((n, n), bool)), (hq, n, n))
+    _assert_grads(got, _library_grads(q, k, v, dout, 0.3, causal))
+
+
+def test_attn_bwd_w1_top1_is_causal_within_each_group():
+    """w = 1, top-1: each group's subsequence is textbook causal attention,
+    so its gradients are those of that attention alone."""
+    rng = np.random.default_rng(23)
+    hq, hkv, n, d, K = 2, 2, 120, 8, 4
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    dout = rng.standard_normal((hq, n, d)).astype(np.float32)
+    groups = _random_groups(rng, hkv, n, K, 1)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, dout, groups, K, 1, 0.4)
+    for h in range(hq):
+        for g in range(K):
+            idx = np.nonzero(groups[h, :, 0] == g)[0]
+            if idx.size == 0:
+                continue
+            m = idx.size
+            causal = np.tril(np.ones((m, m), bool))[None]
+            rq, rk, rv = _library_grads(q[h:h + 1, idx], k[h:h + 1, idx], v[h:h + 1, idx],
+                                        dout[h:h + 1, idx], 0.4, causal)
+            _assert_grads((dq[h, idx], dk[h, idx], dv[h, idx]), (rq[0], rk[0], rv[0]))
+
+
+def test_attn_bwd_brute_force_mask_small():
+    """Random top-2 routing with grouped-query heads: equal to autograd
+    through a softmax under the explicit mask of A(i)."""
+    rng = np.random.default_rng(24)
+    hq, hkv, n, d, K, w = 4, 2, 80, 16, 4, 6
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    dout = rng.standard_normal((hq, n, d)).astype(np.float32)
+    groups = _random_groups(rng, hkv, n, K, 2)
+    mask = np.repeat(_set_mask(groups, w), hq // hkv, axis=0)
+    got = oracle.attn_bwd(q, k, v, dout, groups, K, w, 0.25)
+    _assert_grads(got, _library_grads(q, k, v, dout, 0.25, mask))
+    # rows-only dq agrees with the full computation
+    rh = np.array([0, 1, 3, 2], np.int32)
+    rp = np.array([0, 5, 79, 40], np.int64)
+    dq_rows = oracle.attn_bwd_rows(q, k, v, dout, groups, K, w, 0.25, rh, rp)
+    np.testing.assert_allclose(dq_rows, got[0][rh, rp], atol=1e-12, rtol=0)
+
+
+def test_attn_bwd_column_identities():
+    """Each row's softmax weights sum to one and its dS sums to zero, so
+    sum_j dv_j equals the sum of dout over the query heads of the key/value
+    head, and sum_j dk_j = 0."""
+    rng = np.random.default_rng(25)
+    hq, hkv, n, d, K, w = 4, 2, 100, 8, 3, 3
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    dout = rng.standard_normal((hq, n, d)).astype(np.float32)
+    groups = _random_groups(rng, hkv, n, K, 1)
+    _, dk, dv = oracle.attn_bwd(q, k, v, dout, groups, K, w, 0.5)
+    r = hq // hkv
+    for hk in range(hkv):
+        want = dout[hk * r:(hk + 1) * r].astype(np.float64).sum(axis=(0, 1))
+        np.testing.assert_allclose(dv[hk].sum(0), want, atol=1e-9, rtol=0)
+        np.testing.assert_allclose(dk[hk].sum(0), 0.0, atol=1e-9)
