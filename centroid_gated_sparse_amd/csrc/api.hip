@@ -239,6 +239,58 @@ focus_status focus_attn_fwd(const void *q, const void *k, const void *v, focus_d
                                FOCUS_PART_ALL, stream);
 }
 
+size_t focus_attn_bwd_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
+                                      int32_t d, int32_t K, int32_t topk)
+{
+    if (dt != FOCUS_BF16 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || n > INT32_MAX / 2 ||
+        (d != 64 && d != 128) || K < 1 || K > kMaxGroups || topk < 1 || topk > K ||
+        n * (int64_t)topk > INT32_MAX)
+        return 0;
+    AttnShape sh{dt, Hq, Hkv, d, K, topk, n, 0, 1.f};
+    return attn_bwd_workspace_bytes(sh);
+}
+
+focus_status focus_attn_bwd(const void *q, const void *k, const void *v, const void *out,
+                            const float *lse, const void *dout, focus_dtype dt, int32_t Hq,
+                            int32_t Hkv, int64_t n, int32_t d, const uint32_t *gmask,
+                            const int32_t *offsets, const int32_t *tokens,
+                            const int32_t *slot_entry, int32_t K, int32_t topk, int64_t window,
+                            float scale, void *dq, void *dk, void *dv, void *workspace,
+                            size_t workspace_bytes, focus_stream stream)
+{
+    g_last_error[0] = 0;
+    focus_status st = check_attn(q, k, v, dt, Hq, Hkv, n, d);
+    if (st != FOCUS_OK)
+        return st;
+    if (dt != FOCUS_BF16)
+        return unsupported("the backward takes bf16 inputs");
+    FOCUS_PTR(out);
+    FOCUS_PTR(lse);
+    FOCUS_PTR(dout);
+    FOCUS_PTR(gmask);
+    FOCUS_PTR(offsets);
+    FOCUS_PTR(tokens);
+    FOCUS_PTR(slot_entry);
+    FOCUS_PTR(dq);
+    FOCUS_PTR(dk);
+    FOCUS_PTR(dv);
+    FOCUS_REQUIRE(K >= 1, "K=%d", K);
+    if (K > kMaxGroups)
+        return unsupported("at most 32 centroids");
+    FOCUS_REQUIRE(topk >= 1 && topk <= K, "topk=%d K=%d", topk, K);
+    FOCUS_REQUIRE(window >= 0, "window=%lld", (long long)window);
+    FOCUS_REQUIRE(n * (int64_t)topk <= INT32_MAX, "n*topk exceeds int32");
+    FOCUS_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+    AttnShape sh{dt, Hq, Hkv, d, K, topk, n, window, scale};
+    const size_t need = attn_bwd_workspace_bytes(sh);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+        return short_workspace(workspace_bytes, need);
+    hipError_t e = launch_attn_bwd(sh, q, k, v, out, lse, dout, gmask, offsets, tokens,
+                                   slot_entry, dq, dk, dv, workspace,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_attn_bwd launch");
+}
+
 size_t focus_dense_workspace_bytes(focus_dtype dt, int32_t Hkv, int64_t n, int32_t d)
 {
     if (Hkv < 1 || n < 1 || (d != 64 && d != 128))

@@ -60,4 +60,12 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
 hipError_t launch_dense(const AttnShape &sh, const void *q, const void *k, const void *v,
                         void *out, float *lse, void *ws, hipStream_t s);
 
+// ---- attn_bwd.hip
+size_t attn_bwd_workspace_bytes(const AttnShape &sh);
+hipError_t launch_attn_bwd(const AttnShape &sh, const void *q, const void *k, const void *v,
+                           const void *out, const float *lse, const void *dout,
+                           const uint32_t *gmask, const int32_t *offsets, const int32_t *tokens,
+                           const int32_t *slot_entry, void *dq, void *dk, void *dv, void *ws,
+                           hipStream_t s);
+
 }  // namespace focus

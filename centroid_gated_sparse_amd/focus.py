@@ -4,7 +4,8 @@ the library's HIP kernels.  Raises if the library has not been built or a
 call returns an error status.
 
 The call names match the C ABI: focus_route, focus_route_project,
-focus_bucket, focus_attn_fwd (+ focus_attn_fwd_part), focus_dense_causal_fwd.  ``focus_forward`` chains
+focus_bucket, focus_attn_fwd (+ focus_attn_fwd_part), focus_attn_bwd,
+focus_dense_causal_fwd.  ``focus_forward`` chains
 the three calls and allocates outputs and workspaces with torch.
 """
 from __future__ import annotations
@@ -27,6 +28,7 @@ SYMBOLS = (
     "focus_route", "focus_route_project", "focus_bucket_workspace_bytes", "focus_bucket",
     "focus_attn_workspace_bytes", "focus_attn_fwd", "focus_attn_fwd_part",
     "focus_dense_workspace_bytes", "focus_dense_causal_fwd",
+    "focus_attn_bwd_workspace_bytes", "focus_attn_bwd",
 )
 
 _lib = None
@@ -71,8 +73,12 @@ def lib() -> ctypes.CDLL:
     L.focus_dense_workspace_bytes.restype = sz
     L.focus_dense_causal_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i32, i64, i32, f32,
                                          P, P, P, sz, P]
+    L.focus_attn_bwd_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i64, i32, i32, i32]
+    L.focus_attn_bwd_workspace_bytes.restype = sz
+    L.focus_attn_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, i32, i32, i64, i32, P, P, P, P,
+                                 i32, i32, i64, f32, P, P, P, P, sz, P]
     for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_attn_fwd",
-                 "focus_attn_fwd_part", "focus_dense_causal_fwd"):
+                 "focus_attn_fwd_part", "focus_dense_causal_fwd", "focus_attn_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -247,6 +253,39 @@ def focus_dense_causal_fwd(q, k, v, scale: float, out=None, lse=None, workspace=
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), Hq, Hkv, n, d, float(scale), _ptr(out),
         _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def focus_attn_bwd_workspace_bytes(dtype_code: int, Hq: int, Hkv: int, n: int, d: int,
+                                   K: int, topk: int) -> int:
+    return int(lib().focus_attn_bwd_workspace_bytes(dtype_code, Hq, Hkv, n, d, K, topk))
+
+
+def focus_attn_bwd(q, k, v, out, lse, dout, gmask, offsets, tokens, slot_entry, K: int,
+                   window: int, scale: float, dq=None, dk=None, dv=None, workspace=None,
+                   stream=None):
+    """Gradients of focus_attn_fwd: q, out, dout bf16 [Hq, n, d]; k, v bf16 [Hkv, n, d];
+    lse fp32 [Hq, n]; the routing and buckets of the forward.
+    Returns (dq [Hq, n, d], dk [Hkv, n, d], dv [Hkv, n, d]) in bf16."""
+    import torch
+
+    Hq, n, d = q.shape
+    Hkv = k.shape[0]
+    topk = slot_entry.shape[2]
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    if workspace is None:
+        need = focus_attn_bwd_workspace_bytes(_dtype_code(q), Hq, Hkv, n, d, K, topk)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("focus_attn_bwd", lib().focus_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _dtype_code(q), Hq, Hkv,
+        n, d, _ptr(gmask), _ptr(offsets), _ptr(tokens), _ptr(slot_entry), K, topk,
+        int(window), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return dq, dk, dv
 
 
 def focus_forward(q, k, v, r, centroids, topk: int, window: int, scale: float | None = None,

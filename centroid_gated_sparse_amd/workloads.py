@@ -204,3 +204,18 @@ def projection_inputs(pw: ProjectionWorkload, seed: int, device="cpu"):
         x[a:b] = torch.randn((b - a, pw.d_model), generator=gen, device=device,
                              dtype=torch.float32).to(dt)
     return x, np.ascontiguousarray(W), np.ascontiguousarray(c)
+
+
+def dout_input(wl: Workload, seed: int, device="cpu"):
+    """dL/dO for the backward: standard normal [Hq, n, d] in the workload
+    dtype, from a stream of its own (seed + 7919, so it never repeats q)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 7919)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    out = torch.empty((wl.hq, wl.n, wl.d), dtype=dt, device=device)
+    for h in range(wl.hq):
+        out[h] = torch.randn((wl.n, wl.d), generator=gen, device=device,
+                             dtype=torch.float32).to(dt)
+    return out

@@ -201,6 +201,44 @@ focus_status focus_attn_fwd_part(const void *q, const void *k, const void *v,
                                  focus_stream stream);
 
 /*
+ * focus_attn_bwd — gradients of focus_attn_fwd with respect to q, k and v
+ * for the hard attended set A(i) (the routing gets no gradient).  Needed to
+ * fine-tune or train through Focus attention (thelatestinai.com Table 5,
+ * all parameters fine-tuned; Technical Summary, from-scratch training).
+ * With P_ij = exp(scale q_i.k_j - lse_i) on A(i), D_i = dO_i . O_i,
+ * dP_ij = dO_i . v_j and dS_ij = P_ij (dP_ij - D_i):
+ *     dq_i = scale sum_j dS_ij k_j
+ *     dk_j = scale sum dS_ij q_i,  dv_j = sum P_ij dO_i
+ * the last two summed over every (query head, row) that attends to j.  Each
+ * pair is evaluated once, under the forward's partition (window pairs apart,
+ * far pairs in the bucket of the lowest shared group).
+ *
+ *   q, out, dout  bf16 [Hq, n, d]  forward inputs, its output, and dL/dO
+ *   k, v          bf16 [Hkv, n, d]
+ *   lse           fp32 [Hq, n]     the forward's log-sum-exp
+ *   gmask, offsets, tokens, slot_entry   the routing and buckets the
+ *                 forward used; K, topk, window, scale as in the forward
+ *   dq            bf16 [Hq, n, d]  out
+ *   dk, dv        bf16 [Hkv, n, d] out
+ *   workspace     >= focus_attn_bwd_workspace_bytes(...) bytes: fp32
+ *                 partials of every row and bucket entry, the tile plan
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are
+ * rounded to bf16 as MFMA operands; outputs rounded to nearest even.
+ * Deterministic (no atomics): two runs give the same bits.
+ * Errors: INVALID_ARGUMENT as focus_attn_fwd; UNSUPPORTED for dt other than
+ * FOCUS_BF16, d not in {64, 128} or K > 32; WORKSPACE if short.
+ */
+size_t focus_attn_bwd_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
+                                      int32_t d, int32_t K, int32_t topk);
+focus_status focus_attn_bwd(const void *q, const void *k, const void *v, const void *out,
+                            const float *lse, const void *dout, focus_dtype dt, int32_t Hq,
+                            int32_t Hkv, int64_t n, int32_t d, const uint32_t *gmask,
+                            const int32_t *offsets, const int32_t *tokens,
+                            const int32_t *slot_entry, int32_t K, int32_t topk,
+                            int64_t window, float scale, void *dq, void *dk, void *dv,
+                            void *workspace, size_t workspace_bytes, focus_stream stream);
+
+/*
  * focus_dense_causal_fwd — plain causal attention (every j <= i) with the
  * same window kernel and layouts; the dense baseline that Focus is compared
  * against (thelatestinai.com Table 6 compares against full attention).

@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(F.SYMBOLS)
@@ -145,6 +145,33 @@ def test_attn_rejects_bad_arguments(L):
     d = L.focus_dense_causal_fwd
     assert d(FAKE, FAKE, FAKE, 1, 8, 3, 256, 128, 0.1, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert d(FAKE, FAKE, FAKE, 1, 8, 2, 256, 64, 0.1, FAKE, FAKE, None, 0, None) == 3
+
+
+def _bwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dt=F.FOCUS_BF16, Hq=8,
+             Hkv=2, n=256, d=128, gmask=FAKE, offsets=FAKE, tokens=FAKE, slot=FAKE, K=4,
+             topk=2, window=16, scale=0.088, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@no_gpu
+def test_attn_bwd_rejects_bad_arguments(L):
+    f = L.focus_attn_bwd
+    assert f(*_bwd_args(dt=F.FOCUS_F32)) == 2          # bf16 only
+    assert f(*_bwd_args(d=96)) == 2
+    assert f(*_bwd_args(Hq=7)) == 1                    # Hq % Hkv
+    assert f(*_bwd_args(dout=None)) == 1
+    assert f(*_bwd_args(lse=FAKE + 4)) == 1
+    assert f(*_bwd_args(dv=None)) == 1
+    assert f(*_bwd_args(window=-1)) == 1
+    assert f(*_bwd_args(topk=5)) == 1
+    assert f(*_bwd_args(wsb=64)) == 3
+    assert F.focus_attn_bwd_workspace_bytes(F.FOCUS_F32, 8, 2, 256, 128, 4, 2) == 0
+    ws = F.focus_attn_bwd_workspace_bytes(F.FOCUS_BF16, 8, 2, 256, 128, 4, 2)
+    # at least the fp32 partials of every row and entry
+    assert ws >= 4 * 128 * (8 * 256 + 2 * 2 * 256 + 8 * 512 + 2 * 2 * 512)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
