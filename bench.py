@@ -303,6 +303,56 @@ def run_project(steps: int, warmup: int) -> int:
     return 0
 
 
+def run_backward(workload: str, steps: int, warmup: int) -> int:
+    """focus_attn_bwd after one forward at a workload: one JSON object with the
+    backward's time, tokens/s and MFMA roofline.  Algorithmic work: 10 d FLOPs
+    per surviving pair (S, dP, dV, dK, dQ at 2 d each); the kernels execute
+    14 d (the dq pass recomputes S and dP)."""
+    import torch
+
+    from centroid_gated_sparse_amd import focus as F
+    from centroid_gated_sparse_amd.workloads import (WORKLOADS, dout_input, qkv_inputs,
+                                                     routing_inputs, seed_for)
+
+    F.lib()
+    wl = WORKLOADS[workload]
+    seed = seed_for(wl.name)
+    c, r, _ = routing_inputs(wl, seed)
+    rt = torch.from_numpy(r).cuda()
+    ct = torch.from_numpy(c).cuda()
+    q, k, v = qkv_inputs(wl, seed, "cuda")
+    dout = dout_input(wl, seed, "cuda")
+    step, b = make_step(F, wl, q, k, v, rt, ct)
+    step()
+    del b["aws"]
+    torch.cuda.empty_cache()
+    H, n, K, topk = wl.hkv, wl.n, wl.K, wl.topk
+    need = F.focus_attn_bwd_workspace_bytes(F.FOCUS_BF16, wl.hq, H, n, wl.d, K, topk)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    log(f"backward: workload {wl.name}, workspace {need / 2**30:.2f} GiB")
+
+    def bwd():
+        F.focus_attn_bwd(q, k, v, b["out"], b["lse"], dout, b["gmask"], b["offsets"],
+                         b["tokens"], b["slot_entry"], K, wl.window, wl.scale, dq, dk, dv, ws)
+
+    ms = timed_ms(bwd, warmup, steps)
+    surv = int(surviving_pairs(b["groups"].cpu().numpy(), K, wl.window).sum()) * (wl.hq // H)
+    achieved = 10.0 * wl.d * surv / (ms / 1e3) / 1e12
+    out = {
+        "bench": "backward", "workload": wl.name, "n": n, "q_heads": wl.hq, "kv_heads": H,
+        "head_dim": wl.d, "centroids": K, "topk": topk, "window": wl.window,
+        "dtype": "bf16", "ms": ms, "tokens_per_s": n / (ms / 1e3),
+        "surviving_pairs": surv,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "flops_per_pair": 10 * wl.d, "executed_flops_per_pair": 14 * wl.d},
+    }
+    log(f"backward: {ms:.1f} ms, {achieved:.0f} TFLOP/s algorithmic")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +365,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the Table 6 context sweep (Focus vs our dense kernel)")
+    ap.add_argument("--backward", action="store_true",
+                    help="only time focus_attn_bwd at --workload")
     ap.add_argument("--project", action="store_true",
                     help="only time the fused routing projection (focus_route_project)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -341,6 +393,8 @@ def main() -> int:
         return run_sweep(args.steps, args.warmup)
     if args.project:
         return run_project(max(args.steps, 5), args.warmup)
+    if args.backward:
+        return run_backward(args.workload, args.steps, args.warmup)
 
     from centroid_gated_sparse_amd import focus as F
     from centroid_gated_sparse_amd.workloads import (WORKLOADS, qkv_inputs, routing_inputs,

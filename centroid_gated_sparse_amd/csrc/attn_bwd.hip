@@ -235,66 +235,70 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
     n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
 
     int it_sub = 0, it_tile = 0;
-    // origin, valid key count and owner flag of the next tile
-    auto next_tile = [&](int &valid, int &owner) -> int64_t {
+    // origin, valid key count and owner flag of the next tile, in order
+    struct TileDesc {
+        int64_t origin;
+        int valid, owner;
+    };
+    auto next_tile = [&]() -> TileDesc {
+        TileDesc t;
         if (GROUP) {
             while (it_tile * kQKeys >= sub_count[it_sub]) {
                 ++it_sub;
                 it_tile = 0;
             }
-            valid = std::min(kQKeys, sub_count[it_sub] - it_tile * kQKeys);
-            owner = sub_owner[it_sub];
-            const int64_t o = (int64_t)sub_start[it_sub] + (int64_t)it_tile * kQKeys;
-            ++it_tile;
-            return o;
+            t.valid = std::min(kQKeys, sub_count[it_sub] - it_tile * kQKeys);
+            t.owner = sub_owner[it_sub];
+            t.origin = (int64_t)sub_start[it_sub] + (int64_t)it_tile * kQKeys;
+        } else {
+            t.origin = j_first + (int64_t)it_tile * kQKeys;
+            t.valid = (int)std::min<int64_t>(kQKeys, p.n - t.origin);
+            t.owner = 0;
         }
-        const int64_t o = j_first + (int64_t)it_tile * kQKeys;
         ++it_tile;
-        valid = (int)std::min<int64_t>(kQKeys, p.n - o);
-        owner = 0;
-        return o;
+        return t;
     };
 
-    // staging registers: CHUNKS chunks of K and of V rows, plus key metadata
+    // Staging: thread t stages key row (t % 64) of a tile, chunks c = 4 i + t / 64 of
+    // its K and V rows.  The key's position (a bucket lookup in the group pass)
+    // is fetched one tile ahead of its rows, so no load waits on another in
+    // the loop.
+    const int srow = threadIdx.x % kQKeys;
+    const int sc0 = threadIdx.x / kQKeys;
+    auto key_pos = [&](const TileDesc &t) -> int {
+        const int r = std::min(srow, t.valid - 1);
+        return GROUP ? tok[t.origin + r] : (int)(t.origin + r);
+    };
+    // (rows past the tile's end load a valid row and are zeroed when they
+    // land, so that no load has to complete before the next is issued)
     uint4 kr[CHUNKS], vr[CHUNKS];
     int kp = kNoPos;
     uint32_t kg = 0;
-    int cur_owner = 0;
-    auto fetch = [&](int64_t origin, int valid) {
+    auto fetch = [&](const TileDesc &t, int pos) {
+        const int64_t base = ((int64_t)kvh * p.n + pos) * D;
 #pragma unroll
         for (int i = 0; i < CHUNKS; ++i) {
-            const int P = i * kBwdThreads + threadIdx.x;
-            const int row = P / KCH, c = P % KCH;
-            const bool ok = row < valid;
-            int pos = 0;
-            if (ok)
-                pos = GROUP ? tok[origin + row] : (int)(origin + row);
-            const int64_t base = ((int64_t)kvh * p.n + pos) * D + c * 8;
-            kr[i] = ok ? *reinterpret_cast<const uint4 *>(p.k + base) : make_uint4(0, 0, 0, 0);
-            vr[i] = ok ? *reinterpret_cast<const uint4 *>(p.v + base) : make_uint4(0, 0, 0, 0);
+            const int c = 4 * i + sc0;
+            kr[i] = *reinterpret_cast<const uint4 *>(p.k + base + c * 8);
+            vr[i] = *reinterpret_cast<const uint4 *>(p.v + base + c * 8);
         }
-        if (threadIdx.x < kQKeys) {
-            const int row = threadIdx.x;
-            kp = kNoPos;
-            kg = 0;
-            if (row < valid) {
-                kp = GROUP ? tok[origin + row] : (int)(origin + row);
-                kg = gmh[kp];
-            }
-        }
+        kg = gmh[pos];
+        kp = srow < t.valid ? pos : kNoPos;
     };
     auto land = [&]() {
+        const bool ok = kp != kNoPos;
+        const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < CHUNKS; ++i) {
-            const int P = i * kBwdThreads + threadIdx.x;
-            const int row = P / KCH, c = P % KCH;
-            *reinterpret_cast<uint4 *>(k_lds + rslot<D>(row, c) * 16) = kr[i];
-            *reinterpret_cast<uint4 *>(v_lds + rslot<D>(row, c) * 16) = vr[i];
-            store_transposed<kQKeys / 8>(kt_lds, kr[i], row, c);
+            const int c = 4 * i + sc0;
+            const uint4 kx = ok ? kr[i] : z, vx = ok ? vr[i] : z;
+            *reinterpret_cast<uint4 *>(k_lds + rslot<D>(srow, c) * 16) = kx;
+            *reinterpret_cast<uint4 *>(v_lds + rslot<D>(srow, c) * 16) = vx;
+            store_transposed<kQKeys / 8>(kt_lds, kx, srow, c);
         }
         if (threadIdx.x < kQKeys) {
-            kpos_lds[threadIdx.x] = kp;
-            kgm_lds[threadIdx.x] = kg;
+            kpos_lds[srow] = kp;
+            kgm_lds[srow] = kp == kNoPos ? 0u : kg;
         }
     };
 
@@ -306,69 +310,132 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
             acc[db][r] = 0.f;
 
     const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
-    int valid0 = 0, owner0 = 0;
+    // tiles it (rows in registers), it + 1 (position known), it + 2
+    // Tile it's rows sit in registers while tile it+1's position is known;
+    // past the last tile the descriptors repeat it, so every load in the
+    // loop is unconditional (no register copy of a load in flight).
+    TileDesc t_cur{}, t_next{};
+    int pos_next = 0;
     if (n_tiles > 0) {
-        const int64_t o = next_tile(valid0, owner0);
-        fetch(o, valid0);
-        cur_owner = owner0;
+        t_cur = next_tile();
+        const int pos0 = key_pos(t_cur);
+        t_next = n_tiles > 1 ? next_tile() : t_cur;
+        pos_next = key_pos(t_next);
+        fetch(t_cur, pos0);
     }
+    // per-lane LDS slots of the MFMA A fragments: K and V rows (row sigma(m)
+    // of each 32-key block, chunk 2ks+h; the second block is 32 rows on) and
+    // K^T (row db*32+m, chunk 4kb+2h+t; later row blocks are 256 slots on)
+    int koff[KS], ktoff[4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        koff[ks] = rslot<D>(sigma(m), 2 * ks + h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        ktoff[j] = tslot<kQKeys / 8>(m, 4 * (j >> 1) + 2 * h + (j & 1));
+
     for (int it = 0; it < n_tiles; ++it) {
         __syncthreads();
         land();
-        const int owner = cur_owner;
+        const int owner = __builtin_amdgcn_readfirstlane(t_cur.owner);
+        const int valid = __builtin_amdgcn_readfirstlane(t_cur.valid);
+        const int origin = __builtin_amdgcn_readfirstlane((int)t_cur.origin);
         __syncthreads();
-        if (it + 1 < n_tiles) {
-            int valid, own;
-            const int64_t o = next_tile(valid, own);
-            fetch(o, valid);
-            cur_owner = own;
+        fetch(t_next, pos_next);
+        t_cur = t_next;
+        if (it + 2 < n_tiles)
+            t_next = next_tile();
+        pos_next = key_pos(t_next);
+
+        // The keys this lane's query takes form one interval [klo, khi] of
+        // the tile: in the window pass positions origin + kk with
+        // 0 <= qpos - kpos < w; in the group pass the keys ascend and the
+        // far ones (kpos <= qpos - w) are a prefix.
+        int klo = 0, khi = -1;
+        if (qvalid) {
+            if (GROUP) {
+                const int lim = qpos - w;
+                if (lim >= kpos_lds[valid - 1]) {
+                    khi = valid - 1;
+                } else {
+                    int lo = 0, hi = valid;
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (kpos_lds[mid] <= lim)
+                            lo = mid + 1;
+                        else
+                            hi = mid;
+                    }
+                    khi = lo - 1;
+                }
+            } else {
+                klo = std::max(0, qpos - origin - w + 1);
+                khi = std::min(qpos - origin, valid - 1);
+            }
         }
-        // S^T and dP^T for the two 32-key blocks, then dS^T as B fragments
+        const bool full = !owner && __builtin_amdgcn_ballot_w64(!(klo <= 0 && khi >= kQKeys - 1)) == 0;
+
+        // S^T and dP^T for the two 32-key blocks.  LDS fragments are read a
+        // block ahead: block 1's between block 0's MFMAs (into the same
+        // registers), K^T's between block 1's; the fences keep that order.
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[kb][r] = dp[kb][r] = 0.f;
+        bf16x8 fa[KS], fb[KS], ktf[DB][4];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            fa[ks] = lds16(k_lds, koff[ks]);
+            fb[ks] = lds16(v_lds, koff[ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks], qf[ks], s[0], 0, 0, 0);
+            dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks], dof[ks], dp[0], 0, 0, 0);
+            fa[ks] = lds16(k_lds, koff[ks] + 32 * KCH);
+            fb[ks] = lds16(v_lds, koff[ks] + 32 * KCH);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks], qf[ks], s[1], 0, 0, 0);
+            dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks], dof[ks], dp[1], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4 * DB / KS; ++q) {
+                const int f = ks * (4 * DB / KS) + q;
+                ktf[f / 4][f % 4] = lds16(kt_lds, ktoff[f % 4] + (f / 4) * 32 * (kQKeys / 8));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // dS^T = P^T (dP^T - D) as bf16 B fragments
         bf16x8 dsf[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s, dp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[r] = dp[r] = 0.f;
-            const int arow = kb * 32 + sigma(m);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(k_lds, rslot<D>(arow, 2 * ks + h)),
-                                                           qf[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    lds16(v_lds, rslot<D>(arow, 2 * ks + h)), dof[ks], dp, 0, 0, 0);
-            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int kk = kb * 32 + 16 * h + r;
-                const int kpos = kpos_lds[kk];
-                bool ok = qvalid && kpos != kNoPos;
-                if (GROUP) {
-                    ok = ok && (int64_t)qpos - kpos >= w;
-                    if (owner)
+                float pr = __builtin_amdgcn_exp2f(s[kb][r] * p.c - l2);
+                if (!full) {
+                    const int kk = kb * 32 + 16 * h + r;
+                    bool ok = kk >= klo && kk <= khi;
+                    if (GROUP && owner)
                         ok = ok && ((qgm & kgm_lds[kk] & low) == 0u);
-                } else {
-                    ok = ok && kpos <= qpos && qpos - kpos < w;
+                    pr = ok ? pr : 0.f;
                 }
-                const float pr = ok ? __builtin_amdgcn_exp2f(s[r] * p.c - l2) : 0.f;
-                s[r] = pr * (dp[r] - dq_d);
+                s[kb][r] = pr * (dp[kb][r] - dq_d);
             }
-            dsf[kb][0] = pack8(s, 0);
-            dsf[kb][1] = pack8(s, 1);
+            dsf[kb][0] = pack8(s[kb], 0);
+            dsf[kb][1] = pack8(s[kb], 1);
         }
         // dq^T += K^T dS^T
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + m;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        lds16(kt_lds, tslot<kQKeys / 8>(d, 4 * kb + 2 * h + t)), dsf[kb][t],
-                        acc[db], 0, 0, 0);
-        }
+            for (int j = 0; j < 4; ++j)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[db][j], dsf[j >> 1][j & 1],
+                                                                 acc[db], 0, 0, 0);
     }
 
     // ---- store: lane (m, h), register r of block db holds dq[query m][d]
@@ -401,8 +468,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     __shared__ __attribute__((aligned(16))) char qt_lds[D * kKQueries * 2];
     __shared__ __attribute__((aligned(16))) char dot_lds[D * kKQueries * 2];
     __shared__ int qpos_lds[kKQueries];
-    __shared__ float ql2_lds[kKQueries];
-    __shared__ float qd_lds[kKQueries];
+    __shared__ __attribute__((aligned(16))) float ql2_lds[kKQueries];
+    __shared__ __attribute__((aligned(16))) float qd_lds[kKQueries];
     __shared__ uint32_t qgm_lds[kKQueries];
     __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
 
@@ -496,7 +563,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     const int n_tiles = tiles_per_head * p.ratio;
 
     int it_head = 0, it_sub = 0, it_tile = 0, it_count = 0;
-    auto next_tile = [&](int &valid, int &owner, int &head) -> int64_t {
+    struct TileDesc {
+        int64_t origin;
+        int valid, owner, head;
+    };
+    auto next_tile = [&]() -> TileDesc {
         if (it_count == tiles_per_head) {  // next query head
             ++it_head;
             it_sub = 0;
@@ -504,74 +575,68 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             it_count = 0;
         }
         ++it_count;
-        head = kvh * p.ratio + it_head;
+        TileDesc t;
+        t.head = kvh * p.ratio + it_head;
         if (GROUP) {
             while (it_tile * kKQueries >= sub_count[it_sub]) {
                 ++it_sub;
                 it_tile = 0;
             }
-            valid = std::min(kKQueries, sub_count[it_sub] - it_tile * kKQueries);
-            owner = sub_owner[it_sub];
-            const int64_t o = (int64_t)sub_start[it_sub] + (int64_t)it_tile * kKQueries;
-            ++it_tile;
-            return o;
+            t.valid = std::min(kKQueries, sub_count[it_sub] - it_tile * kKQueries);
+            t.owner = sub_owner[it_sub];
+            t.origin = (int64_t)sub_start[it_sub] + (int64_t)it_tile * kKQueries;
+        } else {
+            t.origin = i_first + (int64_t)it_tile * kKQueries;
+            t.valid = (int)std::min<int64_t>(kKQueries, p.n - t.origin);
+            t.owner = 0;
         }
-        const int64_t o = i_first + (int64_t)it_tile * kKQueries;
         ++it_tile;
-        valid = (int)std::min<int64_t>(kKQueries, p.n - o);
-        owner = 0;
-        return o;
+        return t;
     };
 
+    // Staging: thread t stages query row (t % 32), chunks c = 8 i + t / 32 of
+    // its Q and dO rows, and (t < 32) the row's position, log2-domain LSE, D
+    // and group bits.  Positions are fetched one tile ahead of the rows.
+    const int srow = threadIdx.x % kKQueries;
+    const int sc0 = threadIdx.x / kKQueries;
+    auto query_pos = [&](const TileDesc &t) -> int {
+        const int r = std::min(srow, t.valid - 1);
+        return GROUP ? tok[t.origin + r] : (int)(t.origin + r);
+    };
     uint4 qr_[CHUNKS], dr_[CHUNKS];
     int qp = kNoPos;
     float ql2 = 0.f, qd = 0.f;
     uint32_t qg = 0;
-    int cur_owner = 0;
-    auto fetch = [&](int64_t origin, int valid, int head) {
+    auto fetch = [&](const TileDesc &t, int pos) {
+        const int64_t qrow = (int64_t)t.head * p.n + pos;
 #pragma unroll
         for (int i = 0; i < CHUNKS; ++i) {
-            const int P = i * kBwdThreads + threadIdx.x;
-            const int row = P / KCH, c = P % KCH;
-            const bool ok = row < valid;
-            int pos = 0;
-            if (ok)
-                pos = GROUP ? tok[origin + row] : (int)(origin + row);
-            const int64_t base = ((int64_t)head * p.n + pos) * D + c * 8;
-            qr_[i] = ok ? *reinterpret_cast<const uint4 *>(p.q + base) : make_uint4(0, 0, 0, 0);
-            dr_[i] =
-                ok ? *reinterpret_cast<const uint4 *>(p.dout + base) : make_uint4(0, 0, 0, 0);
+            const int c = 8 * i + sc0;
+            qr_[i] = *reinterpret_cast<const uint4 *>(p.q + qrow * D + c * 8);
+            dr_[i] = *reinterpret_cast<const uint4 *>(p.dout + qrow * D + c * 8);
         }
-        if (threadIdx.x < kKQueries) {
-            const int row = threadIdx.x;
-            qp = kNoPos;
-            ql2 = 0.f;
-            qd = 0.f;
-            qg = 0;
-            if (row < valid) {
-                qp = GROUP ? tok[origin + row] : (int)(origin + row);
-                const int64_t qrow = (int64_t)head * p.n + qp;
-                ql2 = p.lse[qrow] * kLog2e;
-                qd = p.drow[qrow];
-                qg = gmh[qp];
-            }
-        }
+        ql2 = p.lse[qrow] * kLog2e;
+        qd = p.drow[qrow];
+        qg = gmh[pos];
+        qp = srow < t.valid ? pos : kNoPos;
     };
     auto land = [&]() {
+        const bool ok = qp != kNoPos;
+        const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < CHUNKS; ++i) {
-            const int P = i * kBwdThreads + threadIdx.x;
-            const int row = P / KCH, c = P % KCH;
-            *reinterpret_cast<uint4 *>(q_lds + rslot<D>(row, c) * 16) = qr_[i];
-            *reinterpret_cast<uint4 *>(do_lds + rslot<D>(row, c) * 16) = dr_[i];
-            store_transposed<kKQueries / 8>(qt_lds, qr_[i], row, c);
-            store_transposed<kKQueries / 8>(dot_lds, dr_[i], row, c);
+            const int c = 8 * i + sc0;
+            const uint4 qx = ok ? qr_[i] : z, dx = ok ? dr_[i] : z;
+            *reinterpret_cast<uint4 *>(q_lds + rslot<D>(srow, c) * 16) = qx;
+            *reinterpret_cast<uint4 *>(do_lds + rslot<D>(srow, c) * 16) = dx;
+            store_transposed<kKQueries / 8>(qt_lds, qx, srow, c);
+            store_transposed<kKQueries / 8>(dot_lds, dx, srow, c);
         }
         if (threadIdx.x < kKQueries) {
-            qpos_lds[threadIdx.x] = qp;
-            ql2_lds[threadIdx.x] = ql2;
-            qd_lds[threadIdx.x] = qd;
-            qgm_lds[threadIdx.x] = qg;
+            qpos_lds[srow] = qp;
+            ql2_lds[srow] = ok ? ql2 : 0.f;
+            qd_lds[srow] = ok ? qd : 0.f;
+            qgm_lds[srow] = ok ? qg : 0u;
         }
     };
 
@@ -583,69 +648,128 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             dk_acc[db][r] = dv_acc[db][r] = 0.f;
 
     const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
+    TileDesc t_cur{}, t_next{};
+    int pos_next = 0;
     if (n_tiles > 0) {
-        int valid, own, head;
-        const int64_t o = next_tile(valid, own, head);
-        fetch(o, valid, head);
-        cur_owner = own;
+        t_cur = next_tile();
+        const int pos0 = query_pos(t_cur);
+        t_next = n_tiles > 1 ? next_tile() : t_cur;
+        pos_next = query_pos(t_next);
+        fetch(t_cur, pos0);
     }
+    // per-lane LDS slots: Q and dO rows (row sigma(m), chunk 2ks+h) and
+    // Q^T / dO^T (row db*32+m, chunk 2h+t; later row blocks 128 slots on)
+    int qoff[KS], qtoff[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qoff[ks] = rslot<D>(sigma(m), 2 * ks + h);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        qtoff[t] = tslot<kKQueries / 8>(m, 2 * h + t);
+
     for (int it = 0; it < n_tiles; ++it) {
         __syncthreads();
         land();
-        const int owner = cur_owner;
+        const int owner = __builtin_amdgcn_readfirstlane(t_cur.owner);
+        const int valid = __builtin_amdgcn_readfirstlane(t_cur.valid);
+        const int origin = __builtin_amdgcn_readfirstlane((int)t_cur.origin);
         __syncthreads();
-        if (it + 1 < n_tiles) {
-            int valid, own, head;
-            const int64_t o = next_tile(valid, own, head);
-            fetch(o, valid, head);
-            cur_owner = own;
+        fetch(t_next, pos_next);
+        t_cur = t_next;
+        if (it + 2 < n_tiles)
+            t_next = next_tile();
+        pos_next = query_pos(t_next);
+
+        // The queries that see this lane's key form one interval [qlo, qhi]
+        // of the tile: positions origin + qi with 0 <= qpos - kpos < w in the
+        // window pass; in the group pass the queries ascend and the far ones
+        // (qpos >= kpos + w) are a suffix.
+        int qlo = 0, qhi = -1;
+        if (kvalid) {
+            if (GROUP) {
+                const int lim = kpos + w;
+                qhi = valid - 1;
+                if (qpos_lds[0] < lim) {
+                    int lo = 0, hi = valid;
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (qpos_lds[mid] < lim)
+                            lo = mid + 1;
+                        else
+                            hi = mid;
+                    }
+                    qlo = lo;
+                }
+            } else {
+                qlo = std::max(0, kpos - origin);
+                qhi = std::min(valid - 1, kpos - origin + w - 1);
+            }
         }
-        // S = Q K^T and dP = dO V^T: rows are queries (sigma), columns keys
+        const bool full =
+            !owner && __builtin_amdgcn_ballot_w64(!(qlo <= 0 && qhi >= kKQueries - 1)) == 0;
+
+        // S = Q K^T and dP = dO V^T: rows are queries (sigma), columns keys.
+        // The Q / dO fragments are read first; the Q^T / dO^T fragments of
+        // the second product are read between the MFMAs (fenced order).
+        bf16x8 qfr[KS], dfr[KS], dtf[DB][2], qtf[DB][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qfr[ks] = lds16(q_lds, qoff[ks]);
+            dfr[ks] = lds16(do_lds, qoff[ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = dp[r] = 0.f;
-        const int arow = sigma(m);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(q_lds, rslot<D>(arow, 2 * ks + h)),
-                                                       kf[ks], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(do_lds, rslot<D>(arow, 2 * ks + h)),
-                                                        vf[ks], dp, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[ks], kf[ks], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[ks], vf[ks], dp, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 2 * DB / KS; ++q) {
+                const int f = ks * (2 * DB / KS) + q;  // f / 2 = db, f % 2 = t
+                dtf[f / 2][f % 2] = lds16(dot_lds, qtoff[f % 2] + (f / 2) * 32 * (kKQueries / 8));
+                qtf[f / 2][f % 2] = lds16(qt_lds, qtoff[f % 2] + (f / 2) * 32 * (kKQueries / 8));
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // P and dS, four queries at a time (their log2-domain LSE and D are
+        // read as vectors: queries 16h + 4j .. 16h + 4j + 3)
         f32x16 ds;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qi = 16 * h + r;
-            const int qpos = qpos_lds[qi];
-            bool ok = kvalid && qpos != kNoPos;
-            if (GROUP) {
-                ok = ok && (int64_t)qpos - kpos >= w;
-                if (owner)
-                    ok = ok && ((qgm_lds[qi] & kgm & low) == 0u);
-            } else {
-                ok = ok && kpos <= qpos && qpos - kpos < w;
+        for (int j = 0; j < 4; ++j) {
+            const float4 l4 = reinterpret_cast<const float4 *>(ql2_lds)[4 * h + j];
+            const float4 d4 = reinterpret_cast<const float4 *>(qd_lds)[4 * h + j];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * j + u;
+                float pr = __builtin_amdgcn_exp2f(s[r] * p.c - lv[u]);
+                if (!full) {
+                    const int qi = 16 * h + r;
+                    bool ok = qi >= qlo && qi <= qhi;
+                    if (GROUP && owner)
+                        ok = ok && ((qgm_lds[qi] & kgm & low) == 0u);
+                    pr = ok ? pr : 0.f;
+                }
+                s[r] = pr;
+                ds[r] = pr * (dp[r] - dv4[u]);
             }
-            const float pr = ok ? __builtin_amdgcn_exp2f(s[r] * p.c - ql2_lds[qi]) : 0.f;
-            s[r] = pr;
-            ds[r] = pr * (dp[r] - qd_lds[qi]);
         }
         const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
         const bf16x8 dsf[2] = {pack8(ds, 0), pack8(ds, 1)};
         // dv^T += dO^T P, dk^T += Q^T dS
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + m;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                dv_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    lds16(dot_lds, tslot<kKQueries / 8>(d, 2 * h + t)), pf[t], dv_acc[db], 0, 0,
-                    0);
-                dk_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    lds16(qt_lds, tslot<kKQueries / 8>(d, 2 * h + t)), dsf[t], dk_acc[db], 0, 0,
-                    0);
+                dv_acc[db] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(dtf[db][t], pf[t], dv_acc[db], 0, 0, 0);
+                dk_acc[db] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf[db][t], dsf[t], dk_acc[db], 0, 0, 0);
             }
-        }
     }
 
     if (kvalid) {
