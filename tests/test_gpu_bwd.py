@@ -91,3 +91,60 @@ def test_backward_deterministic():
     _, b = gpu_backward(wl, c, r, q, k, v, dout)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_backward_medium_7b_shape_all_rows():
+    """The 7B grouped-query head shape (32/8 heads of 128) at n = 2500: 20
+    query tiles and a ragged tail, every gradient against the oracle."""
+    wl = W("bwd_gqa7b_n2500", 2500, 32, 8, 128, 4, 2, 256, "bf16", qkv_std=128 ** -0.5)
+    log(f"backward {wl}")
+    seed = 3100
+    c, r, _ = routing_inputs(wl, seed)
+    q, k, v = qkv_inputs(wl, seed, DEV)
+    dout = dout_input(wl, seed, DEV)
+    res, got = gpu_backward(wl, c, r, q, k, v, dout)
+    g_ref, _ = oracle.route(r, c, wl.topk)
+    ref = oracle.attn_bwd(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v),
+                          to_bf16_bits(dout), g_ref, wl.K, wl.window, wl.scale)
+    check_grads(wl.name, got, ref)
+
+
+@pytest.mark.parametrize("name", ["gqa7b_n128k_skew", "gqa7b_n1m_k8"])
+def test_backward_full_size(name):
+    """At the full workload sizes: dq of sampled rows against the oracle
+    (each row needs only its own attended set), and over every key the
+    column identities sum_j dv_j = sum of dO over the key/value head's query
+    heads and sum_j dk_j = 0 (each row's weights sum to one and its dS to
+    zero), checked against the L1 size of the summed gradients."""
+    from centroid_gated_sparse_amd.workloads import WORKLOADS, sample_rows, seed_for
+
+    wl = WORKLOADS[name]
+    seed = seed_for(name)
+    log(f"backward full size {wl}")
+    c, r, _ = routing_inputs(wl, seed)
+    q, k, v = qkv_inputs(wl, seed, DEV)
+    dout = dout_input(wl, seed, DEV)
+    res, (dq, dk, dv) = gpu_backward(wl, c, r, q, k, v, dout)
+    g_ref, _ = oracle.route(r, c, wl.topk)
+    assert np.array_equal(res["groups"].cpu().numpy(), g_ref)
+    del res
+    rh, rp = sample_rows(wl, seed, 256)
+    dq_ref = oracle.attn_bwd_rows(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v),
+                                  to_bf16_bits(dout), g_ref, wl.K, wl.window, wl.scale, rh, rp)
+    dq_s = dq[torch.from_numpy(rh).long().to(DEV), torch.from_numpy(rp).long().to(DEV)]
+    gv = dq_s.float().cpu().double().numpy()
+    err_max = np.abs(gv - dq_ref).max() / np.abs(dq_ref).max()
+    err_norm = np.linalg.norm(gv - dq_ref) / np.linalg.norm(dq_ref)
+    log(f"[{name}] sampled dq rows: max {err_max:.3e}, normwise {err_norm:.3e}")
+    assert err_max <= MAX_TOL and err_norm <= NORM_TOL
+    ratio = wl.hq // wl.hkv
+    for hk in range(wl.hkv):
+        sdv = dv[hk].double().sum(0)
+        want = dout[hk * ratio:(hk + 1) * ratio].double().sum((0, 1))
+        l1 = dv[hk].double().abs().sum(0)
+        rel_v = ((sdv - want).abs() / l1).max().item()
+        sdk = dk[hk].double().sum(0)
+        rel_k = (sdk.abs() / dk[hk].double().abs().sum(0)).max().item()
+        log(f"[{name}] head {hk}: |sum dv - sum dO| / sum|dv| = {rel_v:.2e}, "
+            f"|sum dk| / sum|dk| = {rel_k:.2e}")
+        assert rel_v <= 1e-2 and rel_k <= 1e-2
