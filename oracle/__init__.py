@@ -66,9 +66,12 @@ def _load():
                                          i64, f64, P, P, i64, P, i32]
     lib.oracle_attn_bwd.argtypes = [P, P, P, P, i32, i32, i32, i64, i32, P, i32, i32, i64,
                                     f64, P, P, P, i32]
+    lib.oracle_sinkhorn.argtypes = [P, P, i32, i64, i32, i32, i32, P]
+    lib.oracle_gated_attn_rows.argtypes = [P, P, P, i32, i32, i32, i64, i32, P, i32, i64, f64,
+                                           f64, P, P, i64, P, P, i32]
     for f in (lib.oracle_route, lib.oracle_bucket, lib.oracle_attn_rows,
               lib.oracle_pair_counts, lib.oracle_project, lib.oracle_attn_bwd_rows,
-              lib.oracle_attn_bwd):
+              lib.oracle_attn_bwd, lib.oracle_sinkhorn, lib.oracle_gated_attn_rows):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -263,3 +266,40 @@ def attn_bwd_rows(q, k, v, dout, groups: np.ndarray, K: int, window: int, scale:
                                         float(scale), _ptr(rh), _ptr(rp), rh.shape[0],
                                         _ptr(dq), int(nthreads)), "attn_bwd_rows")
     return dq
+
+
+def sinkhorn(r: np.ndarray, centroids: np.ndarray, iters: int) -> np.ndarray:
+    """Sinkhorn soft assignment of every token to the groups: float64
+    [H, n, K], rows summing to 1 and columns approaching n/K."""
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    H, n, dg = r.shape
+    K = c.shape[1]
+    A = np.empty((H, n, K), np.float64)
+    _check(_load().oracle_sinkhorn(_ptr(r), _ptr(c), H, n, dg, K, int(iters), _ptr(A)),
+           "sinkhorn")
+    return A
+
+
+def gated_attn_rows(q, k, v, A: np.ndarray, window: int, lam: float, scale: float,
+                    row_head: np.ndarray, row_pos: np.ndarray, nthreads: int = 0):
+    """Training-mode gated dense causal attention of the listed rows.
+    A: float64 [Hkv, n, K] assignment.  Returns (o [rows, d], lse [rows])."""
+    qa, qb = _as_raw(q)
+    ka, kb = _as_raw(k)
+    va, vb = _as_raw(v)
+    assert qb == kb == vb
+    Hq, n, d = qa.shape
+    Hkv = ka.shape[0]
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    assert A.shape[:2] == (Hkv, n)
+    K = A.shape[2]
+    rh = np.ascontiguousarray(row_head, dtype=np.int32)
+    rp = np.ascontiguousarray(row_pos, dtype=np.int64)
+    o = np.empty((rh.shape[0], d), np.float64)
+    lse = np.empty(rh.shape[0], np.float64)
+    _check(_load().oracle_gated_attn_rows(_ptr(qa), _ptr(ka), _ptr(va), qb, Hq, Hkv, n, d,
+                                          _ptr(A), K, int(window), float(lam), float(scale),
+                                          _ptr(rh), _ptr(rp), rh.shape[0], _ptr(o), _ptr(lse),
+                                          int(nthreads)), "gated_attn_rows")
+    return o, lse

@@ -636,3 +636,154 @@ done:
     free(bits);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Training-mode forward (Technical Summary, Core Architecture: soft
+ * assignment of each projected token to the groups; Gated Attention: the
+ * distant pairs pass a learned gate s_ij = q_i.k_j * sigmoid(lambda a_ij)
+ * with a_ij the group affinity; Key Technical Innovation: Sinkhorn
+ * normalisation replaces softmax so that group sizes stay balanced, a
+ * doubly-stochastic assignment; Significance: training still computes all
+ * O(n^2) pairs because of the soft gate).  Readings where the pages are
+ * silent:
+ *   - the assignment starts from exp(score - max over the token's groups),
+ *     score as in the routing above;
+ *   - one Sinkhorn iteration scales every group column to total n/K, then
+ *     every token row to total 1; `iters` iterations, so rows end summing
+ *     to 1 exactly and columns approach n/K;
+ *   - a_ij = sum_g A_ig A_jg, the chance that independent draws from the
+ *     two tokens' assignments pick the same group;
+ *   - lambda is a real scalar; the gate multiplies the score of the far
+ *     pairs (i - j >= w) only; window pairs keep the plain score; every
+ *     j <= i is attended (dense causal).
+ * ------------------------------------------------------------------------ */
+
+/* Sinkhorn assignment of every routing head: A [H, n, K] (double). */
+int oracle_sinkhorn(const float *r, const float *centroids, int32_t H, int64_t n,
+                    int32_t dg, int32_t K, int32_t iters, double *A)
+{
+    if (!r || !centroids || !A || H < 1 || n < 1 || dg < 1 || K < 1 || K > 32 || iters < 0)
+        return ORACLE_BAD_ARG;
+    double *col = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!col)
+        return ORACLE_NO_MEMORY;
+    for (int h = 0; h < H; ++h) {
+        double *Ah = A + (int64_t)h * n * K;
+        for (int64_t t = 0; t < n; ++t) {
+            const float *rt = r + ((int64_t)h * n + t) * dg;
+            double mx = -INFINITY;
+            for (int g = 0; g < K; ++g) {
+                double s = (double)score_fixed_order(rt, centroids + ((int64_t)h * K + g) * dg,
+                                                     dg);
+                Ah[t * K + g] = s;
+                if (s > mx)
+                    mx = s;
+            }
+            for (int g = 0; g < K; ++g)
+                Ah[t * K + g] = exp(Ah[t * K + g] - mx);
+        }
+        for (int it = 0; it < iters; ++it) {
+            /* columns to n / K */
+            for (int g = 0; g < K; ++g)
+                col[g] = 0.0;
+            for (int64_t t = 0; t < n; ++t)
+                for (int g = 0; g < K; ++g)
+                    col[g] += Ah[t * K + g];
+            for (int64_t t = 0; t < n; ++t)
+                for (int g = 0; g < K; ++g)
+                    Ah[t * K + g] *= ((double)n / K) / col[g];
+            /* rows to 1 */
+            for (int64_t t = 0; t < n; ++t) {
+                double rs = 0.0;
+                for (int g = 0; g < K; ++g)
+                    rs += Ah[t * K + g];
+                for (int g = 0; g < K; ++g)
+                    Ah[t * K + g] /= rs;
+            }
+        }
+    }
+    free(col);
+    return ORACLE_OK;
+}
+
+/* Gated dense causal attention for the listed (query head, row) pairs:
+ * logit_ij = scale * q_i.k_j * (i - j < w ? 1 : sigmoid(lambda a_ij)),
+ * softmax over every j <= i.  A is [Hkv, n, K] (double).  Outputs as in
+ * oracle_attn_rows (o, natural-log lse). */
+int oracle_gated_attn_rows(const void *q, const void *k, const void *v, int32_t is_bf16,
+                           int32_t Hq, int32_t Hkv, int64_t n, int32_t d, const double *A,
+                           int32_t K, int64_t w, double lambda, double scale,
+                           const int32_t *row_head, const int64_t *row_pos, int64_t nrows,
+                           double *o, double *lse, int32_t nthreads)
+{
+    if (!q || !k || !v || !A || !row_head || !row_pos || !o || !lse || Hq < 1 || Hkv < 1 ||
+        Hq % Hkv || n < 1 || d < 1 || K < 1 || w < 0 || nrows < 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t rr = 0; rr < nrows; ++rr)
+        if (row_head[rr] < 0 || row_head[rr] >= Hq || row_pos[rr] < 0 || row_pos[rr] >= n)
+            return ORACLE_BAD_ARG;
+    const int ratio = Hq / Hkv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *sc = (double *)malloc(sizeof(double) * (size_t)n);
+        double *qi = (double *)malloc(sizeof(double) * (size_t)d);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!sc || !qi || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t rr = 0; rr < nrows; ++rr) {
+            if (failed)
+                continue;
+            const int h = row_head[rr];
+            const int64_t i = row_pos[rr];
+            const int64_t hk = h / ratio;
+            const double *Ai = A + (hk * n + i) * K;
+            for (int e = 0; e < d; ++e)
+                qi[e] = widen(q, is_bf16, ((int64_t)h * n + i) * d + e);
+            double mx = -INFINITY;
+            for (int64_t j = 0; j <= i; ++j) {
+                double s = 0.0;
+                const int64_t kb = (hk * n + j) * d;
+                for (int e = 0; e < d; ++e)
+                    s += qi[e] * widen(k, is_bf16, kb + e);
+                double gate = 1.0;
+                if (i - j >= w) {
+                    const double *Aj = A + (hk * n + j) * K;
+                    double a = 0.0;
+                    for (int g = 0; g < K; ++g)
+                        a += Ai[g] * Aj[g];
+                    gate = 1.0 / (1.0 + exp(-lambda * a));
+                }
+                sc[j] = scale * s * gate;
+                if (sc[j] > mx)
+                    mx = sc[j];
+            }
+            double l = 0.0;
+            for (int e = 0; e < d; ++e)
+                acc[e] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                const double p = exp(sc[j] - mx);
+                l += p;
+                const int64_t vb = (hk * n + j) * d;
+                for (int e = 0; e < d; ++e)
+                    acc[e] += p * widen(v, is_bf16, vb + e);
+            }
+            for (int e = 0; e < d; ++e)
+                o[rr * d + e] = acc[e] / l;
+            lse[rr] = mx + log(l);
+        }
+        free(sc);
+        free(qi);
+        free(acc);
+    }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}

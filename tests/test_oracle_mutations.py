@@ -45,6 +45,20 @@ MUTATIONS = {
                       "if (!((i - j) <= w || (bk[i] & bk[j]) != 0))"),
     "bwd_d_unnormalised": ("dd += widen(dout, is_bf16, dob + e) * (acc[e] / l);",
                            "dd += widen(dout, is_bf16, dob + e) * acc[e];"),
+    "sinkhorn_skip_columns": ("Ah[t * K + g] *= ((double)n / K) / col[g];",
+                              "Ah[t * K + g] *= 1.0 + 0.0 * col[g];"),
+    "sinkhorn_rows_first": ("            /* columns to n / K */\n",
+                            "            for (int64_t t = 0; t < n; ++t) { double rs = 0.0;"
+                            " for (int g = 0; g < K; ++g) rs += Ah[t * K + g];"
+                            " for (int g = 0; g < K; ++g) Ah[t * K + g] /= rs; }\n"
+                            "            if (it == iters - 1) break;\n"),
+    "gate_on_window_pairs": ("                if (i - j >= w) {\n                    const double *Aj",
+                             "                if (1) {\n                    const double *Aj"),
+    "gate_sign": ("gate = 1.0 / (1.0 + exp(-lambda * a));", "gate = 1.0 / (1.0 + exp(lambda * a));"),
+    "affinity_first_group_only": ("                    for (int g = 0; g < K; ++g)\n"
+                                  "                        a += Ai[g] * Aj[g];",
+                                  "                    for (int g = 0; g < 1; ++g)\n"
+                                  "                        a += Ai[g] * Aj[g];"),
 }
 
 

@@ -537,3 +537,146 @@ def test_attn_bwd_column_identities():
         want = dout[hk * r:(hk + 1) * r].astype(np.float64).sum(axis=(0, 1))
         np.testing.assert_allclose(dv[hk].sum(0), want, atol=1e-9, rtol=0)
         np.testing.assert_allclose(dk[hk].sum(0), 0.0, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------
+# training-mode forward: Sinkhorn assignment and gated dense attention
+
+def _unit_scores_inputs(u, v):
+    """Routing vectors (u_t, v_t, 0, ...) against centroids e_0, e_1: the fixed-
+    order score of token t is exactly u_t for group 0 and v_t for group 1."""
+    n = len(u)
+    r = np.zeros((1, n, 16), np.float32)
+    r[0, :, 0] = u
+    r[0, :, 1] = v
+    c = np.zeros((1, 2, 16), np.float32)
+    c[0, 0, 0] = 1.0
+    c[0, 1, 1] = 1.0
+    return r, c
+
+
+def test_sinkhorn_rows_and_columns():
+    rng = np.random.default_rng(31)
+    H, n, K = 2, 300, 5
+    r = rng.standard_normal((H, n, 16)).astype(np.float32)
+    c = rng.standard_normal((H, K, 16)).astype(np.float32)
+    A1 = oracle.sinkhorn(r, c, 1)
+    np.testing.assert_allclose(A1.sum(-1), 1.0, atol=1e-12)
+    A = oracle.sinkhorn(r, c, 300)
+    np.testing.assert_allclose(A.sum(-1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(A.sum(1), n / K, rtol=1e-8)
+    assert (A > 0).all()
+
+
+def test_sinkhorn_uniform_and_single_group():
+    H, n = 1, 40
+    r = np.zeros((H, n, 16), np.float32)
+    c = np.random.default_rng(32).standard_normal((H, 4, 16)).astype(np.float32)
+    np.testing.assert_allclose(oracle.sinkhorn(r, c, 3), 0.25, atol=1e-15)
+    r1 = np.random.default_rng(33).standard_normal((H, n, 16)).astype(np.float32)
+    np.testing.assert_allclose(oracle.sinkhorn(r1, c[:, :1], 3), 1.0, atol=1e-15)
+
+
+def test_sinkhorn_two_by_two_closed_form():
+    """n = 2, K = 2: the doubly-stochastic scaling of a positive 2x2 matrix M
+    is [[x, 1-x], [1-x, x]] with x = sqrt(m00 m11) / (sqrt(m00 m11) +
+    sqrt(m01 m10))."""
+    u = np.array([0.5, -1.25], np.float32)
+    v = np.array([-0.75, 1.0], np.float32)
+    r, c = _unit_scores_inputs(u, v)
+    A = oracle.sinkhorn(r, c, 200)[0]
+    s = np.stack([u, v], 1).astype(np.float64)
+    M = np.exp(s - s.max(1, keepdims=True))
+    a, b = math.sqrt(M[0, 0] * M[1, 1]), math.sqrt(M[0, 1] * M[1, 0])
+    x = a / (a + b)
+    np.testing.assert_allclose(A, [[x, 1 - x], [1 - x, x]], atol=1e-12)
+
+
+def test_sinkhorn_one_iteration_worked_example():
+    """One iteration on n = 2 tokens, K = 2 groups, worked by hand: scale each
+    column of M to total n/K = 1, then each row to total 1."""
+    u = np.array([0.5, -1.25], np.float32)
+    v = np.array([-0.75, 1.0], np.float32)
+    r, c = _unit_scores_inputs(u, v)
+    A = oracle.sinkhorn(r, c, 1)[0]
+    m00, m01 = 1.0, math.exp(-0.75 - 0.5)      # token 0: max score 0.5 (group 0)
+    m10, m11 = math.exp(-1.25 - 1.0), 1.0      # token 1: max score 1.0 (group 1)
+    c0, c1 = m00 + m10, m01 + m11
+    b = [[m00 / c0, m01 / c1], [m10 / c0, m11 / c1]]
+    want = [[x / sum(row) for x in row] for row in b]
+    np.testing.assert_allclose(A, want, atol=1e-14)
+
+
+def test_sinkhorn_limit_is_a_diagonal_scaling():
+    """The Sinkhorn-Knopp limit is diag(a) M diag(b): log(A / M) is a sum of a
+    row term and a column term, so its double-centred residual vanishes."""
+    rng = np.random.default_rng(34)
+    n, K = 64, 4
+    u = rng.standard_normal((1, n, 16)).astype(np.float32)
+    cen = rng.standard_normal((1, K, 16)).astype(np.float32)
+    A = oracle.sinkhorn(u, cen, 500)[0]
+    s = np.array([[np.float32(0)] * K] * n, np.float64)
+    for t in range(n):
+        for g in range(K):
+            acc = np.float32(u[0, t, 0]) * np.float32(cen[0, g, 0])
+            for e in range(1, 16):
+                acc = np.float32(acc + np.float32(u[0, t, e]) * np.float32(cen[0, g, e]))
+            s[t, g] = acc
+    L = np.log(A) - s
+    resid = L - L.mean(1, keepdims=True) - L.mean(0, keepdims=True) + L.mean()
+    assert np.abs(resid).max() < 1e-9
+    np.testing.assert_allclose(A.sum(0), n / K, rtol=1e-9)
+
+
+def _gated_library(q, k, v, mult, scale):
+    """Library softmax (torch, float64) of scale * q.k * mult over j <= i."""
+    hq, n, _ = q.shape
+    kt = _expand_kv(k, hq)
+    vt = _expand_kv(v, hq)
+    s = torch.matmul(torch.from_numpy(q).double(), kt.transpose(-1, -2)) * scale
+    s = s * torch.from_numpy(mult).double()
+    causal = torch.ones(n, n, dtype=torch.bool).tril()
+    s = s.masked_fill(~causal, float("-inf"))
+    return (torch.matmul(torch.softmax(s, -1), vt).numpy(), torch.logsumexp(s, -1).numpy())
+
+
+def _all_rows(hq, n):
+    return (np.repeat(np.arange(hq, dtype=np.int32), n),
+            np.tile(np.arange(n, dtype=np.int64), hq))
+
+
+@pytest.mark.parametrize("case", ["lambda_large", "window_ge_n"])
+def test_gated_attention_reduces_to_dense_causal(case):
+    rng = np.random.default_rng(35 + len(case))
+    hq, hkv, n, d, K = 4, 2, 70, 16, 3
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    # mild scores keep every a_ij well above 0, so lambda a_ij is large
+    A = oracle.sinkhorn((0.1 * rng.standard_normal((hkv, n, 16))).astype(np.float32),
+                        rng.standard_normal((hkv, K, 16)).astype(np.float32), 3)
+    assert np.einsum("hik,hjk->hij", A, A).min() > 0.05
+    lam, w = (1e6, 4) if case == "lambda_large" else (-3.0, n)
+    rh, rp = _all_rows(hq, n)
+    o, lse = oracle.gated_attn_rows(q, k, v, A, w, lam, 0.3, rh, rp)
+    o_ref, lse_ref = _library_attention(q, k, v, 0.3, causal=True)
+    np.testing.assert_allclose(o.reshape(hq, n, d), o_ref, atol=1e-9)
+    np.testing.assert_allclose(lse.reshape(hq, n), lse_ref, atol=1e-9)
+
+
+def test_gated_attention_one_hot_assignment():
+    """One-hot assignments make a_ij 1 for tokens of one group and 0 otherwise,
+    so far pairs carry the factor sigmoid(lambda) or 1/2, window pairs 1."""
+    rng = np.random.default_rng(37)
+    hq, hkv, n, d, K, w, lam = 2, 1, 60, 8, 3, 5, 1.7
+    q, k, v = _rand_qkv(rng, hq, hkv, n, d)
+    z = rng.integers(0, K, n)
+    A = np.zeros((hkv, n, K))
+    A[0, np.arange(n), z] = 1.0
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    far_gate = np.where(z[:, None] == z[None, :], 1 / (1 + math.exp(-lam)), 0.5)
+    mult = np.broadcast_to(np.where(i - j < w, 1.0, far_gate), (hq, n, n)).copy()
+    rh, rp = _all_rows(hq, n)
+    o, lse = oracle.gated_attn_rows(q, k, v, A, w, lam, 0.45, rh, rp)
+    o_ref, lse_ref = _gated_library(q, k, v, mult, 0.45)
+    np.testing.assert_allclose(o.reshape(hq, n, d), o_ref, atol=1e-9)
+    np.testing.assert_allclose(lse.reshape(hq, n), lse_ref, atol=1e-9)
