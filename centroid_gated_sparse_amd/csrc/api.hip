@@ -291,6 +291,63 @@ focus_status focus_attn_bwd(const void *q, const void *k, const void *v, const v
     return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_attn_bwd launch");
 }
 
+size_t focus_sinkhorn_workspace_bytes(int32_t H, int64_t n)
+{
+    if (H < 1 || n < 1 || n > INT32_MAX)
+        return 0;
+    return sinkhorn_workspace_bytes(H, n);
+}
+
+focus_status focus_sinkhorn(const float *r, const float *centroids, int32_t H, int64_t n,
+                            int32_t d_g, int32_t K, int32_t iters, float *assign,
+                            void *workspace, size_t workspace_bytes, focus_stream stream)
+{
+    g_last_error[0] = 0;
+    FOCUS_PTR(r);
+    FOCUS_PTR(centroids);
+    FOCUS_PTR(assign);
+    FOCUS_REQUIRE(H >= 1 && n >= 1 && K >= 1, "H=%d n=%lld K=%d", H, (long long)n, K);
+    FOCUS_REQUIRE(n <= INT32_MAX, "n=%lld", (long long)n);
+    if (d_g != kRouteDim)
+        return unsupported("routing dimension must be 16");
+    if (K > kMaxGroups)
+        return unsupported("at most 32 centroids");
+    FOCUS_REQUIRE(iters >= 1 && iters <= 1000, "iters=%d", iters);
+    const size_t need = sinkhorn_workspace_bytes(H, n);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+        return short_workspace(workspace_bytes, need);
+    hipError_t e = launch_sinkhorn(r, centroids, H, n, K, iters, assign, workspace,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_sinkhorn launch");
+}
+
+focus_status focus_gated_attn_fwd(const void *q, const void *k, const void *v, focus_dtype dt,
+                                  int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
+                                  const float *assign, int32_t K, int64_t window, float lambda,
+                                  float scale, void *out, float *lse, focus_stream stream)
+{
+    g_last_error[0] = 0;
+    focus_status st = check_attn(q, k, v, dt, Hq, Hkv, n, d);
+    if (st != FOCUS_OK)
+        return st;
+    if (dt != FOCUS_BF16)
+        return unsupported("the gated forward takes bf16 inputs");
+    FOCUS_PTR(assign);
+    FOCUS_PTR(out);
+    FOCUS_PTR(lse);
+    FOCUS_REQUIRE(K >= 1, "K=%d", K);
+    if (K > kMaxGroups)
+        return unsupported("at most 32 centroids");
+    FOCUS_REQUIRE(window >= 0, "window=%lld", (long long)window);
+    FOCUS_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+    FOCUS_REQUIRE(lambda == lambda && lambda > -1e30f && lambda < 1e30f,
+                  "lambda must be finite");
+    AttnShape sh{dt, Hq, Hkv, d, K, 1, n, window, scale};
+    hipError_t e = launch_gated_attn(sh, q, k, v, assign, lambda, out, lse,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_gated_attn_fwd launch");
+}
+
 size_t focus_dense_workspace_bytes(focus_dtype dt, int32_t Hkv, int64_t n, int32_t d)
 {
     if (Hkv < 1 || n < 1 || (d != 64 && d != 128))

@@ -5,7 +5,7 @@ call returns an error status.
 
 The call names match the C ABI: focus_route, focus_route_project,
 focus_bucket, focus_attn_fwd (+ focus_attn_fwd_part), focus_attn_bwd,
-focus_dense_causal_fwd.  ``focus_forward`` chains
+focus_sinkhorn, focus_gated_attn_fwd, focus_dense_causal_fwd.  ``focus_forward`` chains
 the three calls and allocates outputs and workspaces with torch.
 """
 from __future__ import annotations
@@ -29,6 +29,7 @@ SYMBOLS = (
     "focus_attn_workspace_bytes", "focus_attn_fwd", "focus_attn_fwd_part",
     "focus_dense_workspace_bytes", "focus_dense_causal_fwd",
     "focus_attn_bwd_workspace_bytes", "focus_attn_bwd",
+    "focus_sinkhorn_workspace_bytes", "focus_sinkhorn", "focus_gated_attn_fwd",
 )
 
 _lib = None
@@ -77,8 +78,14 @@ def lib() -> ctypes.CDLL:
     L.focus_attn_bwd_workspace_bytes.restype = sz
     L.focus_attn_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, i32, i32, i64, i32, P, P, P, P,
                                  i32, i32, i64, f32, P, P, P, P, sz, P]
+    L.focus_sinkhorn_workspace_bytes.argtypes = [i32, i64]
+    L.focus_sinkhorn_workspace_bytes.restype = sz
+    L.focus_sinkhorn.argtypes = [P, P, i32, i64, i32, i32, i32, P, P, sz, P]
+    L.focus_gated_attn_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i32, i64, i32, P, i32, i64,
+                                       f32, f32, P, P, P]
     for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_attn_fwd",
-                 "focus_attn_fwd_part", "focus_dense_causal_fwd", "focus_attn_bwd"):
+                 "focus_attn_fwd_part", "focus_dense_causal_fwd", "focus_attn_bwd",
+                 "focus_sinkhorn", "focus_gated_attn_fwd"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -286,6 +293,41 @@ def focus_attn_bwd(q, k, v, out, lse, dout, gmask, offsets, tokens, slot_entry, 
         int(window), float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
         workspace.numel(), _stream(stream)))
     return dq, dk, dv
+
+
+def focus_sinkhorn(r, centroids, iters: int, assign=None, workspace=None, stream=None):
+    """r fp32 [H, n, 16], centroids fp32 [H, K, 16] -> assign fp32 [H, n, K]."""
+    import torch
+
+    H, n, dg = r.shape
+    K = centroids.shape[1]
+    if assign is None:
+        assign = torch.empty((H, n, K), dtype=torch.float32, device=r.device)
+    if workspace is None:
+        need = int(lib().focus_sinkhorn_workspace_bytes(H, n))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=r.device)
+    _check("focus_sinkhorn", lib().focus_sinkhorn(
+        _ptr(r), _ptr(centroids), H, n, dg, K, int(iters), _ptr(assign), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return assign
+
+
+def focus_gated_attn_fwd(q, k, v, assign, window: int, lam: float, scale: float, out=None,
+                         lse=None, stream=None):
+    """Training-mode gated dense causal attention -> (out bf16 [Hq, n, d], lse fp32 [Hq, n])."""
+    import torch
+
+    Hq, n, d = q.shape
+    Hkv = k.shape[0]
+    K = assign.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, n), dtype=torch.float32, device=q.device)
+    _check("focus_gated_attn_fwd", lib().focus_gated_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), Hq, Hkv, n, d, _ptr(assign), K,
+        int(window), float(lam), float(scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def focus_forward(q, k, v, r, centroids, topk: int, window: int, scale: float | None = None,

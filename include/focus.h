@@ -239,6 +239,50 @@ focus_status focus_attn_bwd(const void *q, const void *k, const void *v, const v
                             void *workspace, size_t workspace_bytes, focus_stream stream);
 
 /*
+ * Training-mode forward (Technical Summary, Core Architecture: soft
+ * assignment of tokens to groups and the learned gate
+ * s_ij = q_i.k_j * sigmoid(lambda a_ij) on distant pairs; Key Technical
+ * Innovation: Sinkhorn normalisation instead of softmax, a doubly-stochastic
+ * assignment with balanced group sizes; Significance: training evaluates
+ * all O(n^2) pairs because of the soft gate).
+ *
+ * focus_sinkhorn — soft assignment of every token of every routing head.
+ * Scores as focus_route; the assignment starts from exp(score - the token's
+ * max score) and each of `iters` iterations scales every group column to
+ * total n/K, then every token row to total 1 (rows end summing to 1,
+ * columns approach n/K).
+ *   r          fp32 [H, n, d_g]    routing vectors (d_g = 16)
+ *   centroids  fp32 [H, K, d_g]
+ *   assign     fp32 [H, n, K]      out
+ *   workspace  >= focus_sinkhorn_workspace_bytes(H, n) bytes (fp64 sums)
+ * Column sums are reduced in a fixed order: two calls give the same bits.
+ * Errors: INVALID_ARGUMENT for bad sizes or iters outside [1, 1000];
+ * UNSUPPORTED for d_g != 16 or K > 32; WORKSPACE if short.
+ */
+size_t focus_sinkhorn_workspace_bytes(int32_t H, int64_t n);
+focus_status focus_sinkhorn(const float *r, const float *centroids, int32_t H, int64_t n,
+                            int32_t d_g, int32_t K, int32_t iters, float *assign,
+                            void *workspace, size_t workspace_bytes, focus_stream stream);
+
+/*
+ * focus_gated_attn_fwd — gated dense causal attention: for every j <= i the
+ * logit is scale * q_i.k_j, times sigmoid(lambda a_ij) when i - j >= w, with
+ * a_ij = sum_g assign[i][g] assign[j][g] (the key/value head's assignment);
+ * exact softmax over all j <= i.
+ *   q          bf16 [Hq, n, d];  k, v  bf16 [Hkv, n, d]
+ *   assign     fp32 [Hkv, n, K]  from focus_sinkhorn (rounded to bf16 for
+ *                                the affinity product)
+ *   lambda     any finite value; window w >= 0; scale > 0
+ *   out        bf16 [Hq, n, d];  lse  fp32 [Hq, n] (natural log)
+ * Errors: INVALID_ARGUMENT as focus_attn_fwd (and a non-finite lambda);
+ * UNSUPPORTED for dt other than FOCUS_BF16, d not in {64, 128}, K > 32.
+ */
+focus_status focus_gated_attn_fwd(const void *q, const void *k, const void *v, focus_dtype dt,
+                                  int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
+                                  const float *assign, int32_t K, int64_t window, float lambda,
+                                  float scale, void *out, float *lse, focus_stream stream);
+
+/*
  * focus_dense_causal_fwd — plain causal attention (every j <= i) with the
  * same window kernel and layouts; the dense baseline that Focus is compared
  * against (thelatestinai.com Table 6 compares against full attention).

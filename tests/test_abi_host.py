@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(F.SYMBOLS)
@@ -172,6 +172,31 @@ def test_attn_bwd_rejects_bad_arguments(L):
     ws = F.focus_attn_bwd_workspace_bytes(F.FOCUS_BF16, 8, 2, 256, 128, 4, 2)
     # at least the fp32 partials of every row and entry
     assert ws >= 4 * 128 * (8 * 256 + 2 * 2 * 256 + 8 * 512 + 2 * 2 * 512)
+
+
+@no_gpu
+def test_training_forward_rejects_bad_arguments(L):
+    s = L.focus_sinkhorn
+    ok = [FAKE, FAKE, 2, 100, 16, 4, 3, FAKE, FAKE, 1 << 30, None]
+    bad = list(ok); bad[6] = 0
+    assert s(*bad) == 1                                # iters < 1
+    bad = list(ok); bad[4] = 8
+    assert s(*bad) == 2                                # d_g != 16
+    bad = list(ok); bad[5] = 33
+    assert s(*bad) == 2
+    bad = list(ok); bad[9] = 8
+    assert s(*bad) == 3                                # short workspace
+    g = L.focus_gated_attn_fwd
+    okg = [FAKE, FAKE, FAKE, F.FOCUS_BF16, 8, 2, 256, 128, FAKE, 4, 16, 1.5, 0.088, FAKE, FAKE,
+           None]
+    bad = list(okg); bad[3] = F.FOCUS_F32
+    assert g(*bad) == 2
+    bad = list(okg); bad[11] = float("nan")
+    assert g(*bad) == 1
+    bad = list(okg); bad[8] = None
+    assert g(*bad) == 1
+    bad = list(okg); bad[9] = 40
+    assert g(*bad) == 2
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
