@@ -353,6 +353,53 @@ def run_backward(workload: str, steps: int, warmup: int) -> int:
     return 0
 
 
+def run_train_forward(workload: str, steps: int, warmup: int, lam: float = 2.0,
+                      iters: int = 3) -> int:
+    """Training-mode forward at a workload: focus_sinkhorn + focus_gated_attn_fwd
+    (dense causal, every j <= i).  One JSON object; MFMA roofline of the
+    gated attention kernel on 4 d FLOPs per causal pair (QK^T and PV; the
+    affinity product adds 2 * 16 or 2 * 32 more per pair, not counted)."""
+    import torch
+
+    from centroid_gated_sparse_amd import focus as F
+    from centroid_gated_sparse_amd.workloads import (WORKLOADS, qkv_inputs, routing_inputs,
+                                                     seed_for)
+
+    F.lib()
+    wl = WORKLOADS[workload]
+    seed = seed_for(wl.name)
+    c, r, _ = routing_inputs(wl, seed)
+    rt = torch.from_numpy(r).cuda()
+    ct = torch.from_numpy(c).cuda()
+    q, k, v = qkv_inputs(wl, seed, "cuda")
+    A = torch.empty((wl.hkv, wl.n, wl.K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(int(F.lib().focus_sinkhorn_workspace_bytes(wl.hkv, wl.n)), 16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.hq, wl.n), dtype=torch.float32, device="cuda")
+    sk_ms = timed_ms(lambda: F.focus_sinkhorn(rt, ct, iters, A, ws), warmup, steps)
+    gws = torch.empty(max(int(F.lib().focus_gated_attn_workspace_bytes(wl.hkv, wl.n, wl.K)),
+                          16), dtype=torch.uint8, device="cuda")
+    at_ms = timed_ms(lambda: F.focus_gated_attn_fwd(q, k, v, A, wl.window, lam, wl.scale,
+                                                    out, lse, gws), warmup, steps)
+    pairs = wl.hq * wl.n * (wl.n + 1) // 2
+    achieved = 4.0 * wl.d * pairs / (at_ms / 1e3) / 1e12
+    res = {
+        "bench": "train_forward", "workload": wl.name, "n": wl.n, "q_heads": wl.hq,
+        "kv_heads": wl.hkv, "head_dim": wl.d, "centroids": wl.K, "window": wl.window,
+        "lambda": lam, "sinkhorn_iters": iters, "dtype": "bf16",
+        "sinkhorn_ms": sk_ms, "gated_attn_ms": at_ms,
+        "tokens_per_s": wl.n / ((sk_ms + at_ms) / 1e3),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "kernel": "gated_fwd_kernel (4 d FLOPs per causal pair)"},
+    }
+    log(f"train forward: sinkhorn {sk_ms:.3f} ms, gated attention {at_ms:.1f} ms, "
+        f"{achieved:.0f} TFLOP/s")
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,6 +412,9 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the Table 6 context sweep (Focus vs our dense kernel)")
+    ap.add_argument("--train-forward", action="store_true",
+                    help="only time the training-mode forward (Sinkhorn + gated dense "
+                         "attention) at --workload")
     ap.add_argument("--backward", action="store_true",
                     help="only time focus_attn_bwd at --workload")
     ap.add_argument("--project", action="store_true",
@@ -395,6 +445,8 @@ def main() -> int:
         return run_project(max(args.steps, 5), args.warmup)
     if args.backward:
         return run_backward(args.workload, args.steps, args.warmup)
+    if args.train_forward:
+        return run_train_forward(args.workload, args.steps, args.warmup)
 
     from centroid_gated_sparse_amd import focus as F
     from centroid_gated_sparse_amd.workloads import (WORKLOADS, qkv_inputs, routing_inputs,

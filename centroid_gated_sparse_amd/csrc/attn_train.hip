@@ -175,7 +175,7 @@ struct GatedParams {
     float c;        // scale * log2(e)
     float lam2;     // lambda * log2(e): sigmoid(lambda a) = 1 / (1 + 2^(-lam2 a))
     const __bf16 *q, *k, *v;
-    const float *assign;  // [hkv][n][K]
+    const bf16x8 *apack;  // [hkv][n][KA / 8]: the assignment in bf16, zero-padded
     __bf16 *out;
     float *lse;
 };
@@ -201,16 +201,19 @@ __device__ __forceinline__ bf16x8 glds16(const char *base, int slot)
     return *reinterpret_cast<const bf16x8 *>(base + slot * 16);
 }
 
-// bf16 copy of groups 8c .. 8c+7 of an assignment row (zero past K)
-__device__ __forceinline__ bf16x8 assign_chunk(const float *row, int K, int c)
+// The assignment rounded to bf16 and zero-padded to KA groups, one row of
+// KA / 8 16-byte chunks per token, so the attention kernel reads it with
+// unconditional vector loads.
+__global__ __launch_bounds__(256) void gated_pack_kernel(const float *__restrict__ assign,
+                                                         int64_t rows, int K, int KA,
+                                                         __bf16 *__restrict__ apack)
 {
-    bf16x8 r;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int g = 8 * c + u;
-        r[u] = (__bf16)(g < K ? row[g] : 0.f);
-    }
-    return r;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * KA)
+        return;
+    const int64_t t = idx / KA;
+    const int g = (int)(idx % KA);
+    apack[idx] = (__bf16)(g < K ? assign[t * K + g] : 0.f);
 }
 
 template <int D, int KA>  // KA: groups padded to 16 or 32
@@ -243,10 +246,10 @@ __global__ __launch_bounds__(kGThreads, 1) void gated_fwd_kernel(GatedParams p)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[ks] = qs[ks * 2 + h];
-        const float *arow = p.assign + ((int64_t)kvh * p.n + qpos) * p.K;
+        const bf16x8 *arow = p.apack + ((int64_t)kvh * p.n + qpos) * ACH;
 #pragma unroll
         for (int j = 0; j < KA / 16; ++j)
-            aq[j] = assign_chunk(arow, p.K, 2 * j + h);
+            aq[j] = arow[2 * j + h];
     }
     const int w = p.window;
 
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gated_fwd_kernel(GatedParams p)
             vr[i] = *reinterpret_cast<const uint4 *>(p.v + base + c * 8);
         }
         if (sc0 < ACH)
-            ar = assign_chunk(p.assign + ((int64_t)kvh * p.n + j) * p.K, p.K, sc0);
+            ar = p.apack[((int64_t)kvh * p.n + j) * ACH + sc0];
     };
     auto land = [&]() {
 #pragma unroll
@@ -319,19 +322,43 @@ __global__ __launch_bounds__(kGThreads, 1) void gated_fwd_kernel(GatedParams p)
         const bool all_far = __builtin_amdgcn_ballot_w64(!(fhi >= kGKeys - 1)) == 0;
         const bool none_far = __builtin_amdgcn_ballot_w64(fhi >= 0) == 0;
 
+        // S^T for the two 32-key blocks: block 1's K fragments are read
+        // between block 0's MFMAs, the assignment and V^T fragments between
+        // block 1's (fenced order, so LDS latency is not paid per MFMA).
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 kfr[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kfr[ks] = glds16(k_lds, koff[ks] + kb * 32 * KCH);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 s[kb][r] = 0.f;
+        bf16x8 kfr[KS], vf[DB][4], af[2][KA / 16];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks], qf[ks], s[kb], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks)
+            kfr[ks] = glds16(k_lds, koff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks], qf[ks], s[0], 0, 0, 0);
+            kfr[ks] = glds16(k_lds, koff[ks] + 32 * KCH);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < KA / 16; ++j)
+                af[kb][j] = glds16(a_lds, (kb * 32 + sigma(m)) * ACH + 2 * j + h);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks], qf[ks], s[1], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4 * DB / KS; ++q) {
+                const int f = ks * (4 * DB / KS) + q;
+                vf[f / 4][f % 4] = glds16(vt_lds, vtoff[f % 4] + (f / 4) * 32 * 8);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
             if (!none_far) {
                 // affinity a^T = A_k A_q^T for these 32 keys
                 f32x16 a;
@@ -340,9 +367,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gated_fwd_kernel(GatedParams p)
                     a[r] = 0.f;
 #pragma unroll
                 for (int j = 0; j < KA / 16; ++j)
-                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        glds16(a_lds, (kb * 32 + sigma(m)) * ACH + 2 * j + h), aq[j], a, 0, 0,
-                        0);
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb][j], aq[j], a, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float gate =
@@ -397,16 +422,11 @@ __global__ __launch_bounds__(kGThreads, 1) void gated_fwd_kernel(GatedParams p)
         lrun += swap_halves_sum(ls);
         // O^T += V^T P^T
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            bf16x8 vf[4];
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                vf[j] = glds16(vt_lds, vtoff[j] + db * 32 * 8);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j >> 1][j & 1], o[db], 0,
-                                                               0, 0);
-        }
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][j], pf[j >> 1][j & 1],
+                                                               o[db], 0, 0, 0);
     }
 
     if (qvalid) {
@@ -458,8 +478,13 @@ hipError_t launch_sinkhorn(const float *r, const float *centroids, int H, int64_
     return hipGetLastError();
 }
 
+size_t gated_workspace_bytes(int hkv, int64_t n, int K)
+{
+    return sizeof(__bf16) * (size_t)hkv * n * (K > 16 ? 32 : 16);
+}
+
 hipError_t launch_gated_attn(const AttnShape &sh, const void *q, const void *k, const void *v,
-                             const float *assign, float lambda, void *out, float *lse,
+                             const float *assign, float lambda, void *out, float *lse, void *ws,
                              hipStream_t s)
 {
     GatedParams p{};
@@ -475,10 +500,14 @@ hipError_t launch_gated_attn(const AttnShape &sh, const void *q, const void *k, 
     p.q = static_cast<const __bf16 *>(q);
     p.k = static_cast<const __bf16 *>(k);
     p.v = static_cast<const __bf16 *>(v);
-    p.assign = assign;
+    const bool wide = sh.K > 16;
+    const int KA = wide ? 32 : 16;
+    const int64_t rows = (int64_t)sh.hkv * sh.n;
+    hipLaunchKernelGGL(gated_pack_kernel, dim3((unsigned)((rows * KA + 255) / 256)), dim3(256),
+                       0, s, assign, rows, sh.K, KA, static_cast<__bf16 *>(ws));
+    p.apack = static_cast<const bf16x8 *>(ws);
     p.out = static_cast<__bf16 *>(out);
     p.lse = lse;
-    const bool wide = sh.K > 16;
     if (sh.d == 128)
         wide ? launch_gated_d<128, 32>(p, s) : launch_gated_d<128, 16>(p, s);
     else

@@ -64,8 +64,9 @@ hipError_t launch_dense(const AttnShape &sh, const void *q, const void *k, const
 size_t sinkhorn_workspace_bytes(int H, int64_t n);
 hipError_t launch_sinkhorn(const float *r, const float *centroids, int H, int64_t n, int K,
                            int iters, float *A, void *ws, hipStream_t s);
+size_t gated_workspace_bytes(int hkv, int64_t n, int K);
 hipError_t launch_gated_attn(const AttnShape &sh, const void *q, const void *k, const void *v,
-                             const float *assign, float lambda, void *out, float *lse,
+                             const float *assign, float lambda, void *out, float *lse, void *ws,
                              hipStream_t s);
 
 // ---- attn_bwd.hip

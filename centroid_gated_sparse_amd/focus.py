@@ -29,7 +29,8 @@ SYMBOLS = (
     "focus_attn_workspace_bytes", "focus_attn_fwd", "focus_attn_fwd_part",
     "focus_dense_workspace_bytes", "focus_dense_causal_fwd",
     "focus_attn_bwd_workspace_bytes", "focus_attn_bwd",
-    "focus_sinkhorn_workspace_bytes", "focus_sinkhorn", "focus_gated_attn_fwd",
+    "focus_sinkhorn_workspace_bytes", "focus_sinkhorn", "focus_gated_attn_workspace_bytes",
+    "focus_gated_attn_fwd",
 )
 
 _lib = None
@@ -81,8 +82,10 @@ def lib() -> ctypes.CDLL:
     L.focus_sinkhorn_workspace_bytes.argtypes = [i32, i64]
     L.focus_sinkhorn_workspace_bytes.restype = sz
     L.focus_sinkhorn.argtypes = [P, P, i32, i64, i32, i32, i32, P, P, sz, P]
+    L.focus_gated_attn_workspace_bytes.argtypes = [i32, i64, i32]
+    L.focus_gated_attn_workspace_bytes.restype = sz
     L.focus_gated_attn_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i32, i64, i32, P, i32, i64,
-                                       f32, f32, P, P, P]
+                                       f32, f32, P, P, P, sz, P]
     for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_attn_fwd",
                  "focus_attn_fwd_part", "focus_dense_causal_fwd", "focus_attn_bwd",
                  "focus_sinkhorn", "focus_gated_attn_fwd"):
@@ -313,7 +316,7 @@ def focus_sinkhorn(r, centroids, iters: int, assign=None, workspace=None, stream
 
 
 def focus_gated_attn_fwd(q, k, v, assign, window: int, lam: float, scale: float, out=None,
-                         lse=None, stream=None):
+                         lse=None, workspace=None, stream=None):
     """Training-mode gated dense causal attention -> (out bf16 [Hq, n, d], lse fp32 [Hq, n])."""
     import torch
 
@@ -324,9 +327,13 @@ def focus_gated_attn_fwd(q, k, v, assign, window: int, lam: float, scale: float,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((Hq, n), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = int(lib().focus_gated_attn_workspace_bytes(Hkv, n, K))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check("focus_gated_attn_fwd", lib().focus_gated_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), Hq, Hkv, n, d, _ptr(assign), K,
-        int(window), float(lam), float(scale), _ptr(out), _ptr(lse), _stream(stream)))
+        int(window), float(lam), float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
     return out, lse
 
 

@@ -274,13 +274,18 @@ focus_status focus_sinkhorn(const float *r, const float *centroids, int32_t H, i
  *                                the affinity product)
  *   lambda     any finite value; window w >= 0; scale > 0
  *   out        bf16 [Hq, n, d];  lse  fp32 [Hq, n] (natural log)
+ *   workspace  >= focus_gated_attn_workspace_bytes(Hkv, n, K) bytes (the
+ *              assignment rounded to bf16, padded to 16 or 32 groups)
  * Errors: INVALID_ARGUMENT as focus_attn_fwd (and a non-finite lambda);
- * UNSUPPORTED for dt other than FOCUS_BF16, d not in {64, 128}, K > 32.
+ * UNSUPPORTED for dt other than FOCUS_BF16, d not in {64, 128}, K > 32;
+ * WORKSPACE if short.
  */
+size_t focus_gated_attn_workspace_bytes(int32_t Hkv, int64_t n, int32_t K);
 focus_status focus_gated_attn_fwd(const void *q, const void *k, const void *v, focus_dtype dt,
                                   int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
                                   const float *assign, int32_t K, int64_t window, float lambda,
-                                  float scale, void *out, float *lse, focus_stream stream);
+                                  float scale, void *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, focus_stream stream);
 
 /*
  * focus_dense_causal_fwd — plain causal attention (every j <= i) with the

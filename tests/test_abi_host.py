@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(F.SYMBOLS)
@@ -188,7 +188,7 @@ def test_training_forward_rejects_bad_arguments(L):
     assert s(*bad) == 3                                # short workspace
     g = L.focus_gated_attn_fwd
     okg = [FAKE, FAKE, FAKE, F.FOCUS_BF16, 8, 2, 256, 128, FAKE, 4, 16, 1.5, 0.088, FAKE, FAKE,
-           None]
+           FAKE, 1 << 30, None]
     bad = list(okg); bad[3] = F.FOCUS_F32
     assert g(*bad) == 2
     bad = list(okg); bad[11] = float("nan")
@@ -197,6 +197,8 @@ def test_training_forward_rejects_bad_arguments(L):
     assert g(*bad) == 1
     bad = list(okg); bad[9] = 40
     assert g(*bad) == 2
+    bad = list(okg); bad[16] = 8
+    assert g(*bad) == 3                                # short workspace
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
