@@ -378,8 +378,9 @@ def run_train_forward(workload: str, steps: int, warmup: int, lam: float = 2.0,
     out = torch.empty_like(q)
     lse = torch.empty((wl.hq, wl.n), dtype=torch.float32, device="cuda")
     sk_ms = timed_ms(lambda: F.focus_sinkhorn(rt, ct, iters, A, ws), warmup, steps)
-    gws = torch.empty(max(int(F.lib().focus_gated_attn_workspace_bytes(wl.hkv, wl.n, wl.K)),
-                          16), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(max(int(F.lib().focus_gated_attn_workspace_bytes(wl.hkv, wl.n, wl.d,
+                                                                         wl.K)), 16),
+                      dtype=torch.uint8, device="cuda")
     at_ms = timed_ms(lambda: F.focus_gated_attn_fwd(q, k, v, A, wl.window, lam, wl.scale,
                                                     out, lse, gws), warmup, steps)
     pairs = wl.hq * wl.n * (wl.n + 1) // 2
@@ -392,7 +393,7 @@ def run_train_forward(workload: str, steps: int, warmup: int, lam: float = 2.0,
         "tokens_per_s": wl.n / ((sk_ms + at_ms) / 1e3),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "kernel": "gated_fwd_kernel (4 d FLOPs per causal pair)"},
+                     "kernel": "attn_kernel gated dense pass (4 d FLOPs per causal pair)"},
     }
     log(f"train forward: sinkhorn {sk_ms:.3f} ms, gated attention {at_ms:.1f} ms, "
         f"{achieved:.0f} TFLOP/s")

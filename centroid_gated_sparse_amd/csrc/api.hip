@@ -321,11 +321,13 @@ focus_status focus_sinkhorn(const float *r, const float *centroids, int32_t H, i
     return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_sinkhorn launch");
 }
 
-size_t focus_gated_attn_workspace_bytes(int32_t Hkv, int64_t n, int32_t K)
+size_t focus_gated_attn_workspace_bytes(int32_t Hkv, int64_t n, int32_t d, int32_t K)
 {
-    if (Hkv < 1 || n < 1 || K < 1 || K > kMaxGroups)
+    if (Hkv < 1 || n < 1 || n > INT32_MAX / 2 || (d != 64 && d != 128) || K < 1 ||
+        K > kMaxGroups)
         return 0;
-    return gated_workspace_bytes(Hkv, n, K);
+    AttnShape sh{FOCUS_BF16, Hkv, Hkv, d, K, 1, n, n, 1.f};
+    return gated_dense_workspace_bytes(sh);
 }
 
 focus_status focus_gated_attn_fwd(const void *q, const void *k, const void *v, focus_dtype dt,
@@ -350,12 +352,12 @@ focus_status focus_gated_attn_fwd(const void *q, const void *k, const void *v, f
     FOCUS_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
     FOCUS_REQUIRE(lambda == lambda && lambda > -1e30f && lambda < 1e30f,
                   "lambda must be finite");
-    const size_t need = gated_workspace_bytes(Hkv, n, K);
+    AttnShape sh{dt, Hq, Hkv, d, K, 1, n, window, scale};
+    const size_t need = gated_dense_workspace_bytes(sh);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return short_workspace(workspace_bytes, need);
-    AttnShape sh{dt, Hq, Hkv, d, K, 1, n, window, scale};
-    hipError_t e = launch_gated_attn(sh, q, k, v, assign, lambda, out, lse, workspace,
-                                     static_cast<hipStream_t>(stream));
+    hipError_t e = launch_gated_dense(sh, q, k, v, assign, lambda, out, lse, workspace,
+                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_gated_attn_fwd launch");
 }
 

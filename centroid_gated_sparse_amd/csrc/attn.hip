@@ -427,9 +427,19 @@ struct Acc {
 // ---------------------------------------------------------------------------
 // the attention kernel: GROUP selects the gathered within-group pass
 
-template <int D, bool BF16, bool GROUP>
+// GA != 0 (bf16 dense window pass only): the training-mode gate of the far
+// pairs (Technical Summary, Gated Attention: s_ij = q_i.k_j *
+// sigmoid(lambda a_ij)).  Each stage also holds the tile's keys' assignment
+// rows (bf16, GA = 16 or 32 groups wide, LDS-DMA'd by wavefront 0); the
+// affinity tile a^T = A_k A_q^T is GA / 16 more MFMAs per 32 keys, and far
+// scores are multiplied by sigmoid(lambda a) before the softmax.
+template <int D, bool BF16, bool GROUP, int GA>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
 {
+    // GA: 0, or the gated pass's padded assignment width (16 or 32 groups)
+    constexpr bool GATED = GA != 0;
+    constexpr int GCH = GATED ? GA / 8 : 1;  // 16-byte chunks per assignment row
+    static_assert(!GATED || (BF16 && !GROUP), "the gate is a bf16 dense-pass feature");
     using TL = Tile<D, BF16>;
     using T = typename TL::T;
     constexpr int DB = TL::DB;
@@ -456,6 +466,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     __shared__ __attribute__((aligned(16))) int key_lds1[KEYS];
     __shared__ __attribute__((aligned(16))) int key_lds2[KEYS];
     __shared__ __attribute__((aligned(16))) int key_lds3[KEYS];
+    constexpr int AB = GATED ? kKeyTile * GA * 2 : 16;
+    __shared__ __attribute__((aligned(16))) char a_lds0[AB];
+    __shared__ __attribute__((aligned(16))) char a_lds1[AB];
+    __shared__ __attribute__((aligned(16))) char a_lds2[GATED ? AB : 16];
+    __shared__ __attribute__((aligned(16))) char a_lds3[GATED ? AB : 16];
     // Stage<I> names the arrays of stage I at compile time.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -465,16 +480,17 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         char *k;
         char *v;
         int *key;
+        char *a;
     };
     auto stage = [&](auto I) -> Stage {
         if constexpr (decltype(I)::value == 0)
-            return Stage{k_lds0, v_lds0, key_lds0};
+            return Stage{k_lds0, v_lds0, key_lds0, a_lds0};
         else if constexpr (decltype(I)::value == 1)
-            return Stage{k_lds1, v_lds1, key_lds1};
+            return Stage{k_lds1, v_lds1, key_lds1, a_lds1};
         else if constexpr (decltype(I)::value == 2)
-            return Stage{k_lds2, v_lds2, key_lds2};
+            return Stage{k_lds2, v_lds2, key_lds2, a_lds2};
         else
-            return Stage{k_lds3, v_lds3, key_lds3};
+            return Stage{k_lds3, v_lds3, key_lds3, a_lds3};
     };
     __shared__ int sub_start[kMaxGroups + 1];
     __shared__ int sub_count[kMaxGroups + 1];
@@ -539,6 +555,16 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
 
     typename TL::QFrag qf;
     TL::load_q(qf, static_cast<const T *>(p.q), ((int64_t)hq * p.n + qpos) * D, h);
+    // gated pass: this lane's query's assignment as the B operand of the
+    // affinity product (groups 16j + 8h .. 16j + 8h + 7 for k-step j)
+    bf16x8 aq[GATED ? GA / 16 : 1];
+    if constexpr (GATED) {
+        const bf16x8 *arow =
+            static_cast<const bf16x8 *>(p.apack) + ((int64_t)kvh * p.krows + qpos) * GCH;
+#pragma unroll
+        for (int j = 0; j < GA / 16; ++j)
+            aq[j] = arow[2 * j + h];
+    }
 
     Acc<TL> acc;
     acc.init();
@@ -669,6 +695,36 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         const int *kpos = stage(I).key;
         const uint32_t *kgm = reinterpret_cast<const uint32_t *>(kpos + kKeyTile);
         TL::qk(s, qf, stage(I).k, lo);
+        if constexpr (GATED) {
+            // far keys (position <= qpos - gate_w) take the gate; in the
+            // dense pass key index i of the tile is position kpos[0] + i
+            const int fhi = qpos - p.gate_w - kpos[0];
+            if (__builtin_amdgcn_ballot_w64(fhi >= 0) != 0) {
+                const bool all_far = __builtin_amdgcn_ballot_w64(!(fhi >= kKeyTile - 1)) == 0;
+                const char *al = stage(I).a;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int row = kb * 32 + sigma(m);
+                    f32x16 a;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        a[r] = 0.f;
+#pragma unroll
+                    for (int j = 0; j < GA / 16; ++j)
+                        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            *reinterpret_cast<const bf16x8 *>(
+                                al + (row * GCH + ((2 * j + h) ^ ((row >> 4) & 1))) * 16),
+                            aq[j], a, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float gate = __builtin_amdgcn_rcpf(
+                            1.f + __builtin_amdgcn_exp2f(-p.lam2 * a[r]));
+                        const int kk = kb * 32 + 16 * h + r;
+                        s[kb][r] *= (all_far || kk <= fhi) ? gate : 1.f;
+                    }
+                }
+            }
+        }
             // does any pair of this tile x wavefront need a mask?
         bool masked;
         if (GROUP) {
@@ -794,6 +850,12 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // LDS-DMA loads each wavefront issues per tile (waited on by count)
         constexpr int DMA_KV = 2 * TL::LOADS;
         const bool key_wave = GROUP && __builtin_amdgcn_readfirstlane(wave) == 0;
+        // gated pass: wavefront 0 also loads the keys' assignment rows
+        // (GA * 128 bytes per tile, one LDS-DMA load per KB).  LDS slot P
+        // holds chunk (P % GCH) ^ ((row >> 4) & 1) of row P / GCH, so the MFMA
+        // reads of rows sigma(m) fall in distinct banks.
+        constexpr int DMA_A = GATED ? kKeyTile * GA * 2 / 1024 : 0;
+        const bool a_wave = GATED && __builtin_amdgcn_readfirstlane(wave) == 0;
         auto issue = [&](auto I) {
             int nv, no;
             const int64_t origin = tile_origin(nv, no);
@@ -806,6 +868,20 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 }
             } else if (threadIdx.x < kKeyTile) {
                 kp[threadIdx.x] = (int)(origin + threadIdx.x);
+            }
+            if constexpr (GATED) {
+                if (a_wave) {
+                    const char *abase = static_cast<const char *>(p.apack) +
+                                        ((int64_t)kvh * p.krows + origin) * GA * 2;
+#pragma unroll
+                    for (int i = 0; i < DMA_A; ++i) {
+                        const int P = i * kWave + lane;
+                        const int row = P / GCH;
+                        const int c = (P % GCH) ^ ((row >> 4) & 1);
+                        dma16(abase, (uint32_t)(row * GCH + c) * 16u,
+                              lds_address(stage(I).a) + i * 1024);
+                    }
+                }
             }
             if (threadIdx.x == 0) {
                 kp[2 * kKeyTile] = nv;
@@ -823,12 +899,15 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 __builtin_amdgcn_s_waitcnt(0x70);
             else if (key_wave)
                 __builtin_amdgcn_s_waitcnt(0x70 | (DMA_KV + 2));
+            else if (a_wave)
+                __builtin_amdgcn_s_waitcnt(0x70 | (DMA_KV + DMA_A));
             else
                 __builtin_amdgcn_s_waitcnt(0x70 | DMA_KV);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         };
         static_assert(!BF16 || TL::LOADS == 1 || TL::LOADS == 2, "vmcnt counts assume 1-2 loads");
+        static_assert(DMA_KV + DMA_A <= 15, "vmcnt immediate holds 4 bits here");
 
         // prologue: tiles 0 and 1 (tile 0's iterator position is current)
         if (T > 0)
@@ -1159,11 +1238,11 @@ Layout make_layout(const AttnShape &sh)
     return L;
 }
 
-template <int D, bool BF16, bool GROUP>
+template <int D, bool BF16, bool GROUP, int GA = 0>
 hipError_t launch_attn_kernel(const Params &p, hipStream_t s)
 {
     const int grid = (p.total_blocks + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((attn_kernel<D, BF16, GROUP>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, BF16, GROUP, GA>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1331,6 +1410,79 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
         e = dispatch_attn<false>(sh.d, bf16, wp, s);
     }
     return e;
+}
+
+namespace {
+// The assignment rounded to bf16, padded to ga groups (16 or 32) and to
+// n_pad zero rows per head: [hkv][n_pad][ga].
+__global__ __launch_bounds__(256) void gate_pack_kernel(const float *__restrict__ assign,
+                                                        int64_t n, int64_t n_pad, int K, int ga,
+                                                        int64_t total, __bf16 *__restrict__ apack)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total)
+        return;
+    const int g = (int)(idx % ga);
+    const int64_t ht = idx / ga;
+    const int64_t h = ht / n_pad, t = ht % n_pad;
+    apack[idx] = (__bf16)((t < n && g < K) ? assign[(h * n + t) * K + g] : 0.f);
+}
+}  // namespace
+
+size_t gated_dense_workspace_bytes(const AttnShape &sh)
+{
+    const int64_t n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
+    return dense_workspace_bytes(sh) +
+           align_up((size_t)sh.hkv * n_pad * kGateGroups * 2, 256);
+}
+
+hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k, const void *v,
+                              const float *assign, float lambda, void *out, float *lse, void *ws,
+                              hipStream_t s)
+{
+    AttnShape d = sh;
+    d.window = sh.n;
+    d.K = 1;
+    d.topk = 1;
+    Layout L = make_layout(d);
+    const int64_t n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
+    const size_t half = align_up((size_t)sh.hkv * sh.d * n_pad * 2, 256);
+    __bf16 *vt = static_cast<__bf16 *>(ws);
+    __bf16 *kp = reinterpret_cast<__bf16 *>(static_cast<char *>(ws) + half);
+    __bf16 *apack = reinterpret_cast<__bf16 *>(static_cast<char *>(ws) + 2 * half);
+    hipError_t e = launch_transpose(sh.d, static_cast<const __bf16 *>(v), nullptr, sh.n, sh.n,
+                                    n_pad, sh.hkv, vt, s);
+    if (e == hipSuccess)
+        e = launch_gather(sh.d, static_cast<const __bf16 *>(k), (const int32_t *)nullptr, sh.n,
+                          sh.n, n_pad, sh.hkv, kp, s);
+    if (e != hipSuccess)
+        return e;
+    const int ga = sh.K > 16 ? 32 : 16;
+    const int64_t total = (int64_t)sh.hkv * n_pad * ga;
+    hipLaunchKernelGGL(gate_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       assign, sh.n, n_pad, sh.K, ga, total, apack);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    Params p = base_params(d, L);
+    p.q = q;
+    p.kmat = kp;
+    p.vmat = vt;
+    p.krows = n_pad;
+    p.vcols = n_pad;
+    p.merge = 0;
+    p.out = out;
+    p.lse = lse;
+    p.row_tiles = (int)((sh.n + (kRowsPerBlock / L.hpb) - 1) / (kRowsPerBlock / L.hpb));
+    p.total_blocks = sh.hkv * L.nhg * p.row_tiles;
+    p.apack = apack;
+    p.gate_w = (int)std::min<int64_t>(sh.window, sh.n);
+    p.lam2 = lambda * kLog2e;
+    if (ga == 16)
+        return sh.d == 64 ? launch_attn_kernel<64, true, false, 16>(p, s)
+                          : launch_attn_kernel<128, true, false, 16>(p, s);
+    return sh.d == 64 ? launch_attn_kernel<64, true, false, 32>(p, s)
+                      : launch_attn_kernel<128, true, false, 32>(p, s);
 }
 
 hipError_t launch_dense(const AttnShape &sh, const void *q, const void *k, const void *v,

@@ -45,7 +45,15 @@ struct Params {
     float *lse;
     int row_tiles;
     int total_blocks;
+    // gated dense pass (training mode): bf16 assignment rows padded to 16
+    // or 32 groups, [hkv][krows][16 or 32]; far pairs (i - j >= gate_w)
+    // multiply their score by sigmoid(lambda a_ij)
+    const void *apack;
+    int gate_w;
+    float lam2;  // lambda * log2(e)
 };
+
+constexpr int kGateGroups = 32;  // widest assignment row of the gated pass
 
 // ---------------------------------------------------------------------------
 // small helpers

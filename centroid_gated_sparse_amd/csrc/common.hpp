@@ -59,15 +59,15 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
                        int parts, hipStream_t s);
 hipError_t launch_dense(const AttnShape &sh, const void *q, const void *k, const void *v,
                         void *out, float *lse, void *ws, hipStream_t s);
+size_t gated_dense_workspace_bytes(const AttnShape &sh);
+hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k, const void *v,
+                              const float *assign, float lambda, void *out, float *lse, void *ws,
+                              hipStream_t s);
 
 // ---- attn_train.hip
 size_t sinkhorn_workspace_bytes(int H, int64_t n);
 hipError_t launch_sinkhorn(const float *r, const float *centroids, int H, int64_t n, int K,
                            int iters, float *A, void *ws, hipStream_t s);
-size_t gated_workspace_bytes(int hkv, int64_t n, int K);
-hipError_t launch_gated_attn(const AttnShape &sh, const void *q, const void *k, const void *v,
-                             const float *assign, float lambda, void *out, float *lse, void *ws,
-                             hipStream_t s);
 
 // ---- attn_bwd.hip
 size_t attn_bwd_workspace_bytes(const AttnShape &sh);

@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.focus_sinkhorn_workspace_bytes.argtypes = [i32, i64]
     L.focus_sinkhorn_workspace_bytes.restype = sz
     L.focus_sinkhorn.argtypes = [P, P, i32, i64, i32, i32, i32, P, P, sz, P]
-    L.focus_gated_attn_workspace_bytes.argtypes = [i32, i64, i32]
+    L.focus_gated_attn_workspace_bytes.argtypes = [i32, i64, i32, i32]
     L.focus_gated_attn_workspace_bytes.restype = sz
     L.focus_gated_attn_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i32, i64, i32, P, i32, i64,
                                        f32, f32, P, P, P, sz, P]
@@ -328,7 +328,7 @@ def focus_gated_attn_fwd(q, k, v, assign, window: int, lam: float, scale: float,
     if lse is None:
         lse = torch.empty((Hq, n), dtype=torch.float32, device=q.device)
     if workspace is None:
-        need = int(lib().focus_gated_attn_workspace_bytes(Hkv, n, K))
+        need = int(lib().focus_gated_attn_workspace_bytes(Hkv, n, d, K))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check("focus_gated_attn_fwd", lib().focus_gated_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), Hq, Hkv, n, d, _ptr(assign), K,

@@ -271,16 +271,17 @@ focus_status focus_sinkhorn(const float *r, const float *centroids, int32_t H, i
  * exact softmax over all j <= i.
  *   q          bf16 [Hq, n, d];  k, v  bf16 [Hkv, n, d]
  *   assign     fp32 [Hkv, n, K]  from focus_sinkhorn (rounded to bf16 for
- *                                the affinity product)
+ *                                the affinity product, a bf16 MFMA)
  *   lambda     any finite value; window w >= 0; scale > 0
  *   out        bf16 [Hq, n, d];  lse  fp32 [Hq, n] (natural log)
- *   workspace  >= focus_gated_attn_workspace_bytes(Hkv, n, K) bytes (the
- *              assignment rounded to bf16, padded to 16 or 32 groups)
+ *   workspace  >= focus_gated_attn_workspace_bytes(Hkv, n, d, K) bytes:
+ *              padded copies of K and V^T and the assignment rounded to
+ *              bf16, padded to 32 groups
  * Errors: INVALID_ARGUMENT as focus_attn_fwd (and a non-finite lambda);
  * UNSUPPORTED for dt other than FOCUS_BF16, d not in {64, 128}, K > 32;
  * WORKSPACE if short.
  */
-size_t focus_gated_attn_workspace_bytes(int32_t Hkv, int64_t n, int32_t K);
+size_t focus_gated_attn_workspace_bytes(int32_t Hkv, int64_t n, int32_t d, int32_t K);
 focus_status focus_gated_attn_fwd(const void *q, const void *k, const void *v, focus_dtype dt,
                                   int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
                                   const float *assign, int32_t K, int64_t window, float lambda,
