@@ -350,3 +350,47 @@ def focus_forward(q, k, v, r, centroids, topk: int, window: int, scale: float | 
                               stream=stream)
     return dict(out=out, lse=lse, groups=groups, gmask=gmask, offsets=offsets,
                 tokens=tokens, slot_entry=slot_entry)
+
+
+# ----------------------------------------------------------------------------
+# autograd: q, k, v get the gradients of focus_attn_fwd (the routing is a
+# hard choice and gets none)
+
+def _autograd_function():
+    import torch
+
+    class FocusAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, r, centroids, topk, window, scale):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            res = focus_forward(q, k, v, r, centroids, topk, window, scale)
+            ctx.save_for_backward(q, k, v, res["out"], res["lse"], res["gmask"],
+                                  res["offsets"], res["tokens"], res["slot_entry"])
+            ctx.K = centroids.shape[1]
+            ctx.window = window
+            ctx.scale = scale
+            return res["out"]
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse, gmask, offsets, tokens, slot_entry = ctx.saved_tensors
+            dq, dk, dv = focus_attn_bwd(q, k, v, out, lse, dout.contiguous(), gmask, offsets,
+                                        tokens, slot_entry, ctx.K, ctx.window, ctx.scale)
+            return dq, dk, dv, None, None, None, None, None
+
+    return FocusAttention
+
+
+_FocusAttention = None
+
+
+def focus_attention(q, k, v, r, centroids, topk: int, window: int, scale: float | None = None):
+    """Differentiable Focus attention (bf16): out = focus_attn_fwd(...), and
+    backward through focus_attn_bwd.  q [Hq, n, d], k/v [Hkv, n, d],
+    r fp32 [Hkv, n, 16], centroids fp32 [Hkv, K, 16]."""
+    global _FocusAttention
+    if _FocusAttention is None:
+        _FocusAttention = _autograd_function()
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _FocusAttention.apply(q, k, v, r, centroids, int(topk), int(window), float(scale))

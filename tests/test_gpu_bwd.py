@@ -148,3 +148,22 @@ def test_backward_full_size(name):
         log(f"[{name}] head {hk}: |sum dv - sum dO| / sum|dv| = {rel_v:.2e}, "
             f"|sum dk| / sum|dk| = {rel_k:.2e}")
         assert rel_v <= 1e-2 and rel_k <= 1e-2
+
+
+def test_autograd_function_matches_oracle():
+    """focus_attention as a torch.autograd.Function: .grad of q, k, v after
+    (out * dO).sum().backward() equals the oracle's gradients."""
+    wl = CASES[0]
+    seed = 3200
+    c, r, _ = routing_inputs(wl, seed)
+    q, k, v = qkv_inputs(wl, seed, DEV)
+    dout = dout_input(wl, seed, DEV)
+    qg, kg, vg = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out = F.focus_attention(qg, kg, vg, torch.from_numpy(r).to(DEV),
+                            torch.from_numpy(c).to(DEV), wl.topk, wl.window, wl.scale)
+    (out.float() * dout.float()).sum().backward()
+    torch.cuda.synchronize()
+    g_ref, _ = oracle.route(r, c, wl.topk)
+    ref = oracle.attn_bwd(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v),
+                          to_bf16_bits(dout), g_ref, wl.K, wl.window, wl.scale)
+    check_grads("autograd", (qg.grad, kg.grad, vg.grad), ref)
