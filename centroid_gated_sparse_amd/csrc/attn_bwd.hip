@@ -29,11 +29,16 @@
 // entry for the groups); a merge kernel adds a row's window part and its k
 // group parts and rounds to bf16.
 //
-// Operands on v_mfma_f32_32x32x16_bf16 need both fragments contiguous along
-// the reduction index.  Tiles are staged through LDS by plain loads; the
-// transposed operands (K^T in the dq pass, Q^T and dO^T in the dk/dv pass)
-// are written transposed into LDS at staging time, so no transposed copy is
-// kept in HBM.  The group passes read rows through the bucket's token list.
+// Data movement.  The group passes read copies of their rows gathered into
+// bucket (entry) order by a prepare kernel, so that every staged tile, in
+// both partitions, is a run of consecutive rows.  Tiles go straight from HBM
+// into a three-stage LDS ring by LDS-DMA (two tiles in flight while one is
+// computed; one barrier per tile), row-major with 16-byte chunks XOR-swizzled.
+// v_mfma_f32_32x32x16_bf16 needs both operands contiguous along the
+// reduction index: the row operands (K and V in the dq pass, Q and dO in the
+// dk/dv pass) are read as 16-byte fragments, the transposed ones (K^T, and
+// Q^T and dO^T) with the LDS transpose read ds_read_b64_tr_b16 from the same
+// row-major tile.
 #include <algorithm>
 
 #include "attn_common.hpp"
@@ -46,20 +51,22 @@ constexpr int kBwdThreads = 256;  // 4 wavefronts
 constexpr int kBwdRows = 128;     // query rows (dq pass) or keys (dk/dv pass) per block
 constexpr int kQKeys = 64;        // dq pass: keys per staged tile
 constexpr int kKQueries = 32;     // dk/dv pass: queries per staged tile
-constexpr int kNoPos = 0x7fffffff;
+constexpr int kStages = 3;        // LDS ring depth
 
 struct BwdParams {
     int hq, hkv, ratio, K, topk, window;
     int64_t n, E;
     float c;      // scale * log2(e)
     float scale;
+    // rows in position order (window pass) or gathered in entry order (group
+    // pass): [heads][rows][D] with rows = n or E
     const __bf16 *q, *k, *v, *dout;
-    const float *lse;
-    const float *drow;  // D_i = dO_i . O_i, [hq][n]
+    const float *lse;   // forward log-sum-exp, [hq][rows]
+    const float *drow;  // D_i = dO_i . O_i, [hq][rows]
     // group pass
+    const uint32_t *egm;     // group bits per entry [hkv][E]
     const int32_t *tokens;   // [hkv][E]
     const int32_t *offsets;  // [hkv][K(K+1)+1]
-    const uint32_t *gmask;   // [hkv][n]
     const int4 *tiles;       // [hkv][max_tiles]: (sub-bucket, first entry, rows)
     const int32_t *ntiles;
     int max_tiles;
@@ -69,34 +76,48 @@ struct BwdParams {
     float *dk, *dv; // [hkv][rows][D]
 };
 
-// XOR swizzles of 16-byte LDS slots.  Row-major tiles ([rows][D], read as
-// A fragments row sigma(m), chunk 2ks+h) and transposed tiles ([D][cols],
-// read row d, chunk c) are laid out so that the 8 lanes served together read
-// distinct banks.
+// XOR swizzle of the 16-byte chunks of a row-major [rows][D] tile (chunk c of
+// row r sits in slot c ^ rswz(r)).  With 64 banks of 4 bytes it keeps three
+// access patterns free of bank conflicts: 16-byte fragment reads of rows
+// sigma(m) (16 lanes, rows differing in bits 0, 1, 2 and 4), transpose reads
+// (32 lanes, 4 consecutive rows times 64 bytes) and the row writes of the
+// DMA (16 lanes, one row).
 template <int D>
 __device__ __forceinline__ int rswz(int row)
 {
-    if (D == 128)
-        return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
-    return ((row & 3) | (((row >> 4) & 1) << 2)) ^ ((row >> 2) & 1);
+    if (D == 128)  // row bits 0,1 -> chunk bits 2,3; bit 2 -> 0; bit 4 -> 1
+        return ((row & 3) << 2) | ((row >> 2) & 1) | (((row >> 4) & 1) << 1);
+    // 128-byte rows: bit 0 already picks the bank half; bit 1 -> 2, 2 -> 0, 4 -> 1
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 4) & 1) << 1);
 }
 template <int D>
-__device__ __forceinline__ int rslot(int row, int c)  // row-major [rows][D]
+__device__ __forceinline__ uint32_t rbyte(int row, int c)  // byte offset of chunk c of row
 {
-    return row * (D / 8) + (c ^ rswz<D>(row));
-}
-// transposed tile with CH 16-byte chunks per row
-template <int CH>
-__device__ __forceinline__ int tslot(int d, int c)
-{
-    if (CH == 8)
-        return d * 8 + (c ^ ((d & 7) ^ ((d >> 3) & 1)));
-    return d * 4 + (c ^ ((d >> 2) & 3));  // CH == 4
+    return (uint32_t)((row * (D / 8) + (c ^ rswz<D>(row))) * 16);
 }
 
-__device__ __forceinline__ bf16x8 lds16(const char *base, int slot)
+__device__ __forceinline__ bf16x8 lds16(const char *base, uint32_t off)
 {
-    return *reinterpret_cast<const bf16x8 *>(base + slot * 16);
+    return *reinterpret_cast<const bf16x8 *>(base + off);
+}
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte pieces addressed by lanes 4v + i / 4 (v = 0..3).  With
+// lane 4a + b addressing row r0 + a, columns c0 + 4b .. c0 + 4b + 3 of a
+// row-major tile, lane i thus holds rows r0 .. r0 + 3 of column c0 + i.
+typedef short s16x4 __attribute__((vector_size(8)));
+__device__ __forceinline__ uint2 lds_tr(const char *p)
+{
+    const s16x4 r =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+    return __builtin_bit_cast(uint2, r);
+}
+// A fragment of a transposed operand: lane (m, h) gets column m of rows
+// r0 + 8h .. r0 + 8h + 7 (the two halves of 4 rows from two transpose reads)
+__device__ __forceinline__ bf16x8 tr_frag(const char *tile, uint32_t o0, uint32_t o1)
+{
+    const uint2 a = lds_tr(tile + o0), b = lds_tr(tile + o1);
+    return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
 }
 
 // fp32 accumulator registers 8t .. 8t+7 as one bf16 B fragment
@@ -109,19 +130,45 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 &x, int t)
     return r;
 }
 
-// Stores one chunk (8 values of row `row`, columns 8c..8c+7) transposed into
-// a [D][cols] tile with CH chunks per row.
-template <int CH>
-__device__ __forceinline__ void store_transposed(char *tl, const uint4 &v, int row, int c)
-{
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    const int kc = row >> 3, ke = row & 7;
+// LDS-DMA of a [ROWS][D] tile of consecutive rows: load i of wavefront w
+// fills the 1024 LDS bytes (w L + i) * 1024 ..., i.e. rows (w L + i) R ..
+// (R rows per load), lane l slot l % KCH of its row, so it fetches the chunk
+// the swizzle keeps there.  Rows at or past `valid` re-read row valid - 1 (the
+// kernels mask them), so no load leaves the tile's rows.
+template <int D, int ROWS>
+struct TileDma {
+    static constexpr int RB = D * 2;
+    static constexpr int KCH = D / 8;
+    static constexpr int R = 1024 / RB;
+    static constexpr int LOADS = ROWS / R / (kBwdThreads / kWave);
+    static_assert(LOADS >= 1 && LOADS * R * (kBwdThreads / kWave) == ROWS, "tile shape");
+    int row[LOADS];
+    uint32_t cofs[LOADS];
+    __device__ void init(int wave, int lane)
+    {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int d = 8 * c + u;
-        const uint16_t bits = (uint16_t)((u & 1) ? (w[u >> 1] >> 16) : (w[u >> 1] & 0xffffu));
-        *reinterpret_cast<uint16_t *>(tl + tslot<CH>(d, kc) * 16 + ke * 2) = bits;
+        for (int i = 0; i < LOADS; ++i) {
+            row[i] = (wave * LOADS + i) * R + lane / KCH;
+            cofs[i] = (uint32_t)(((lane % KCH) ^ rswz<D>(row[i])) * 16);
+        }
     }
+    __device__ void issue(const void *base, int valid, uint32_t lds, int wave) const
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            dma16(base, (uint32_t)(std::min(row[i], valid - 1) * RB) + cofs[i],
+                  lds + (uint32_t)(wave * LOADS + i) * 1024u);
+    }
+};
+
+// "s_waitcnt vmcnt(n) lgkmcnt(0)" for a wave-uniform n known to be a or b
+template <int A, int B>
+__device__ __forceinline__ void wait_vm(bool first)
+{
+    if (first)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(A));
+    else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(B));
 }
 
 // ---------------------------------------------------------------------------
@@ -132,17 +179,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
 {
     constexpr int KS = D / 16;   // k-steps over d
     constexpr int DB = D / 32;   // 32-row blocks of d
-    constexpr int KCH = D / 8;   // 16-byte chunks per row
-    constexpr int CHUNKS = kQKeys * KCH / kBwdThreads;  // per thread per matrix
-    __shared__ __attribute__((aligned(16))) char k_lds[kQKeys * D * 2];
-    __shared__ __attribute__((aligned(16))) char v_lds[kQKeys * D * 2];
-    __shared__ __attribute__((aligned(16))) char kt_lds[D * kQKeys * 2];
-    __shared__ int kpos_lds[kQKeys];
-    __shared__ uint32_t kgm_lds[kQKeys];
+    constexpr int RB = D * 2;    // bytes per row
+    using Dma = TileDma<D, kQKeys>;
+    struct Stage {
+        char k[kQKeys * RB];
+        char v[kQKeys * RB];
+        int pos[kWave];       // key positions
+        uint32_t gm[kWave];   // key group bits (group pass)
+        int desc[4];          // origin, valid keys, owner flag
+    };
+    __shared__ __attribute__((aligned(16))) Stage stg[kStages];
     __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int m = lane % 32;
     const int h = lane / 32;
 
@@ -159,27 +209,28 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
         hq = blockIdx.x / p.row_tiles;
         kvh = hq / p.ratio;
     }
-    int g = 0, mq = 0, e_start = 0, tile_rows;
-    int64_t p_start = 0;
+    int g = 0, mq = 0, tile_rows;
+    int64_t row0;  // first query row (entry or position)
     if (GROUP) {
         const int4 t = p.tiles[(int64_t)kvh * p.max_tiles + slot];
         g = t.x / (p.K + 1);
         mq = t.x % (p.K + 1);
-        e_start = t.y;
+        row0 = t.y;
         tile_rows = t.z;
     } else {
-        p_start = (int64_t)slot * kBwdRows;
-        tile_rows = (int)std::min<int64_t>(kBwdRows, p.n - p_start);
+        row0 = (int64_t)slot * kBwdRows;
+        tile_rows = (int)std::min<int64_t>(kBwdRows, p.n - row0);
     }
+    const int64_t rows = GROUP ? p.E : p.n;
     const int32_t *tok = GROUP ? p.tokens + (int64_t)kvh * p.E : nullptr;
-    const uint32_t *gmh = p.gmask + (int64_t)kvh * p.n;
+    const uint32_t *egm = GROUP ? p.egm + (int64_t)kvh * p.E : nullptr;
 
     // ---- this lane's query (column m of the wavefront's 32 rows)
     const int qr = wave * 32 + m;
     const bool qvalid = qr < tile_rows;
     const int qrc = qvalid ? qr : 0;
-    const int qpos = GROUP ? tok[e_start + qrc] : (int)(p_start + qrc);
-    const int64_t qrow = (int64_t)hq * p.n + qpos;
+    const int qpos = GROUP ? tok[row0 + qrc] : (int)(row0 + qrc);
+    const int64_t qrow = (int64_t)hq * rows + row0 + qrc;
     bf16x8 qf[KS], dof[KS];
     {
         const bf16x8 *qs = reinterpret_cast<const bf16x8 *>(p.q + qrow * D);
@@ -192,14 +243,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
     }
     const float l2 = p.lse[qrow] * kLog2e;
     const float dq_d = p.drow[qrow];
-    const uint32_t qgm = gmh[qpos];
+    const uint32_t qgm = GROUP ? egm[row0 + qrc] : 0u;
     const int w = p.window;
 
     // ---- key tiles
     int n_tiles = 0;
     int64_t j_first = 0;
     if (GROUP) {
-        const int bq_max = tok[e_start + tile_rows - 1];
+        const int bq_max = tok[row0 + tile_rows - 1];
         if (threadIdx.x <= p.K) {
             const int mk = threadIdx.x;
             const int sbk = g * (p.K + 1) + mk;
@@ -227,78 +278,55 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
         for (int i = 0; i <= p.K; ++i)
             n_tiles += (sub_count[i] + kQKeys - 1) / kQKeys;
     } else if (w > 0) {
-        const int64_t lo = std::max<int64_t>(0, p_start - w + 1);
+        const int64_t lo = std::max<int64_t>(0, row0 - w + 1);
         j_first = (lo / kQKeys) * kQKeys;
-        const int64_t j_last = p_start + tile_rows - 1;
+        const int64_t j_last = row0 + tile_rows - 1;
         n_tiles = (int)((j_last - j_first) / kQKeys + 1);
     }
     n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
 
+    // tiles in order: (first row, valid keys, owner flag)
     int it_sub = 0, it_tile = 0;
-    // origin, valid key count and owner flag of the next tile, in order
-    struct TileDesc {
-        int64_t origin;
-        int valid, owner;
-    };
-    auto next_tile = [&]() -> TileDesc {
-        TileDesc t;
+    auto next_tile = [&](int &origin, int &valid, int &owner) {
         if (GROUP) {
             while (it_tile * kQKeys >= sub_count[it_sub]) {
                 ++it_sub;
                 it_tile = 0;
             }
-            t.valid = std::min(kQKeys, sub_count[it_sub] - it_tile * kQKeys);
-            t.owner = sub_owner[it_sub];
-            t.origin = (int64_t)sub_start[it_sub] + (int64_t)it_tile * kQKeys;
+            valid = std::min(kQKeys, sub_count[it_sub] - it_tile * kQKeys);
+            owner = sub_owner[it_sub];
+            origin = sub_start[it_sub] + it_tile * kQKeys;
         } else {
-            t.origin = j_first + (int64_t)it_tile * kQKeys;
-            t.valid = (int)std::min<int64_t>(kQKeys, p.n - t.origin);
-            t.owner = 0;
+            origin = (int)(j_first + (int64_t)it_tile * kQKeys);
+            valid = (int)std::min<int64_t>(kQKeys, p.n - origin);
+            owner = 0;
         }
         ++it_tile;
-        return t;
     };
 
-    // Staging: thread t stages key row (t % 64) of a tile, chunks c = 4 i + t / 64 of
-    // its K and V rows.  The key's position (a bucket lookup in the group pass)
-    // is fetched one tile ahead of its rows, so no load waits on another in
-    // the loop.
-    const int srow = threadIdx.x % kQKeys;
-    const int sc0 = threadIdx.x / kQKeys;
-    auto key_pos = [&](const TileDesc &t) -> int {
-        const int r = std::min(srow, t.valid - 1);
-        return GROUP ? tok[t.origin + r] : (int)(t.origin + r);
-    };
-    // (rows past the tile's end load a valid row and are zeroed when they
-    // land, so that no load has to complete before the next is issued)
-    uint4 kr[CHUNKS], vr[CHUNKS];
-    int kp = kNoPos;
-    uint32_t kg = 0;
-    auto fetch = [&](const TileDesc &t, int pos) {
-        const int64_t base = ((int64_t)kvh * p.n + pos) * D;
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-            const int c = 4 * i + sc0;
-            kr[i] = *reinterpret_cast<const uint4 *>(p.k + base + c * 8);
-            vr[i] = *reinterpret_cast<const uint4 *>(p.v + base + c * 8);
+    // ---- staging: K and V tiles by LDS-DMA (all waves), key positions
+    // (wave 0) and group bits (wave 1) of the group pass by 4-byte DMA
+    Dma dma;
+    dma.init(wave, lane);
+    constexpr int DMA_KV = 2 * Dma::LOADS;
+    const bool extra = GROUP && wave < 2;
+    auto issue = [&](int S) {
+        int origin, valid, owner;
+        next_tile(origin, valid, owner);
+        const int64_t r0 = (int64_t)kvh * rows + origin;
+        dma.issue(p.k + r0 * D, valid, lds_address(stg[S].k), wave);
+        dma.issue(p.v + r0 * D, valid, lds_address(stg[S].v), wave);
+        if (GROUP) {
+            const uint32_t lo = (uint32_t)std::min(lane, valid - 1) * 4u;
+            if (wave == 0)
+                dma4(tok + origin, lo, lds_address(stg[S].pos));
+            else if (wave == 1)
+                dma4(egm + origin, lo, lds_address(stg[S].gm));
         }
-        kg = gmh[pos];
-        kp = srow < t.valid ? pos : kNoPos;
-    };
-    auto land = [&]() {
-        const bool ok = kp != kNoPos;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-            const int c = 4 * i + sc0;
-            const uint4 kx = ok ? kr[i] : z, vx = ok ? vr[i] : z;
-            *reinterpret_cast<uint4 *>(k_lds + rslot<D>(srow, c) * 16) = kx;
-            *reinterpret_cast<uint4 *>(v_lds + rslot<D>(srow, c) * 16) = vx;
-            store_transposed<kQKeys / 8>(kt_lds, kx, srow, c);
-        }
-        if (threadIdx.x < kQKeys) {
-            kpos_lds[srow] = kp;
-            kgm_lds[srow] = kp == kNoPos ? 0u : kg;
+        if (threadIdx.x == 0) {
+            stg[S].desc[0] = origin;
+            stg[S].desc[1] = valid;
+            stg[S].desc[2] = owner;
         }
     };
 
@@ -309,43 +337,54 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
         for (int r = 0; r < 16; ++r)
             acc[db][r] = 0.f;
 
-    const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
-    // tiles it (rows in registers), it + 1 (position known), it + 2
-    // Tile it's rows sit in registers while tile it+1's position is known;
-    // past the last tile the descriptors repeat it, so every load in the
-    // loop is unconditional (no register copy of a load in flight).
-    TileDesc t_cur{}, t_next{};
-    int pos_next = 0;
-    if (n_tiles > 0) {
-        t_cur = next_tile();
-        const int pos0 = key_pos(t_cur);
-        t_next = n_tiles > 1 ? next_tile() : t_cur;
-        pos_next = key_pos(t_next);
-        fetch(t_cur, pos0);
-    }
-    // per-lane LDS slots of the MFMA A fragments: K and V rows (row sigma(m)
-    // of each 32-key block, chunk 2ks+h; the second block is 32 rows on) and
-    // K^T (row db*32+m, chunk 4kb+2h+t; later row blocks are 256 slots on)
-    int koff[KS], ktoff[4];
+    // per-lane LDS byte offsets of the MFMA A fragments: K and V rows (row
+    // sigma(m) of each 32-key block, chunk 2ks+h; the second block is 32 rows
+    // on) and K^T by transpose reads (d = 32 db + m, keys 8h + 4s + 0..3 of
+    // each 16-key step; steps are 8 or 32 rows apart)
+    uint32_t koff[KS], tro[DB][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        koff[ks] = rslot<D>(sigma(m), 2 * ks + h);
+        koff[ks] = rbyte<D>(sigma(m), 2 * ks + h);
+    {
+        const int jj = lane & 15, gp = (lane >> 4) & 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        ktoff[j] = tslot<kQKeys / 8>(m, 4 * (j >> 1) + 2 * h + (j & 1));
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int row = 16 * h + 4 * s + (jj >> 2);
+                const int col = 32 * db + 16 * gp + 4 * (jj & 3);
+                tro[db][s] = rbyte<D>(row, col >> 3) + (uint32_t)(col & 7) * 2u;
+            }
+    }
 
-    for (int it = 0; it < n_tiles; ++it) {
-        __syncthreads();
-        land();
-        const int owner = __builtin_amdgcn_readfirstlane(t_cur.owner);
-        const int valid = __builtin_amdgcn_readfirstlane(t_cur.valid);
-        const int origin = __builtin_amdgcn_readfirstlane((int)t_cur.origin);
-        __syncthreads();
-        fetch(t_next, pos_next);
-        t_cur = t_next;
-        if (it + 2 < n_tiles)
-            t_next = next_tile();
-        pos_next = key_pos(t_next);
+    const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
+    const int T = n_tiles;
+    // the loads above have landed before any DMA is issued (the compiler's
+    // own wait tracking then has nothing left outstanding in the loop)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    if (T > 0)
+        issue(0);
+    if (T > 1)
+        issue(1);
+    if (T > 1)
+        wait_vm<DMA_KV + 1, DMA_KV>(extra);
+    else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+
+    for (int u = 0; u < T; ++u) {
+        const int S = u % kStages;
+        if (u + 2 < T)
+            issue((u + 2) % kStages);
+        const char *kl = stg[S].k;
+        const char *vl = stg[S].v;
+        const int *kpos_lds = stg[S].pos;
+        const uint32_t *kgm_lds = stg[S].gm;
+        const int origin = __builtin_amdgcn_readfirstlane(stg[S].desc[0]);
+        const int valid = __builtin_amdgcn_readfirstlane(stg[S].desc[1]);
+        const int owner = __builtin_amdgcn_readfirstlane(stg[S].desc[2]);
 
         // The keys this lane's query takes form one interval [klo, khi] of
         // the tile: in the window pass positions origin + kk with
@@ -387,16 +426,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
         bf16x8 fa[KS], fb[KS], ktf[DB][4];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            fa[ks] = lds16(k_lds, koff[ks]);
-            fb[ks] = lds16(v_lds, koff[ks]);
+            fa[ks] = lds16(kl, koff[ks]);
+            fb[ks] = lds16(vl, koff[ks]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks], qf[ks], s[0], 0, 0, 0);
             dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks], dof[ks], dp[0], 0, 0, 0);
-            fa[ks] = lds16(k_lds, koff[ks] + 32 * KCH);
-            fb[ks] = lds16(v_lds, koff[ks] + 32 * KCH);
+            fa[ks] = lds16(kl, koff[ks] + 32 * RB);
+            fb[ks] = lds16(vl, koff[ks] + 32 * RB);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -405,8 +444,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
             dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks], dof[ks], dp[1], 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < 4 * DB / KS; ++q) {
-                const int f = ks * (4 * DB / KS) + q;
-                ktf[f / 4][f % 4] = lds16(kt_lds, ktoff[f % 4] + (f / 4) * 32 * (kQKeys / 8));
+                const int f = ks * (4 * DB / KS) + q;  // f / 4 = db, f % 4 = j = 2 kb + t
+                const int db = f / 4, j = f % 4;
+                const uint32_t step = (uint32_t)(32 * (j >> 1) + 8 * (j & 1)) * RB;
+                ktf[db][j] = tr_frag(kl, tro[db][0] + step, tro[db][1] + step);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -436,13 +477,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
             for (int j = 0; j < 4; ++j)
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[db][j], dsf[j >> 1][j & 1],
                                                                  acc[db], 0, 0, 0);
+        // end of the tile: the next tile's loads have landed (the newest
+        // ones may still fly), every wave is done with this stage
+        if (u + 1 < T) {
+            if (u + 2 < T)
+                wait_vm<DMA_KV + 1, DMA_KV>(extra);
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
     }
 
     // ---- store: lane (m, h), register r of block db holds dq[query m][d]
     if (qvalid) {
-        const int64_t row = GROUP ? (int64_t)e_start + qr : p_start + qr;
-        const int64_t rows = GROUP ? p.E : p.n;
-        float *dst = p.dq + ((int64_t)hq * rows + row) * D;
+        float *dst = p.dq + ((int64_t)hq * rows + row0 + qr) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -461,20 +510,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
 {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    constexpr int KCH = D / 8;
-    constexpr int CHUNKS = kKQueries * KCH / kBwdThreads;  // per thread per matrix
-    __shared__ __attribute__((aligned(16))) char q_lds[kKQueries * D * 2];
-    __shared__ __attribute__((aligned(16))) char do_lds[kKQueries * D * 2];
-    __shared__ __attribute__((aligned(16))) char qt_lds[D * kKQueries * 2];
-    __shared__ __attribute__((aligned(16))) char dot_lds[D * kKQueries * 2];
-    __shared__ int qpos_lds[kKQueries];
-    __shared__ __attribute__((aligned(16))) float ql2_lds[kKQueries];
-    __shared__ __attribute__((aligned(16))) float qd_lds[kKQueries];
-    __shared__ uint32_t qgm_lds[kKQueries];
+    constexpr int RB = D * 2;
+    using Dma = TileDma<D, kKQueries>;
+    struct Stage {
+        char q[kKQueries * RB];
+        char d[kKQueries * RB];
+        int pos[kWave];        // query positions
+        float lse[kWave];      // query log-sum-exp
+        float dd[kWave];       // query D_i
+        uint32_t gm[kWave];    // query group bits (group pass)
+        int desc[4];           // origin, valid queries, owner flag
+    };
+    __shared__ __attribute__((aligned(16))) Stage stg[kStages];
     __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int m = lane % 32;
     const int h = lane / 32;
 
@@ -489,29 +540,30 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         slot = blockIdx.x % p.row_tiles;
         kvh = blockIdx.x / p.row_tiles;
     }
-    int g = 0, mk = 0, e_start = 0, tile_keys;
-    int64_t p_start = 0;
+    int g = 0, mk = 0, tile_keys;
+    int64_t row0;
     if (GROUP) {
         const int4 t = p.tiles[(int64_t)kvh * p.max_tiles + slot];
         g = t.x / (p.K + 1);
         mk = t.x % (p.K + 1);
-        e_start = t.y;
+        row0 = t.y;
         tile_keys = t.z;
     } else {
-        p_start = (int64_t)slot * kBwdRows;
-        tile_keys = (int)std::min<int64_t>(kBwdRows, p.n - p_start);
+        row0 = (int64_t)slot * kBwdRows;
+        tile_keys = (int)std::min<int64_t>(kBwdRows, p.n - row0);
     }
+    const int64_t rows = GROUP ? p.E : p.n;
     const int32_t *tok = GROUP ? p.tokens + (int64_t)kvh * p.E : nullptr;
-    const uint32_t *gmh = p.gmask + (int64_t)kvh * p.n;
+    const uint32_t *egm = GROUP ? p.egm + (int64_t)kvh * p.E : nullptr;
 
     // ---- this lane's key (column m of the wavefront's 32 keys)
     const int kr = wave * 32 + m;
     const bool kvalid = kr < tile_keys;
     const int krc = kvalid ? kr : 0;
-    const int kpos = GROUP ? tok[e_start + krc] : (int)(p_start + krc);
+    const int kpos = GROUP ? tok[row0 + krc] : (int)(row0 + krc);
     bf16x8 kf[KS], vf[KS];
     {
-        const int64_t row = (int64_t)kvh * p.n + kpos;
+        const int64_t row = (int64_t)kvh * rows + row0 + krc;
         const bf16x8 *ks_ = reinterpret_cast<const bf16x8 *>(p.k + row * D);
         const bf16x8 *vs_ = reinterpret_cast<const bf16x8 *>(p.v + row * D);
 #pragma unroll
@@ -520,14 +572,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             vf[ks] = vs_[ks * 2 + h];
         }
     }
-    const uint32_t kgm = gmh[kpos];
+    const uint32_t kgm = GROUP ? egm[row0 + krc] : 0u;
     const int w = p.window;
 
     // ---- query tiles, per query head
     int tiles_per_head = 0;
     int64_t i_first = 0;
     if (GROUP) {
-        const int bk_min = tok[e_start];  // keys ascend inside the sub-bucket
+        const int bk_min = tok[row0];  // keys ascend inside the sub-bucket
         if (threadIdx.x <= p.K) {
             const int mq = threadIdx.x;
             const int sbq = g * (p.K + 1) + mq;
@@ -555,19 +607,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         for (int i = 0; i <= p.K; ++i)
             tiles_per_head += (sub_count[i] + kKQueries - 1) / kKQueries;
     } else if (w > 0) {
-        i_first = p_start;
-        const int64_t i_last = std::min<int64_t>(p.n - 1, p_start + tile_keys - 1 + w - 1);
+        i_first = row0;
+        const int64_t i_last = std::min<int64_t>(p.n - 1, row0 + tile_keys - 1 + w - 1);
         tiles_per_head = (int)((i_last - i_first) / kKQueries + 1);
     }
     tiles_per_head = __builtin_amdgcn_readfirstlane(tiles_per_head);
     const int n_tiles = tiles_per_head * p.ratio;
 
+    // tiles in order, per query head: (head, first row, valid queries, owner)
     int it_head = 0, it_sub = 0, it_tile = 0, it_count = 0;
-    struct TileDesc {
-        int64_t origin;
-        int valid, owner, head;
-    };
-    auto next_tile = [&]() -> TileDesc {
+    auto next_tile = [&](int &head, int &origin, int &valid, int &owner) {
         if (it_count == tiles_per_head) {  // next query head
             ++it_head;
             it_sub = 0;
@@ -575,68 +624,51 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             it_count = 0;
         }
         ++it_count;
-        TileDesc t;
-        t.head = kvh * p.ratio + it_head;
+        head = kvh * p.ratio + it_head;
         if (GROUP) {
             while (it_tile * kKQueries >= sub_count[it_sub]) {
                 ++it_sub;
                 it_tile = 0;
             }
-            t.valid = std::min(kKQueries, sub_count[it_sub] - it_tile * kKQueries);
-            t.owner = sub_owner[it_sub];
-            t.origin = (int64_t)sub_start[it_sub] + (int64_t)it_tile * kKQueries;
+            valid = std::min(kKQueries, sub_count[it_sub] - it_tile * kKQueries);
+            owner = sub_owner[it_sub];
+            origin = sub_start[it_sub] + it_tile * kKQueries;
         } else {
-            t.origin = i_first + (int64_t)it_tile * kKQueries;
-            t.valid = (int)std::min<int64_t>(kKQueries, p.n - t.origin);
-            t.owner = 0;
+            origin = (int)(i_first + (int64_t)it_tile * kKQueries);
+            valid = (int)std::min<int64_t>(kKQueries, p.n - origin);
+            owner = 0;
         }
         ++it_tile;
-        return t;
     };
 
-    // Staging: thread t stages query row (t % 32), chunks c = 8 i + t / 32 of
-    // its Q and dO rows, and (t < 32) the row's position, log2-domain LSE, D
-    // and group bits.  Positions are fetched one tile ahead of the rows.
-    const int srow = threadIdx.x % kKQueries;
-    const int sc0 = threadIdx.x / kKQueries;
-    auto query_pos = [&](const TileDesc &t) -> int {
-        const int r = std::min(srow, t.valid - 1);
-        return GROUP ? tok[t.origin + r] : (int)(t.origin + r);
-    };
-    uint4 qr_[CHUNKS], dr_[CHUNKS];
-    int qp = kNoPos;
-    float ql2 = 0.f, qd = 0.f;
-    uint32_t qg = 0;
-    auto fetch = [&](const TileDesc &t, int pos) {
-        const int64_t qrow = (int64_t)t.head * p.n + pos;
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-            const int c = 8 * i + sc0;
-            qr_[i] = *reinterpret_cast<const uint4 *>(p.q + qrow * D + c * 8);
-            dr_[i] = *reinterpret_cast<const uint4 *>(p.dout + qrow * D + c * 8);
+    // ---- staging: Q and dO tiles by LDS-DMA (all waves); per query, the
+    // log-sum-exp (wave 1) and D (wave 2), and in the group pass the position
+    // (wave 0) and group bits (wave 3), by 4-byte DMA
+    Dma dma;
+    dma.init(wave, lane);
+    constexpr int DMA_QD = 2 * Dma::LOADS;
+    const bool extra = GROUP ? true : (wave == 1 || wave == 2);
+    auto issue = [&](int S) {
+        int head, origin, valid, owner;
+        next_tile(head, origin, valid, owner);
+        const int64_t r0 = (int64_t)head * rows + origin;
+        dma.issue(p.q + r0 * D, valid, lds_address(stg[S].q), wave);
+        dma.issue(p.dout + r0 * D, valid, lds_address(stg[S].d), wave);
+        const uint32_t lo = (uint32_t)std::min(lane, valid - 1) * 4u;
+        if (wave == 0) {
+            if (GROUP)
+                dma4(tok + origin, lo, lds_address(stg[S].pos));
+        } else if (wave == 1) {
+            dma4(p.lse + r0, lo, lds_address(stg[S].lse));
+        } else if (wave == 2) {
+            dma4(p.drow + r0, lo, lds_address(stg[S].dd));
+        } else if (GROUP) {
+            dma4(egm + origin, lo, lds_address(stg[S].gm));
         }
-        ql2 = p.lse[qrow] * kLog2e;
-        qd = p.drow[qrow];
-        qg = gmh[pos];
-        qp = srow < t.valid ? pos : kNoPos;
-    };
-    auto land = [&]() {
-        const bool ok = qp != kNoPos;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-            const int c = 8 * i + sc0;
-            const uint4 qx = ok ? qr_[i] : z, dx = ok ? dr_[i] : z;
-            *reinterpret_cast<uint4 *>(q_lds + rslot<D>(srow, c) * 16) = qx;
-            *reinterpret_cast<uint4 *>(do_lds + rslot<D>(srow, c) * 16) = dx;
-            store_transposed<kKQueries / 8>(qt_lds, qx, srow, c);
-            store_transposed<kKQueries / 8>(dot_lds, dx, srow, c);
-        }
-        if (threadIdx.x < kKQueries) {
-            qpos_lds[srow] = qp;
-            ql2_lds[srow] = ok ? ql2 : 0.f;
-            qd_lds[srow] = ok ? qd : 0.f;
-            qgm_lds[srow] = ok ? qg : 0u;
+        if (threadIdx.x == 0) {
+            stg[S].desc[0] = origin;
+            stg[S].desc[1] = valid;
+            stg[S].desc[2] = owner;
         }
     };
 
@@ -647,38 +679,51 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         for (int r = 0; r < 16; ++r)
             dk_acc[db][r] = dv_acc[db][r] = 0.f;
 
-    const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
-    TileDesc t_cur{}, t_next{};
-    int pos_next = 0;
-    if (n_tiles > 0) {
-        t_cur = next_tile();
-        const int pos0 = query_pos(t_cur);
-        t_next = n_tiles > 1 ? next_tile() : t_cur;
-        pos_next = query_pos(t_next);
-        fetch(t_cur, pos0);
-    }
-    // per-lane LDS slots: Q and dO rows (row sigma(m), chunk 2ks+h) and
-    // Q^T / dO^T (row db*32+m, chunk 2h+t; later row blocks 128 slots on)
-    int qoff[KS], qtoff[2];
+    // per-lane LDS byte offsets: Q and dO rows (row sigma(m), chunk 2ks+h)
+    // and Q^T / dO^T by transpose reads (d = 32 db + m, queries
+    // 16h + 8t + 4s + 0..3; t adds 8 rows)
+    uint32_t qoff[KS], tro[DB][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qoff[ks] = rslot<D>(sigma(m), 2 * ks + h);
+        qoff[ks] = rbyte<D>(sigma(m), 2 * ks + h);
+    {
+        const int jj = lane & 15, gp = (lane >> 4) & 1;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-        qtoff[t] = tslot<kKQueries / 8>(m, 2 * h + t);
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int row = 16 * h + 4 * s + (jj >> 2);
+                const int col = 32 * db + 16 * gp + 4 * (jj & 3);
+                tro[db][s] = rbyte<D>(row, col >> 3) + (uint32_t)(col & 7) * 2u;
+            }
+    }
 
-    for (int it = 0; it < n_tiles; ++it) {
-        __syncthreads();
-        land();
-        const int owner = __builtin_amdgcn_readfirstlane(t_cur.owner);
-        const int valid = __builtin_amdgcn_readfirstlane(t_cur.valid);
-        const int origin = __builtin_amdgcn_readfirstlane((int)t_cur.origin);
-        __syncthreads();
-        fetch(t_next, pos_next);
-        t_cur = t_next;
-        if (it + 2 < n_tiles)
-            t_next = next_tile();
-        pos_next = query_pos(t_next);
+    const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
+    const int T = n_tiles;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    if (T > 0)
+        issue(0);
+    if (T > 1)
+        issue(1);
+    if (T > 1)
+        wait_vm<DMA_QD + 1, DMA_QD>(extra);
+    else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+
+    for (int u = 0; u < T; ++u) {
+        const int S = u % kStages;
+        if (u + 2 < T)
+            issue((u + 2) % kStages);
+        const char *ql = stg[S].q;
+        const char *dl = stg[S].d;
+        const int *qpos_lds = stg[S].pos;
+        const uint32_t *qgm_lds = stg[S].gm;
+        const int origin = __builtin_amdgcn_readfirstlane(stg[S].desc[0]);
+        const int valid = __builtin_amdgcn_readfirstlane(stg[S].desc[1]);
+        const int owner = __builtin_amdgcn_readfirstlane(stg[S].desc[2]);
 
         // The queries that see this lane's key form one interval [qlo, qhi]
         // of the tile: positions origin + qi with 0 <= qpos - kpos < w in the
@@ -714,8 +759,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         bf16x8 qfr[KS], dfr[KS], dtf[DB][2], qtf[DB][2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            qfr[ks] = lds16(q_lds, qoff[ks]);
-            dfr[ks] = lds16(do_lds, qoff[ks]);
+            qfr[ks] = lds16(ql, qoff[ks]);
+            dfr[ks] = lds16(dl, qoff[ks]);
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x16 s, dp;
@@ -729,24 +774,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
 #pragma unroll
             for (int q = 0; q < 2 * DB / KS; ++q) {
                 const int f = ks * (2 * DB / KS) + q;  // f / 2 = db, f % 2 = t
-                dtf[f / 2][f % 2] = lds16(dot_lds, qtoff[f % 2] + (f / 2) * 32 * (kKQueries / 8));
-                qtf[f / 2][f % 2] = lds16(qt_lds, qtoff[f % 2] + (f / 2) * 32 * (kKQueries / 8));
+                const int db = f / 2, t = f % 2;
+                const uint32_t step = (uint32_t)(8 * t * RB);
+                dtf[db][t] = tr_frag(dl, tro[db][0] + step, tro[db][1] + step);
+                qtf[db][t] = tr_frag(ql, tro[db][0] + step, tro[db][1] + step);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // P and dS, four queries at a time (their log2-domain LSE and D are
-        // read as vectors: queries 16h + 4j .. 16h + 4j + 3)
+        // P and dS, four queries at a time (their log-sum-exp and D are read
+        // as vectors: queries 16h + 4j .. 16h + 4j + 3)
         f32x16 ds;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 l4 = reinterpret_cast<const float4 *>(ql2_lds)[4 * h + j];
-            const float4 d4 = reinterpret_cast<const float4 *>(qd_lds)[4 * h + j];
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float4 l4 = reinterpret_cast<const float4 *>(stg[S].lse)[4 * h + j];
+            const float4 d4 = reinterpret_cast<const float4 *>(stg[S].dd)[4 * h + j];
+            const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
             const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = 4 * j + u;
-                float pr = __builtin_amdgcn_exp2f(s[r] * p.c - lv[u]);
+            for (int u4 = 0; u4 < 4; ++u4) {
+                const int r = 4 * j + u4;
+                float pr = __builtin_amdgcn_exp2f(s[r] * p.c - lv[u4]);
                 if (!full) {
                     const int qi = 16 * h + r;
                     bool ok = qi >= qlo && qi <= qhi;
@@ -755,7 +802,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
                     pr = ok ? pr : 0.f;
                 }
                 s[r] = pr;
-                ds[r] = pr * (dp[r] - dv4[u]);
+                ds[r] = pr * (dp[r] - dv4[u4]);
             }
         }
         const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
@@ -770,13 +817,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
                 dk_acc[db] =
                     __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf[db][t], dsf[t], dk_acc[db], 0, 0, 0);
             }
+        if (u + 1 < T) {
+            if (u + 2 < T)
+                wait_vm<DMA_QD + 1, DMA_QD>(extra);
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
     }
 
     if (kvalid) {
-        const int64_t row = GROUP ? (int64_t)e_start + kr : p_start + kr;
-        const int64_t rows = GROUP ? p.E : p.n;
-        float *dk = p.dk + ((int64_t)kvh * rows + row) * D;
-        float *dv = p.dv + ((int64_t)kvh * rows + row) * D;
+        float *dk = p.dk + ((int64_t)kvh * rows + row0 + kr) * D;
+        float *dv = p.dv + ((int64_t)kvh * rows + row0 + kr) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -845,6 +898,46 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const int32_t *__restrict
     }
 }
 
+// Bucket-order copies for the group passes: row e of head h of each
+// destination is row tokens[h / ratio][e] of head h of its source (whole
+// rows, 16 bytes per lane).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_gather_rows_kernel(
+    const __bf16 *__restrict__ a, const __bf16 *__restrict__ b,
+    const int32_t *__restrict__ tokens, int ratio, int64_t n, int64_t E, int64_t total,
+    __bf16 *__restrict__ da, __bf16 *__restrict__ db)
+{
+    constexpr int KCH = D / 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t r = idx / KCH;
+    if (r >= total)
+        return;
+    const int c = (int)(idx % KCH);
+    const int64_t h = r / E, e = r % E;
+    const int64_t src = (h * n + tokens[(h / ratio) * E + e]) * D + c * 8;
+    reinterpret_cast<uint4 *>(da + r * D)[c] = *reinterpret_cast<const uint4 *>(a + src);
+    reinterpret_cast<uint4 *>(db + r * D)[c] = *reinterpret_cast<const uint4 *>(b + src);
+}
+
+// The per-row scalars of the same copies: log-sum-exp and D per (query
+// head, entry), group bits per (key/value head, entry).
+__global__ __launch_bounds__(256) void bwd_gather_scalars_kernel(
+    const float *__restrict__ lse, const float *__restrict__ drow,
+    const uint32_t *__restrict__ gmask, const int32_t *__restrict__ tokens, int hq, int hkv,
+    int ratio, int64_t n, int64_t E, float *__restrict__ glse, float *__restrict__ gd,
+    uint32_t *__restrict__ egm)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx < (int64_t)hq * E) {
+        const int64_t h = idx / E, e = idx % E;
+        const int64_t src = h * n + tokens[(h / ratio) * E + e];
+        glse[idx] = lse[src];
+        gd[idx] = drow[src];
+    }
+    if (idx < (int64_t)hkv * E)
+        egm[idx] = gmask[(idx / E) * n + tokens[idx]];
+}
+
 // out[head][t] = win[head][t] + sum_s grp[head'][slot_entry[t][s]], in bf16;
 // the bucket arrays are per key/value head (head' = head / ratio).
 template <int D>
@@ -880,7 +973,8 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(const float *__restrict_
 }
 
 struct BwdLayout {
-    size_t drow, dq_win, dk_win, dv_win, dq_grp, dk_grp, dv_grp, tiles, ntiles, total;
+    size_t drow, dq_win, dk_win, dv_win, dq_grp, dk_grp, dv_grp, tiles, ntiles;
+    size_t kg, vg, qg, dog, glse, gd, egm, total;
     int max_tiles;
 };
 
@@ -905,6 +999,14 @@ BwdLayout bwd_layout(const AttnShape &sh)
     L.dv_grp = take(sizeof(float) * sh.hkv * E * sh.d);
     L.tiles = take(sizeof(int4) * sh.hkv * (size_t)L.max_tiles);
     L.ntiles = take(sizeof(int32_t) * sh.hkv);
+    // bucket-order copies read by the group passes
+    L.kg = take(sizeof(__bf16) * sh.hkv * E * sh.d);
+    L.vg = take(sizeof(__bf16) * sh.hkv * E * sh.d);
+    L.qg = take(sizeof(__bf16) * sh.hq * E * sh.d);
+    L.dog = take(sizeof(__bf16) * sh.hq * E * sh.d);
+    L.glse = take(sizeof(float) * sh.hq * E);
+    L.gd = take(sizeof(float) * sh.hq * E);
+    L.egm = take(sizeof(uint32_t) * sh.hkv * E);
     L.total = off;
     return L;
 }
@@ -938,7 +1040,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
     p.drow = reinterpret_cast<float *>(base + L.drow);
     p.tokens = tokens;
     p.offsets = offsets;
-    p.gmask = gmask;
+    p.egm = nullptr;
     p.tiles = reinterpret_cast<const int4 *>(base + L.tiles);
     p.ntiles = reinterpret_cast<const int32_t *>(base + L.ntiles);
     p.max_tiles = L.max_tiles;
@@ -953,7 +1055,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
                        reinterpret_cast<int4 *>(base + L.tiles),
                        reinterpret_cast<int32_t *>(base + L.ntiles));
 
-    // window pass
+    // window pass: rows in position order
     p.dq = reinterpret_cast<float *>(base + L.dq_win);
     p.dk = reinterpret_cast<float *>(base + L.dk_win);
     p.dv = reinterpret_cast<float *>(base + L.dv_win);
@@ -961,14 +1063,42 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
                        dim3(kBwdThreads), 0, s, p);
     hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3((unsigned)(sh.hkv * p.row_tiles)),
                        dim3(kBwdThreads), 0, s, p);
-    // group pass
-    p.dq = reinterpret_cast<float *>(base + L.dq_grp);
-    p.dk = reinterpret_cast<float *>(base + L.dk_grp);
-    p.dv = reinterpret_cast<float *>(base + L.dv_grp);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)(sh.hq * L.max_tiles)),
-                       dim3(kBwdThreads), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3((unsigned)(sh.hkv * L.max_tiles)),
-                       dim3(kBwdThreads), 0, s, p);
+
+    // group pass: rows gathered into bucket order first
+    if (E > 0) {
+        __bf16 *kg = reinterpret_cast<__bf16 *>(base + L.kg);
+        __bf16 *vg = reinterpret_cast<__bf16 *>(base + L.vg);
+        __bf16 *qg = reinterpret_cast<__bf16 *>(base + L.qg);
+        __bf16 *dog = reinterpret_cast<__bf16 *>(base + L.dog);
+        float *glse = reinterpret_cast<float *>(base + L.glse);
+        float *gd = reinterpret_cast<float *>(base + L.gd);
+        uint32_t *egm = reinterpret_cast<uint32_t *>(base + L.egm);
+        const int64_t krows = (int64_t)sh.hkv * E, qrows_g = (int64_t)sh.hq * E;
+        hipLaunchKernelGGL(bwd_gather_rows_kernel<D>,
+                           dim3((unsigned)((krows * (D / 8) + 255) / 256)), dim3(256), 0, s,
+                           p.k, p.v, tokens, 1, n, E, krows, kg, vg);
+        hipLaunchKernelGGL(bwd_gather_rows_kernel<D>,
+                           dim3((unsigned)((qrows_g * (D / 8) + 255) / 256)), dim3(256), 0, s,
+                           p.q, p.dout, tokens, p.ratio, n, E, qrows_g, qg, dog);
+        hipLaunchKernelGGL(bwd_gather_scalars_kernel, dim3((unsigned)((qrows_g + 255) / 256)),
+                           dim3(256), 0, s, lse, p.drow, gmask, tokens, sh.hq, sh.hkv, p.ratio,
+                           n, E, glse, gd, egm);
+        BwdParams pg = p;
+        pg.q = qg;
+        pg.k = kg;
+        pg.v = vg;
+        pg.dout = dog;
+        pg.lse = glse;
+        pg.drow = gd;
+        pg.egm = egm;
+        pg.dq = reinterpret_cast<float *>(base + L.dq_grp);
+        pg.dk = reinterpret_cast<float *>(base + L.dk_grp);
+        pg.dv = reinterpret_cast<float *>(base + L.dv_grp);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)(sh.hq * L.max_tiles)),
+                           dim3(kBwdThreads), 0, s, pg);
+        hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3((unsigned)(sh.hkv * L.max_tiles)),
+                           dim3(kBwdThreads), 0, s, pg);
+    }
     // merge
     const int64_t qv = qrows * (D / 4), kv = (int64_t)sh.hkv * n * (D / 4);
     hipLaunchKernelGGL(bwd_merge_kernel<D>, dim3((unsigned)((qv + 255) / 256)), dim3(256), 0, s,
