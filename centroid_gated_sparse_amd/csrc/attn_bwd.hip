@@ -61,7 +61,7 @@ struct BwdParams {
     // rows in position order (window pass) or gathered in entry order (group
     // pass): [heads][rows][D] with rows = n or E
     const __bf16 *q, *k, *v, *dout;
-    const float *lse;   // forward log-sum-exp, [hq][rows]
+    const float *l2;    // forward log-sum-exp times log2(e), [hq][rows]
     const float *drow;  // D_i = dO_i . O_i, [hq][rows]
     // group pass
     const uint32_t *egm;     // group bits per entry [hkv][E]
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
             dof[ks] = ds[ks * 2 + h];
         }
     }
-    const float l2 = p.lse[qrow] * kLog2e;
+    const float l2 = p.l2[qrow];
     const float dq_d = p.drow[qrow];
     const uint32_t qgm = GROUP ? egm[row0 + qrc] : 0u;
     const int w = p.window;
@@ -515,11 +515,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     struct Stage {
         char q[kKQueries * RB];
         char d[kKQueries * RB];
-        int pos[kWave];        // query positions
-        float lse[kWave];      // query log-sum-exp
+        int pos[kWave];        // query positions (group pass)
+        float l2[kWave];       // query log-sum-exp times log2(e)
         float dd[kWave];       // query D_i
         uint32_t gm[kWave];    // query group bits (group pass)
-        int desc[4];           // origin, valid queries, owner flag
     };
     __shared__ __attribute__((aligned(16))) Stage stg[kStages];
     __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
@@ -612,45 +611,60 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         tiles_per_head = (int)((i_last - i_first) / kKQueries + 1);
     }
     tiles_per_head = __builtin_amdgcn_readfirstlane(tiles_per_head);
-    const int n_tiles = tiles_per_head * p.ratio;
+    const int T = tiles_per_head * p.ratio;
+    // a tile whose first query is at or after this wave's largest kpos + w
+    // is seen by every key of the wave (group pass)
+    int wave_lim = kvalid ? kpos + w : -0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        wave_lim = std::max(wave_lim, __shfl_xor(wave_lim, off));
+    wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
 
-    // tiles in order, per query head: (head, first row, valid queries, owner)
-    int it_head = 0, it_sub = 0, it_tile = 0, it_count = 0;
-    auto next_tile = [&](int &head, int &origin, int &valid, int &owner) {
-        if (it_count == tiles_per_head) {  // next query head
-            ++it_head;
-            it_sub = 0;
-            it_tile = 0;
-            it_count = 0;
+    // ---- tiles in order, per query head (wave-uniform iterator; the issue
+    // side runs two tiles ahead of the compute side)
+    struct It {
+        int head, sub, tile, count, cnt, start, owner;
+    };
+    auto it_next = [&](It &t, int &head, int &origin, int &valid, int &owner) {
+        if (t.count == tiles_per_head) {  // next query head
+            ++t.head;
+            t.sub = -1;
+            t.tile = 0;
+            t.cnt = 0;
+            t.count = 0;
         }
-        ++it_count;
-        head = kvh * p.ratio + it_head;
+        ++t.count;
+        head = kvh * p.ratio + t.head;
         if (GROUP) {
-            while (it_tile * kKQueries >= sub_count[it_sub]) {
-                ++it_sub;
-                it_tile = 0;
+            while (t.tile * kKQueries >= t.cnt) {
+                ++t.sub;
+                t.tile = 0;
+                t.cnt = __builtin_amdgcn_readfirstlane(sub_count[t.sub]);
+                t.start = __builtin_amdgcn_readfirstlane(sub_start[t.sub]);
+                t.owner = __builtin_amdgcn_readfirstlane(sub_owner[t.sub]);
             }
-            valid = std::min(kKQueries, sub_count[it_sub] - it_tile * kKQueries);
-            owner = sub_owner[it_sub];
-            origin = sub_start[it_sub] + it_tile * kKQueries;
+            valid = std::min(kKQueries, t.cnt - t.tile * kKQueries);
+            origin = t.start + t.tile * kKQueries;
+            owner = t.owner;
         } else {
-            origin = (int)(i_first + (int64_t)it_tile * kKQueries);
+            origin = (int)(i_first + (int64_t)t.tile * kKQueries);
             valid = (int)std::min<int64_t>(kKQueries, p.n - origin);
             owner = 0;
         }
-        ++it_tile;
+        ++t.tile;
     };
+    It it_issue{0, -1, 0, 0, 0, 0, 0}, it_comp{0, -1, 0, 0, 0, 0, 0};
 
     // ---- staging: Q and dO tiles by LDS-DMA (all waves); per query, the
-    // log-sum-exp (wave 1) and D (wave 2), and in the group pass the position
-    // (wave 0) and group bits (wave 3), by 4-byte DMA
+    // log2-domain log-sum-exp (wave 1) and D (wave 2), and in the group pass
+    // the position (wave 0) and group bits (wave 3), by 4-byte DMA
     Dma dma;
     dma.init(wave, lane);
     constexpr int DMA_QD = 2 * Dma::LOADS;
     const bool extra = GROUP ? true : (wave == 1 || wave == 2);
     auto issue = [&](int S) {
         int head, origin, valid, owner;
-        next_tile(head, origin, valid, owner);
+        it_next(it_issue, head, origin, valid, owner);
         const int64_t r0 = (int64_t)head * rows + origin;
         dma.issue(p.q + r0 * D, valid, lds_address(stg[S].q), wave);
         dma.issue(p.dout + r0 * D, valid, lds_address(stg[S].d), wave);
@@ -659,16 +673,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             if (GROUP)
                 dma4(tok + origin, lo, lds_address(stg[S].pos));
         } else if (wave == 1) {
-            dma4(p.lse + r0, lo, lds_address(stg[S].lse));
+            dma4(p.l2 + r0, lo, lds_address(stg[S].l2));
         } else if (wave == 2) {
             dma4(p.drow + r0, lo, lds_address(stg[S].dd));
         } else if (GROUP) {
             dma4(egm + origin, lo, lds_address(stg[S].gm));
-        }
-        if (threadIdx.x == 0) {
-            stg[S].desc[0] = origin;
-            stg[S].desc[1] = valid;
-            stg[S].desc[2] = owner;
         }
     };
 
@@ -699,7 +708,145 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     }
 
     const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
-    const int T = n_tiles;
+
+    // One query tile in stage S.  Order: S = Q K^T, then dP = dO V^T (each
+    // with its 16-byte fragments streamed two steps ahead and the transpose
+    // reads of dO^T / Q^T between the MFMAs), then P (exp2 and the key's
+    // query mask), dv^T += dO^T P while dS = P (dP - D) is formed, and
+    // dk^T += Q^T dS.
+    auto body = [&](int S, int u) {
+        if (u + 2 < T)
+            issue(S == 0 ? 2 : S - 1);
+        int head_c, origin, valid, owner;
+        it_next(it_comp, head_c, origin, valid, owner);
+        (void)head_c;
+        const char *ql = stg[S].q;
+        const char *dl = stg[S].d;
+        const int qfirst = GROUP ? stg[S].pos[0] : 0;
+
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            s[r] = dp[r] = 0.f;
+        bf16x8 dtf[DB][2], qtf[DB][2];
+        bf16x8 fr[3];
+        fr[0] = lds16(ql, qoff[0]);
+        fr[1] = lds16(ql, qoff[1]);
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) {  // i < KS: S step i; else dP step i - KS
+            if (i + 2 < 2 * KS) {
+                const int n2 = i + 2;
+                fr[n2 % 3] = lds16(n2 < KS ? ql : dl, qoff[n2 % KS]);
+            }
+            if (i < KS)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3], kf[i], s, 0, 0, 0);
+            else
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3], vf[i - KS], dp, 0, 0, 0);
+            // transpose reads: dO^T during S, Q^T during dP (2 DB fragments each)
+#pragma unroll
+            for (int q = 0; q < 2 * DB / KS; ++q) {
+                const int f = (i % KS) * (2 * DB / KS) + q;  // f / 2 = db, f % 2 = t
+                const int db = f / 2, t = f % 2;
+                const uint32_t step = (uint32_t)(8 * t * RB);
+                if (i < KS)
+                    dtf[db][t] = tr_frag(dl, tro[db][0] + step, tro[db][1] + step);
+                else
+                    qtf[db][t] = tr_frag(ql, tro[db][0] + step, tro[db][1] + step);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // Queries this lane's key sees, as a bit mask over the tile: an
+        // interval (window: 0 <= qpos - kpos < w; group: the queries ascend,
+        // the far ones qpos >= kpos + w are a suffix), in the group pass's
+        // owner tiles also without a lower shared group.
+        uint32_t qmask;
+        if (GROUP) {
+            const uint32_t vmask = valid == kKQueries ? 0xffffffffu : ((1u << valid) - 1u);
+            int qlo = 0;
+            if (__builtin_amdgcn_readfirstlane(qfirst) < wave_lim && kvalid) {
+                const int lim = kpos + w;
+                if (qfirst < lim) {
+                    int lo = 0, hi = valid;
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (stg[S].pos[mid] < lim)
+                            lo = mid + 1;
+                        else
+                            hi = mid;
+                    }
+                    qlo = lo;
+                }
+            }
+            qmask = kvalid && qlo < kKQueries ? (vmask & (0xffffffffu << qlo)) : 0u;
+            if (owner) {
+                for (int qi = 0; qi < valid; ++qi)
+                    if ((stg[S].gm[qi] & kgm & low) != 0u)
+                        qmask &= ~(1u << qi);
+            }
+        } else {
+            const int qlo = std::max(0, kpos - origin);
+            const int qhi = std::min(valid - 1, kpos - origin + w - 1);
+            qmask = kvalid && qhi >= qlo
+                        ? (uint32_t)((2ull << qhi) - (1ull << qlo))
+                        : 0u;
+        }
+        // this lane's 16 queries are 16h .. 16h + 15
+        const uint32_t mh = qmask >> (16 * h);
+
+        // P = exp2(S c - L log2 e) on the mask (log-sum-exp and D read as
+        // vectors: queries 16h + 4j .. 16h + 4j + 3)
+        float dv4[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 l4 = reinterpret_cast<const float4 *>(stg[S].l2)[4 * h + j];
+            const float4 d4 = reinterpret_cast<const float4 *>(stg[S].dd)[4 * h + j];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            dv4[4 * j] = d4.x;
+            dv4[4 * j + 1] = d4.y;
+            dv4[4 * j + 2] = d4.z;
+            dv4[4 * j + 3] = d4.w;
+#pragma unroll
+            for (int u4 = 0; u4 < 4; ++u4) {
+                const int r = 4 * j + u4;
+                const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - lv[u4]);
+                const int keep = __builtin_amdgcn_sbfe((int)mh, r, 1);  // 0 or -1
+                s[r] = __int_as_float(__float_as_int(pr) & keep);
+            }
+        }
+        const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
+        // dv^T += dO^T P while dS = P (dP - D) is formed
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                dv_acc[db] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(dtf[db][t], pf[t], dv_acc[db], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dp[r] = s[r] * (dp[r] - dv4[r]);
+        const bf16x8 dsf[2] = {pack8(dp, 0), pack8(dp, 1)};
+        // dk^T += Q^T dS
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                dk_acc[db] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf[db][t], dsf[t], dk_acc[db], 0, 0, 0);
+        // end of the tile: the next tile's loads have landed (the newest
+        // ones may still fly), every wave is done with this stage
+        if (u + 1 < T) {
+            if (u + 2 < T)
+                wait_vm<DMA_QD + 1, DMA_QD>(extra);
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+    };
+
+    // the loads above have landed before any DMA is issued (the compiler's
+    // own wait tracking then has nothing outstanding in the loop)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     asm volatile("" ::: "memory");
@@ -712,120 +859,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     else
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __syncthreads();
-
-    for (int u = 0; u < T; ++u) {
-        const int S = u % kStages;
-        if (u + 2 < T)
-            issue((u + 2) % kStages);
-        const char *ql = stg[S].q;
-        const char *dl = stg[S].d;
-        const int *qpos_lds = stg[S].pos;
-        const uint32_t *qgm_lds = stg[S].gm;
-        const int origin = __builtin_amdgcn_readfirstlane(stg[S].desc[0]);
-        const int valid = __builtin_amdgcn_readfirstlane(stg[S].desc[1]);
-        const int owner = __builtin_amdgcn_readfirstlane(stg[S].desc[2]);
-
-        // The queries that see this lane's key form one interval [qlo, qhi]
-        // of the tile: positions origin + qi with 0 <= qpos - kpos < w in the
-        // window pass; in the group pass the queries ascend and the far ones
-        // (qpos >= kpos + w) are a suffix.
-        int qlo = 0, qhi = -1;
-        if (kvalid) {
-            if (GROUP) {
-                const int lim = kpos + w;
-                qhi = valid - 1;
-                if (qpos_lds[0] < lim) {
-                    int lo = 0, hi = valid;
-                    while (lo < hi) {
-                        const int mid = (lo + hi) >> 1;
-                        if (qpos_lds[mid] < lim)
-                            lo = mid + 1;
-                        else
-                            hi = mid;
-                    }
-                    qlo = lo;
-                }
-            } else {
-                qlo = std::max(0, kpos - origin);
-                qhi = std::min(valid - 1, kpos - origin + w - 1);
-            }
-        }
-        const bool full =
-            !owner && __builtin_amdgcn_ballot_w64(!(qlo <= 0 && qhi >= kKQueries - 1)) == 0;
-
-        // S = Q K^T and dP = dO V^T: rows are queries (sigma), columns keys.
-        // The Q / dO fragments are read first; the Q^T / dO^T fragments of
-        // the second product are read between the MFMAs (fenced order).
-        bf16x8 qfr[KS], dfr[KS], dtf[DB][2], qtf[DB][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qfr[ks] = lds16(ql, qoff[ks]);
-            dfr[ks] = lds16(dl, qoff[ks]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            s[r] = dp[r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[ks], kf[ks], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[ks], vf[ks], dp, 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 2 * DB / KS; ++q) {
-                const int f = ks * (2 * DB / KS) + q;  // f / 2 = db, f % 2 = t
-                const int db = f / 2, t = f % 2;
-                const uint32_t step = (uint32_t)(8 * t * RB);
-                dtf[db][t] = tr_frag(dl, tro[db][0] + step, tro[db][1] + step);
-                qtf[db][t] = tr_frag(ql, tro[db][0] + step, tro[db][1] + step);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // P and dS, four queries at a time (their log-sum-exp and D are read
-        // as vectors: queries 16h + 4j .. 16h + 4j + 3)
-        f32x16 ds;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 l4 = reinterpret_cast<const float4 *>(stg[S].lse)[4 * h + j];
-            const float4 d4 = reinterpret_cast<const float4 *>(stg[S].dd)[4 * h + j];
-            const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int u4 = 0; u4 < 4; ++u4) {
-                const int r = 4 * j + u4;
-                float pr = __builtin_amdgcn_exp2f(s[r] * p.c - lv[u4]);
-                if (!full) {
-                    const int qi = 16 * h + r;
-                    bool ok = qi >= qlo && qi <= qhi;
-                    if (GROUP && owner)
-                        ok = ok && ((qgm_lds[qi] & kgm & low) == 0u);
-                    pr = ok ? pr : 0.f;
-                }
-                s[r] = pr;
-                ds[r] = pr * (dp[r] - dv4[u4]);
-            }
-        }
-        const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
-        const bf16x8 dsf[2] = {pack8(ds, 0), pack8(ds, 1)};
-        // dv^T += dO^T P, dk^T += Q^T dS
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                dv_acc[db] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(dtf[db][t], pf[t], dv_acc[db], 0, 0, 0);
-                dk_acc[db] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf[db][t], dsf[t], dk_acc[db], 0, 0, 0);
-            }
-        if (u + 1 < T) {
-            if (u + 2 < T)
-                wait_vm<DMA_QD + 1, DMA_QD>(extra);
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-        }
-    }
+    for (int u = 0, S = 0; u < T; ++u, S = S == kStages - 1 ? 0 : S + 1)
+        body(S, u);
 
     if (kvalid) {
         float *dk = p.dk + ((int64_t)kvh * rows + row0 + kr) * D;
@@ -848,11 +883,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
 // ---------------------------------------------------------------------------
 // row statistics, plan and merge
 
-// D_i = dO_i . O_i in fp32, one wavefront per row.
+// D_i = dO_i . O_i in fp32, one wavefront per row, and the row's
+// log-sum-exp in the log2 domain (L_i log2 e) for the exp2 of the passes.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_drow_kernel(const __bf16 *__restrict__ out,
                                                        const __bf16 *__restrict__ dout,
-                                                       int64_t rows, float *__restrict__ drow)
+                                                       const float *__restrict__ lse,
+                                                       int64_t rows, float *__restrict__ drow,
+                                                       float *__restrict__ l2)
 {
     const int lane = threadIdx.x % kWave;
     const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -864,8 +902,10 @@ __global__ __launch_bounds__(256) void bwd_drow_kernel(const __bf16 *__restrict_
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
         s += __shfl_xor(s, off);
-    if (lane == 0)
+    if (lane == 0) {
         drow[r] = s;
+        l2[r] = lse[r] * kLog2e;
+    }
 }
 
 // Tiles of up to 128 entries inside each sub-bucket, one block per head.
@@ -919,19 +959,19 @@ __global__ __launch_bounds__(256) void bwd_gather_rows_kernel(
     reinterpret_cast<uint4 *>(db + r * D)[c] = *reinterpret_cast<const uint4 *>(b + src);
 }
 
-// The per-row scalars of the same copies: log-sum-exp and D per (query
+// The per-row scalars of the same copies: log2-domain log-sum-exp and D per (query
 // head, entry), group bits per (key/value head, entry).
 __global__ __launch_bounds__(256) void bwd_gather_scalars_kernel(
-    const float *__restrict__ lse, const float *__restrict__ drow,
+    const float *__restrict__ l2, const float *__restrict__ drow,
     const uint32_t *__restrict__ gmask, const int32_t *__restrict__ tokens, int hq, int hkv,
-    int ratio, int64_t n, int64_t E, float *__restrict__ glse, float *__restrict__ gd,
+    int ratio, int64_t n, int64_t E, float *__restrict__ gl2, float *__restrict__ gd,
     uint32_t *__restrict__ egm)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx < (int64_t)hq * E) {
         const int64_t h = idx / E, e = idx % E;
         const int64_t src = h * n + tokens[(h / ratio) * E + e];
-        glse[idx] = lse[src];
+        gl2[idx] = l2[src];
         gd[idx] = drow[src];
     }
     if (idx < (int64_t)hkv * E)
@@ -973,8 +1013,8 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(const float *__restrict_
 }
 
 struct BwdLayout {
-    size_t drow, dq_win, dk_win, dv_win, dq_grp, dk_grp, dv_grp, tiles, ntiles;
-    size_t kg, vg, qg, dog, glse, gd, egm, total;
+    size_t drow, l2, dq_win, dk_win, dv_win, dq_grp, dk_grp, dv_grp, tiles, ntiles;
+    size_t kg, vg, qg, dog, gl2, gd, egm, total;
     int max_tiles;
 };
 
@@ -991,6 +1031,7 @@ BwdLayout bwd_layout(const AttnShape &sh)
         return o;
     };
     L.drow = take(sizeof(float) * sh.hq * n);
+    L.l2 = take(sizeof(float) * sh.hq * n);
     L.dq_win = take(sizeof(float) * sh.hq * n * sh.d);
     L.dk_win = take(sizeof(float) * sh.hkv * n * sh.d);
     L.dv_win = take(sizeof(float) * sh.hkv * n * sh.d);
@@ -1004,7 +1045,7 @@ BwdLayout bwd_layout(const AttnShape &sh)
     L.vg = take(sizeof(__bf16) * sh.hkv * E * sh.d);
     L.qg = take(sizeof(__bf16) * sh.hq * E * sh.d);
     L.dog = take(sizeof(__bf16) * sh.hq * E * sh.d);
-    L.glse = take(sizeof(float) * sh.hq * E);
+    L.gl2 = take(sizeof(float) * sh.hq * E);
     L.gd = take(sizeof(float) * sh.hq * E);
     L.egm = take(sizeof(uint32_t) * sh.hkv * E);
     L.total = off;
@@ -1036,7 +1077,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
     p.k = static_cast<const __bf16 *>(k);
     p.v = static_cast<const __bf16 *>(v);
     p.dout = static_cast<const __bf16 *>(dout);
-    p.lse = lse;
+    p.l2 = reinterpret_cast<float *>(base + L.l2);
     p.drow = reinterpret_cast<float *>(base + L.drow);
     p.tokens = tokens;
     p.offsets = offsets;
@@ -1048,8 +1089,9 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
 
     const int64_t qrows = (int64_t)sh.hq * n;
     hipLaunchKernelGGL(bwd_drow_kernel<D>, dim3((unsigned)((qrows + 3) / 4)), dim3(256), 0, s,
-                       static_cast<const __bf16 *>(out), p.dout, qrows,
-                       reinterpret_cast<float *>(base + L.drow));
+                       static_cast<const __bf16 *>(out), p.dout, lse, qrows,
+                       reinterpret_cast<float *>(base + L.drow),
+                       reinterpret_cast<float *>(base + L.l2));
     hipLaunchKernelGGL(bwd_plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets,
                        num_subbuckets(sh.K), L.max_tiles,
                        reinterpret_cast<int4 *>(base + L.tiles),
@@ -1070,7 +1112,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
         __bf16 *vg = reinterpret_cast<__bf16 *>(base + L.vg);
         __bf16 *qg = reinterpret_cast<__bf16 *>(base + L.qg);
         __bf16 *dog = reinterpret_cast<__bf16 *>(base + L.dog);
-        float *glse = reinterpret_cast<float *>(base + L.glse);
+        float *gl2 = reinterpret_cast<float *>(base + L.gl2);
         float *gd = reinterpret_cast<float *>(base + L.gd);
         uint32_t *egm = reinterpret_cast<uint32_t *>(base + L.egm);
         const int64_t krows = (int64_t)sh.hkv * E, qrows_g = (int64_t)sh.hq * E;
@@ -1081,14 +1123,14 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
                            dim3((unsigned)((qrows_g * (D / 8) + 255) / 256)), dim3(256), 0, s,
                            p.q, p.dout, tokens, p.ratio, n, E, qrows_g, qg, dog);
         hipLaunchKernelGGL(bwd_gather_scalars_kernel, dim3((unsigned)((qrows_g + 255) / 256)),
-                           dim3(256), 0, s, lse, p.drow, gmask, tokens, sh.hq, sh.hkv, p.ratio,
-                           n, E, glse, gd, egm);
+                           dim3(256), 0, s, p.l2, p.drow, gmask, tokens, sh.hq, sh.hkv, p.ratio,
+                           n, E, gl2, gd, egm);
         BwdParams pg = p;
         pg.q = qg;
         pg.k = kg;
         pg.v = vg;
         pg.dout = dog;
-        pg.lse = glse;
+        pg.l2 = gl2;
         pg.drow = gd;
         pg.egm = egm;
         pg.dq = reinterpret_cast<float *>(base + L.dq_grp);
