@@ -51,7 +51,8 @@ constexpr int kBwdThreads = 256;  // 4 wavefronts
 constexpr int kBwdRows = 128;     // query rows (dq pass) or keys (dk/dv pass) per block
 constexpr int kQKeys = 64;        // dq pass: keys per staged tile
 constexpr int kKQueries = 32;     // dk/dv pass: queries per staged tile
-constexpr int kStages = 3;        // LDS ring depth
+constexpr int kStages = 3;        // LDS ring depth (dq pass)
+constexpr int kDkvStages = 4;     // LDS ring depth (dk/dv pass)
 
 struct BwdParams {
     int hq, hkv, ratio, K, topk, window;
@@ -196,19 +197,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
     const int m = lane % 32;
     const int h = lane / 32;
 
-    // ---- work item: (query head, tile)
-    int hq, kvh, slot;
-    if (GROUP) {
-        slot = blockIdx.x % p.max_tiles;
-        hq = blockIdx.x / p.max_tiles;
-        kvh = hq / p.ratio;
-        if (slot >= p.ntiles[kvh])
-            return;
-    } else {
-        slot = blockIdx.x % p.row_tiles;
-        hq = blockIdx.x / p.row_tiles;
-        kvh = hq / p.ratio;
-    }
+    // ---- work item: (key/value head, tile, query head of that key/value
+    // head), in that order, the query heads of one tile adjacent (they read
+    // the same key tiles); each XCD takes one contiguous range of the list
+    // (the grid is a multiple of 8 long), so neighbouring tiles share its L2
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int tiles_per_kvh = GROUP ? p.max_tiles : p.row_tiles;
+    if (b >= p.hkv * tiles_per_kvh * p.ratio)
+        return;
+    const int hr = b % p.ratio;
+    const int slot = (b / p.ratio) % tiles_per_kvh;
+    const int kvh = b / p.ratio / tiles_per_kvh;
+    const int hq = kvh * p.ratio + hr;
+    if (GROUP && slot >= p.ntiles[kvh])
+        return;
     int g = 0, mq = 0, tile_rows;
     int64_t row0;  // first query row (entry or position)
     if (GROUP) {
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         float dd[kWave];       // query D_i
         uint32_t gm[kWave];    // query group bits (group pass)
     };
-    __shared__ __attribute__((aligned(16))) Stage stg[kStages];
+    __shared__ __attribute__((aligned(16))) Stage stg[kDkvStages];
     __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
 
     const int lane = threadIdx.x % kWave;
@@ -528,17 +530,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     const int m = lane % 32;
     const int h = lane / 32;
 
-    // ---- work item: (key/value head, tile of 128 keys)
-    int kvh, slot;
-    if (GROUP) {
-        slot = blockIdx.x % p.max_tiles;
-        kvh = blockIdx.x / p.max_tiles;
-        if (slot >= p.ntiles[kvh])
-            return;
-    } else {
-        slot = blockIdx.x % p.row_tiles;
-        kvh = blockIdx.x / p.row_tiles;
-    }
+    // ---- work item: (key/value head, tile of 128 keys); each XCD takes one
+    // contiguous range (the grid is a multiple of 8 long), so neighbouring
+    // key tiles, which stream the same query tiles, share its L2
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int tiles_per_kvh = GROUP ? p.max_tiles : p.row_tiles;
+    if (b >= p.hkv * tiles_per_kvh)
+        return;
+    const int slot = b % tiles_per_kvh;
+    const int kvh = b / tiles_per_kvh;
+    if (GROUP && slot >= p.ntiles[kvh])
+        return;
     int g = 0, mk = 0, tile_keys;
     int64_t row0;
     if (GROUP) {
@@ -709,14 +711,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
 
     const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
 
-    // One query tile in stage S.  Order: S = Q K^T, then dP = dO V^T (each
-    // with its 16-byte fragments streamed two steps ahead and the transpose
-    // reads of dO^T / Q^T between the MFMAs), then P (exp2 and the key's
-    // query mask), dv^T += dO^T P while dS = P (dP - D) is formed, and
-    // dk^T += Q^T dS.
+    // One query tile in stage S, ordered so that the vector work overlaps
+    // the matrix cores: S = Q K^T (16-byte fragments streamed two steps
+    // ahead, the transpose reads of dO^T in between); the key's query mask;
+    // dP = dO V^T with P = exp2(S c - L log2 e) formed two elements per step
+    // (Q^T transpose reads in between); dv^T += dO^T P with dS = P (dP - D)
+    // formed two elements per step; dk^T += Q^T dS; then the DMA of tile
+    // u + 3 and the end-of-tile barrier.
     auto body = [&](int S, int u) {
-        if (u + 2 < T)
-            issue(S == 0 ? 2 : S - 1);
         int head_c, origin, valid, owner;
         it_next(it_comp, head_c, origin, valid, owner);
         (void)head_c;
@@ -732,17 +734,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         bf16x8 fr[3];
         fr[0] = lds16(ql, qoff[0]);
         fr[1] = lds16(ql, qoff[1]);
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) {  // i < KS: S step i; else dP step i - KS
+        auto stream = [&](int i) {  // fragment i + 2 of the 2 KS sequence (Q then dO)
             if (i + 2 < 2 * KS) {
                 const int n2 = i + 2;
                 fr[n2 % 3] = lds16(n2 < KS ? ql : dl, qoff[n2 % KS]);
             }
-            if (i < KS)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3], kf[i], s, 0, 0, 0);
-            else
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3], vf[i - KS], dp, 0, 0, 0);
-            // transpose reads: dO^T during S, Q^T during dP (2 DB fragments each)
+        };
+        auto transpose_reads = [&](int i) {  // dO^T during S, Q^T during dP
 #pragma unroll
             for (int q = 0; q < 2 * DB / KS; ++q) {
                 const int f = (i % KS) * (2 * DB / KS) + q;  // f / 2 = db, f % 2 = t
@@ -753,8 +751,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
                 else
                     qtf[db][t] = tr_frag(ql, tro[db][0] + step, tro[db][1] + step);
             }
+        };
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            stream(i);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3], kf[i], s, 0, 0, 0);
+            transpose_reads(i);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // log2-domain log-sum-exp of this lane's queries 16h .. 16h + 15
+        float4 l4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            l4[j] = reinterpret_cast<const float4 *>(stg[S].l2)[4 * h + j];
 
         // Queries this lane's key sees, as a bit mask over the tile: an
         // interval (window: 0 <= qpos - kpos < w; group: the queries ascend,
@@ -793,38 +802,46 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         }
         // this lane's 16 queries are 16h .. 16h + 15
         const uint32_t mh = qmask >> (16 * h);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // P = exp2(S c - L log2 e) on the mask (log-sum-exp and D read as
-        // vectors: queries 16h + 4j .. 16h + 4j + 3)
-        float dv4[16];
+        // dP chain; P of registers 2i, 2i + 1 after dP step i
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 l4 = reinterpret_cast<const float4 *>(stg[S].l2)[4 * h + j];
-            const float4 d4 = reinterpret_cast<const float4 *>(stg[S].dd)[4 * h + j];
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            dv4[4 * j] = d4.x;
-            dv4[4 * j + 1] = d4.y;
-            dv4[4 * j + 2] = d4.z;
-            dv4[4 * j + 3] = d4.w;
+        for (int i = 0; i < KS; ++i) {
+            stream(KS + i);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(KS + i) % 3], vf[i], dp, 0, 0, 0);
+            transpose_reads(KS + i);
 #pragma unroll
-            for (int u4 = 0; u4 < 4; ++u4) {
-                const int r = 4 * j + u4;
-                const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - lv[u4]);
+            for (int e = 0; e < 16 / KS; ++e) {
+                const int r = (16 / KS) * i + e;
+                const float l = r % 4 == 0 ? l4[r / 4].x : r % 4 == 1 ? l4[r / 4].y
+                              : r % 4 == 2 ? l4[r / 4].z : l4[r / 4].w;
+                const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - l);
                 const int keep = __builtin_amdgcn_sbfe((int)mh, r, 1);  // 0 or -1
                 s[r] = __int_as_float(__float_as_int(pr) & keep);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
-        // dv^T += dO^T P while dS = P (dP - D) is formed
+        float4 d4[4];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int j = 0; j < 4; ++j)
+            d4[j] = reinterpret_cast<const float4 *>(stg[S].dd)[4 * h + j];
+        __builtin_amdgcn_sched_barrier(0);
+        // dv^T += dO^T P; dS of registers 2i, 2i + 1 after MFMA i
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                dv_acc[db] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(dtf[db][t], pf[t], dv_acc[db], 0, 0, 0);
+        for (int i = 0; i < 2 * DB; ++i) {
+            const int db = i / 2, t = i % 2;
+            dv_acc[db] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(dtf[db][t], pf[t], dv_acc[db], 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dp[r] = s[r] * (dp[r] - dv4[r]);
+            for (int e = 0; e < 16 / (2 * DB); ++e) {
+                const int r = (16 / (2 * DB)) * i + e;
+                const float dd = r % 4 == 0 ? d4[r / 4].x : r % 4 == 1 ? d4[r / 4].y
+                               : r % 4 == 2 ? d4[r / 4].z : d4[r / 4].w;
+                dp[r] = s[r] * (dp[r] - dd);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         const bf16x8 dsf[2] = {pack8(dp, 0), pack8(dp, 1)};
         // dk^T += Q^T dS
 #pragma unroll
@@ -833,10 +850,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             for (int t = 0; t < 2; ++t)
                 dk_acc[db] =
                     __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf[db][t], dsf[t], dk_acc[db], 0, 0, 0);
-        // end of the tile: the next tile's loads have landed (the newest
-        // ones may still fly), every wave is done with this stage
+        // tile u + 3 into the stage tile u - 1 left (every wave passed the
+        // barrier after it), then: tile u + 1 landed (u + 2 and u + 3 may
+        // still fly) and every wave done with this stage
+        if (u + 3 < T)
+            issue(S == 0 ? kDkvStages - 1 : S - 1);
         if (u + 1 < T) {
-            if (u + 2 < T)
+            if (u + 3 < T)
+                wait_vm<2 * (DMA_QD + 1), 2 * DMA_QD>(extra);
+            else if (u + 2 < T)
                 wait_vm<DMA_QD + 1, DMA_QD>(extra);
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -850,16 +872,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     asm volatile("" ::: "memory");
-    if (T > 0)
-        issue(0);
-    if (T > 1)
-        issue(1);
-    if (T > 1)
+    for (int i = 0; i < kDkvStages - 1 && i < T; ++i)
+        issue(i);
+    if (T > 2)
+        wait_vm<2 * (DMA_QD + 1), 2 * DMA_QD>(extra);
+    else if (T > 1)
         wait_vm<DMA_QD + 1, DMA_QD>(extra);
     else
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __syncthreads();
-    for (int u = 0, S = 0; u < T; ++u, S = S == kStages - 1 ? 0 : S + 1)
+    for (int u = 0, S = 0; u < T; ++u, S = S == kDkvStages - 1 ? 0 : S + 1)
         body(S, u);
 
     if (kvalid) {
@@ -1052,6 +1074,12 @@ BwdLayout bwd_layout(const AttnShape &sh)
     return L;
 }
 
+// grid length rounded up to a whole number of blocks per XCD
+inline unsigned xcd_grid(int64_t blocks)
+{
+    return (unsigned)((blocks + kXcds - 1) / kXcds * kXcds);
+}
+
 template <int D>
 hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const void *v,
                         const void *out, const float *lse, const void *dout,
@@ -1101,9 +1129,9 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
     p.dq = reinterpret_cast<float *>(base + L.dq_win);
     p.dk = reinterpret_cast<float *>(base + L.dk_win);
     p.dv = reinterpret_cast<float *>(base + L.dv_win);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)(sh.hq * p.row_tiles)),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(xcd_grid(sh.hq * p.row_tiles)),
                        dim3(kBwdThreads), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3((unsigned)(sh.hkv * p.row_tiles)),
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3(xcd_grid(sh.hkv * p.row_tiles)),
                        dim3(kBwdThreads), 0, s, p);
 
     // group pass: rows gathered into bucket order first
@@ -1136,9 +1164,9 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
         pg.dq = reinterpret_cast<float *>(base + L.dq_grp);
         pg.dk = reinterpret_cast<float *>(base + L.dk_grp);
         pg.dv = reinterpret_cast<float *>(base + L.dv_grp);
-        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)(sh.hq * L.max_tiles)),
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(xcd_grid(sh.hq * L.max_tiles)),
                            dim3(kBwdThreads), 0, s, pg);
-        hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3((unsigned)(sh.hkv * L.max_tiles)),
+        hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3(xcd_grid(sh.hkv * L.max_tiles)),
                            dim3(kBwdThreads), 0, s, pg);
     }
     // merge
