@@ -47,11 +47,12 @@ namespace focus {
 namespace {
 using namespace attn;
 
-constexpr int kBwdThreads = 256;  // 4 wavefronts
+constexpr int kBwdThreads = 256;  // dk/dv pass: 4 wavefronts
+constexpr int kDqThreads = 512;   // dq pass: 8 wavefronts, 2 per SIMD
 constexpr int kBwdRows = 128;     // query rows (dq pass) or keys (dk/dv pass) per block
 constexpr int kQKeys = 64;        // dq pass: keys per staged tile
 constexpr int kKQueries = 32;     // dk/dv pass: queries per staged tile
-constexpr int kStages = 3;        // LDS ring depth (dq pass)
+constexpr int kDqStages = 4;      // LDS ring depth (dq pass)
 constexpr int kDkvStages = 4;     // LDS ring depth (dk/dv pass)
 
 struct BwdParams {
@@ -136,13 +137,13 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 &x, int t)
 // (R rows per load), lane l slot l % KCH of its row, so it fetches the chunk
 // the swizzle keeps there.  Rows at or past `valid` re-read row valid - 1 (the
 // kernels mask them), so no load leaves the tile's rows.
-template <int D, int ROWS>
+template <int D, int ROWS, int WAVES = kBwdThreads / kWave>
 struct TileDma {
     static constexpr int RB = D * 2;
     static constexpr int KCH = D / 8;
     static constexpr int R = 1024 / RB;
-    static constexpr int LOADS = ROWS / R / (kBwdThreads / kWave);
-    static_assert(LOADS >= 1 && LOADS * R * (kBwdThreads / kWave) == ROWS, "tile shape");
+    static constexpr int LOADS = ROWS / R / WAVES;
+    static_assert(LOADS >= 1 && LOADS * R * WAVES == ROWS, "tile shape");
     int row[LOADS];
     uint32_t cofs[LOADS];
     __device__ void init(int wave, int lane)
@@ -176,26 +177,30 @@ __device__ __forceinline__ void wait_vm(bool first)
 // dq pass
 
 template <int D, bool GROUP>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
 {
     constexpr int KS = D / 16;   // k-steps over d
     constexpr int DB = D / 32;   // 32-row blocks of d
     constexpr int RB = D * 2;    // bytes per row
-    using Dma = TileDma<D, kQKeys>;
+    constexpr int WAVES = kDqThreads / kWave;
+    using Dma = TileDma<D, kQKeys, WAVES>;
     struct Stage {
         char k[kQKeys * RB];
         char v[kQKeys * RB];
-        int pos[kWave];       // key positions
+        int pos[kWave];       // key positions (group pass)
         uint32_t gm[kWave];   // key group bits (group pass)
-        int desc[4];          // origin, valid keys, owner flag
     };
-    __shared__ __attribute__((aligned(16))) Stage stg[kStages];
+    __shared__ __attribute__((aligned(16))) Stage stg[kDqStages];
     __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int m = lane % 32;
     const int h = lane / 32;
+    // waves w and w + 4 (one SIMD) share the 32 queries of group w % 4 and
+    // take the two 32-key halves of every key tile
+    const int qg = wave & 3;
+    const int kh = wave >> 2;
 
     // ---- work item: (key/value head, tile, query head of that key/value
     // head), in that order, the query heads of one tile adjacent (they read
@@ -227,8 +232,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
     const int32_t *tok = GROUP ? p.tokens + (int64_t)kvh * p.E : nullptr;
     const uint32_t *egm = GROUP ? p.egm + (int64_t)kvh * p.E : nullptr;
 
-    // ---- this lane's query (column m of the wavefront's 32 rows)
-    const int qr = wave * 32 + m;
+    // ---- this lane's query (column m of the wave pair's 32 rows)
+    const int qr = qg * 32 + m;
     const bool qvalid = qr < tile_rows;
     const int qrc = qvalid ? qr : 0;
     const int qpos = GROUP ? tok[row0 + qrc] : (int)(row0 + qrc);
@@ -285,26 +290,40 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
         const int64_t j_last = row0 + tile_rows - 1;
         n_tiles = (int)((j_last - j_first) / kQKeys + 1);
     }
-    n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+    const int T = __builtin_amdgcn_readfirstlane(n_tiles);
+    // a group tile whose last key is at or before this wave's smallest
+    // qpos - w is taken whole by every query of the wave
+    int wave_lim = qvalid ? qpos - w : 0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        wave_lim = std::min(wave_lim, __shfl_xor(wave_lim, off));
+    wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
 
-    // tiles in order: (first row, valid keys, owner flag)
-    int it_sub = 0, it_tile = 0;
-    auto next_tile = [&](int &origin, int &valid, int &owner) {
+    // ---- tiles in order (wave-uniform iterator; the issue side runs three
+    // tiles ahead of the compute side)
+    struct It {
+        int sub, tile, cnt, start, owner;
+    };
+    auto it_next = [&](It &t, int &origin, int &valid, int &owner) {
         if (GROUP) {
-            while (it_tile * kQKeys >= sub_count[it_sub]) {
-                ++it_sub;
-                it_tile = 0;
+            while (t.tile * kQKeys >= t.cnt) {
+                ++t.sub;
+                t.tile = 0;
+                t.cnt = __builtin_amdgcn_readfirstlane(sub_count[t.sub]);
+                t.start = __builtin_amdgcn_readfirstlane(sub_start[t.sub]);
+                t.owner = __builtin_amdgcn_readfirstlane(sub_owner[t.sub]);
             }
-            valid = std::min(kQKeys, sub_count[it_sub] - it_tile * kQKeys);
-            owner = sub_owner[it_sub];
-            origin = sub_start[it_sub] + it_tile * kQKeys;
+            valid = std::min(kQKeys, t.cnt - t.tile * kQKeys);
+            origin = t.start + t.tile * kQKeys;
+            owner = t.owner;
         } else {
-            origin = (int)(j_first + (int64_t)it_tile * kQKeys);
+            origin = (int)(j_first + (int64_t)t.tile * kQKeys);
             valid = (int)std::min<int64_t>(kQKeys, p.n - origin);
             owner = 0;
         }
-        ++it_tile;
+        ++t.tile;
     };
+    It it_issue{-1, 0, 0, 0, 0}, it_comp{-1, 0, 0, 0, 0};
 
     // ---- staging: K and V tiles by LDS-DMA (all waves), key positions
     // (wave 0) and group bits (wave 1) of the group pass by 4-byte DMA
@@ -314,7 +333,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
     const bool extra = GROUP && wave < 2;
     auto issue = [&](int S) {
         int origin, valid, owner;
-        next_tile(origin, valid, owner);
+        it_next(it_issue, origin, valid, owner);
         const int64_t r0 = (int64_t)kvh * rows + origin;
         dma.issue(p.k + r0 * D, valid, lds_address(stg[S].k), wave);
         dma.issue(p.v + r0 * D, valid, lds_address(stg[S].v), wave);
@@ -325,11 +344,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
             else if (wave == 1)
                 dma4(egm + origin, lo, lds_address(stg[S].gm));
         }
-        if (threadIdx.x == 0) {
-            stg[S].desc[0] = origin;
-            stg[S].desc[1] = valid;
-            stg[S].desc[2] = owner;
-        }
     };
 
     f32x16 acc[DB];
@@ -339,168 +353,191 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams p)
         for (int r = 0; r < 16; ++r)
             acc[db][r] = 0.f;
 
-    // per-lane LDS byte offsets of the MFMA A fragments: K and V rows (row
-    // sigma(m) of each 32-key block, chunk 2ks+h; the second block is 32 rows
-    // on) and K^T by transpose reads (d = 32 db + m, keys 8h + 4s + 0..3 of
-    // each 16-key step; steps are 8 or 32 rows apart)
+    // per-lane LDS byte offsets in this wave's 32-key half: K and V rows
+    // (row 32 kh + sigma(m), chunk 2ks+h) and K^T by transpose reads
+    // (d = 32 db + m, keys 32 kh + 16h + 8t + 4s + 0..3; t adds 8 rows)
     uint32_t koff[KS], tro[DB][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        koff[ks] = rbyte<D>(sigma(m), 2 * ks + h);
+        koff[ks] = rbyte<D>(32 * kh + sigma(m), 2 * ks + h);
     {
         const int jj = lane & 15, gp = (lane >> 4) & 1;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const int row = 16 * h + 4 * s + (jj >> 2);
+                const int row = 32 * kh + 16 * h + 4 * s + (jj >> 2);
                 const int col = 32 * db + 16 * gp + 4 * (jj & 3);
                 tro[db][s] = rbyte<D>(row, col >> 3) + (uint32_t)(col & 7) * 2u;
             }
     }
 
     const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
-    const int T = n_tiles;
-    // the loads above have landed before any DMA is issued (the compiler's
-    // own wait tracking then has nothing left outstanding in the loop)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    asm volatile("" ::: "memory");
-    if (T > 0)
-        issue(0);
-    if (T > 1)
-        issue(1);
-    if (T > 1)
-        wait_vm<DMA_KV + 1, DMA_KV>(extra);
-    else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    __syncthreads();
 
-    for (int u = 0; u < T; ++u) {
-        const int S = u % kStages;
-        if (u + 2 < T)
-            issue((u + 2) % kStages);
+    // One key tile in stage S: S^T = K Q^T, then dP^T = V dO^T with
+    // P^T = exp2(S^T c - L log2 e) formed two elements per step (K^T
+    // transpose reads in between), dS^T = P^T (dP^T - D), dq^T += K^T dS^T,
+    // then the DMA of tile u + 3 and the end-of-tile barrier.
+    auto body = [&](int S, int u) {
+        int origin, valid, owner;
+        it_next(it_comp, origin, valid, owner);
         const char *kl = stg[S].k;
         const char *vl = stg[S].v;
-        const int *kpos_lds = stg[S].pos;
-        const uint32_t *kgm_lds = stg[S].gm;
-        const int origin = __builtin_amdgcn_readfirstlane(stg[S].desc[0]);
-        const int valid = __builtin_amdgcn_readfirstlane(stg[S].desc[1]);
-        const int owner = __builtin_amdgcn_readfirstlane(stg[S].desc[2]);
+        const int klast = GROUP ? stg[S].pos[valid - 1] : 0;
 
-        // The keys this lane's query takes form one interval [klo, khi] of
-        // the tile: in the window pass positions origin + kk with
-        // 0 <= qpos - kpos < w; in the group pass the keys ascend and the
-        // far ones (kpos <= qpos - w) are a prefix.
-        int klo = 0, khi = -1;
-        if (qvalid) {
-            if (GROUP) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            s[r] = dp[r] = 0.f;
+        bf16x8 ktf[DB][2];
+        bf16x8 fr[3];
+        fr[0] = lds16(kl, koff[0]);
+        fr[1] = lds16(kl, koff[1]);
+        auto stream = [&](int i) {  // fragment i + 2 of the 2 KS sequence (K then V)
+            if (i + 2 < 2 * KS) {
+                const int n2 = i + 2;
+                fr[n2 % 3] = lds16(n2 < KS ? kl : vl, koff[n2 % KS]);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            stream(i);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3], qf[i], s, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // Keys this lane's query takes, as a bit mask over the wave's half:
+        // an interval (window: 0 <= qpos - kpos < w; group: the keys ascend,
+        // the far ones kpos <= qpos - w are a prefix), in the group pass's
+        // owner tiles also without a lower shared group.
+        uint32_t kmask;
+        if (GROUP) {
+            int khi = valid - 1;
+            if (__builtin_amdgcn_readfirstlane(klast) > wave_lim && qvalid) {
                 const int lim = qpos - w;
-                if (lim >= kpos_lds[valid - 1]) {
-                    khi = valid - 1;
-                } else {
+                if (klast > lim) {
                     int lo = 0, hi = valid;
                     while (lo < hi) {
                         const int mid = (lo + hi) >> 1;
-                        if (kpos_lds[mid] <= lim)
+                        if (stg[S].pos[mid] <= lim)
                             lo = mid + 1;
                         else
                             hi = mid;
                     }
                     khi = lo - 1;
                 }
-            } else {
-                klo = std::max(0, qpos - origin - w + 1);
-                khi = std::min(qpos - origin, valid - 1);
             }
+            // keys 32 kh .. 32 kh + 31 of the tile, at or below khi
+            const int top = khi - 32 * kh;
+            kmask = !qvalid || top < 0 ? 0u : top >= 31 ? 0xffffffffu : ((2u << top) - 1u);
+            if (owner) {
+                for (int kk = 0; kk < 32; ++kk)
+                    if (32 * kh + kk < valid &&
+                        (qgm & stg[S].gm[32 * kh + kk] & low) != 0u)
+                        kmask &= ~(1u << kk);
+            }
+        } else {
+            const int lo = std::max(0, qpos - origin - w + 1) - 32 * kh;
+            const int hi = std::min(qpos - origin, valid - 1) - 32 * kh;
+            const int clo = std::max(lo, 0), chi = std::min(hi, 31);
+            kmask = qvalid && chi >= clo ? (uint32_t)((2ull << chi) - (1ull << clo)) : 0u;
         }
-        const bool full = !owner && __builtin_amdgcn_ballot_w64(!(klo <= 0 && khi >= kQKeys - 1)) == 0;
-
-        // S^T and dP^T for the two 32-key blocks.  LDS fragments are read a
-        // block ahead: block 1's between block 0's MFMAs (into the same
-        // registers), K^T's between block 1's; the fences keep that order.
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[kb][r] = dp[kb][r] = 0.f;
-        bf16x8 fa[KS], fb[KS], ktf[DB][4];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            fa[ks] = lds16(kl, koff[ks]);
-            fb[ks] = lds16(vl, koff[ks]);
-        }
+        // this lane's 16 keys are 16h .. 16h + 15 of the half
+        const uint32_t mh = kmask >> (16 * h);
         __builtin_amdgcn_sched_barrier(0);
+
+        // dP^T chain with P^T of registers 2i, 2i + 1 after step i, and the
+        // K^T fragments read in between
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks], qf[ks], s[0], 0, 0, 0);
-            dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks], dof[ks], dp[0], 0, 0, 0);
-            fa[ks] = lds16(kl, koff[ks] + 32 * RB);
-            fb[ks] = lds16(vl, koff[ks] + 32 * RB);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int i = 0; i < KS; ++i) {
+            stream(KS + i);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(KS + i) % 3], dof[i], dp, 0, 0, 0);
+            {
+                static_assert(2 * DB == KS, "one K^T fragment per step");
+                const int db = i / 2, t = i % 2;
+                const uint32_t step = (uint32_t)(8 * t * RB);
+                ktf[db][t] = tr_frag(kl, tro[db][0] + step, tro[db][1] + step);
+            }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks], qf[ks], s[1], 0, 0, 0);
-            dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks], dof[ks], dp[1], 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 4 * DB / KS; ++q) {
-                const int f = ks * (4 * DB / KS) + q;  // f / 4 = db, f % 4 = j = 2 kb + t
-                const int db = f / 4, j = f % 4;
-                const uint32_t step = (uint32_t)(32 * (j >> 1) + 8 * (j & 1)) * RB;
-                ktf[db][j] = tr_frag(kl, tro[db][0] + step, tro[db][1] + step);
+            for (int e = 0; e < 16 / KS; ++e) {
+                const int r = (16 / KS) * i + e;
+                const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - l2);
+                const int keep = __builtin_amdgcn_sbfe((int)mh, r, 1);  // 0 or -1
+                s[r] = __int_as_float(__float_as_int(pr) & keep);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         // dS^T = P^T (dP^T - D) as bf16 B fragments
-        bf16x8 dsf[2][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pr = __builtin_amdgcn_exp2f(s[kb][r] * p.c - l2);
-                if (!full) {
-                    const int kk = kb * 32 + 16 * h + r;
-                    bool ok = kk >= klo && kk <= khi;
-                    if (GROUP && owner)
-                        ok = ok && ((qgm & kgm_lds[kk] & low) == 0u);
-                    pr = ok ? pr : 0.f;
-                }
-                s[kb][r] = pr * (dp[kb][r] - dq_d);
-            }
-            dsf[kb][0] = pack8(s[kb], 0);
-            dsf[kb][1] = pack8(s[kb], 1);
-        }
+        for (int r = 0; r < 16; ++r)
+            dp[r] = s[r] * (dp[r] - dq_d);
+        const bf16x8 dsf[2] = {pack8(dp, 0), pack8(dp, 1)};
         // dq^T += K^T dS^T
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[db][j], dsf[j >> 1][j & 1],
-                                                                 acc[db], 0, 0, 0);
-        // end of the tile: the next tile's loads have landed (the newest
-        // ones may still fly), every wave is done with this stage
+            for (int t = 0; t < 2; ++t)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[db][t], dsf[t], acc[db], 0, 0, 0);
+        // tile u + 3 into the stage tile u - 1 left, then: tile u + 1
+        // landed (u + 2 and u + 3 may still fly), every wave done with S
+        if (u + 3 < T)
+            issue(S == 0 ? kDqStages - 1 : S - 1);
         if (u + 1 < T) {
-            if (u + 2 < T)
+            if (u + 3 < T)
+                wait_vm<2 * (DMA_KV + 1), 2 * DMA_KV>(extra);
+            else if (u + 2 < T)
                 wait_vm<DMA_KV + 1, DMA_KV>(extra);
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
-    }
+    };
 
-    // ---- store: lane (m, h), register r of block db holds dq[query m][d]
-    if (qvalid) {
-        float *dst = p.dq + ((int64_t)hq * rows + row0 + qr) * D;
+    // the loads above have landed before any DMA is issued (the compiler's
+    // own wait tracking then has nothing outstanding in the loop)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    for (int i = 0; i < kDqStages - 1 && i < T; ++i)
+        issue(i);
+    if (T > 2)
+        wait_vm<2 * (DMA_KV + 1), 2 * DMA_KV>(extra);
+    else if (T > 1)
+        wait_vm<DMA_KV + 1, DMA_KV>(extra);
+    else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+    for (int u = 0, S = 0; u < T; ++u, S = S == kDqStages - 1 ? 0 : S + 1)
+        body(S, u);
+
+    // ---- the two key halves' partial sums: the second wave of each pair
+    // leaves its accumulators in LDS (the stage ring is free after the
+    // barrier), the first adds them and stores.  Lane (m, h), register r of
+    // block db holds dq[query m][d].
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(&stg[0]);  // [4 pairs][DB][16][64 lanes]
+    if (kh == 1) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[((qg * DB + db) * 16 + r) * kWave + lane] = acc[db][r];
+    }
+    __syncthreads();
+    if (kh == 0 && qvalid) {
+        float *dst = p.dq + ((int64_t)hq * rows + row0 + qr) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[db][r] += red[((qg * DB + db) * 16 + r) * kWave + lane];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * h) =
                     make_float4(acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale,
                                 acc[db][4 * j + 2] * p.scale, acc[db][4 * j + 3] * p.scale);
+        }
     }
 }
 
@@ -1130,7 +1167,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
     p.dk = reinterpret_cast<float *>(base + L.dk_win);
     p.dv = reinterpret_cast<float *>(base + L.dv_win);
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(xcd_grid(sh.hq * p.row_tiles)),
-                       dim3(kBwdThreads), 0, s, p);
+                       dim3(kDqThreads), 0, s, p);
     hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3(xcd_grid(sh.hkv * p.row_tiles)),
                        dim3(kBwdThreads), 0, s, p);
 
@@ -1165,7 +1202,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
         pg.dk = reinterpret_cast<float *>(base + L.dk_grp);
         pg.dv = reinterpret_cast<float *>(base + L.dv_grp);
         hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(xcd_grid(sh.hq * L.max_tiles)),
-                           dim3(kBwdThreads), 0, s, pg);
+                           dim3(kDqThreads), 0, s, pg);
         hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3(xcd_grid(sh.hkv * L.max_tiles)),
                            dim3(kBwdThreads), 0, s, pg);
     }
