@@ -173,6 +173,34 @@ __device__ __forceinline__ void wait_vm(bool first)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(B));
 }
 
+// "s_waitcnt vmcnt(n) lgkmcnt(0)" for a wave-uniform n in 0..47 (larger n
+// waits for 47, which is only more conservative)
+__device__ __forceinline__ void wait_vm_n(int n)
+{
+#define FOCUS_WAIT_CASE(k) \
+    case k:                \
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(k)); \
+        break;
+    switch (n) {
+        FOCUS_WAIT_CASE(0) FOCUS_WAIT_CASE(1) FOCUS_WAIT_CASE(2) FOCUS_WAIT_CASE(3)
+        FOCUS_WAIT_CASE(4) FOCUS_WAIT_CASE(5) FOCUS_WAIT_CASE(6) FOCUS_WAIT_CASE(7)
+        FOCUS_WAIT_CASE(8) FOCUS_WAIT_CASE(9) FOCUS_WAIT_CASE(10) FOCUS_WAIT_CASE(11)
+        FOCUS_WAIT_CASE(12) FOCUS_WAIT_CASE(13) FOCUS_WAIT_CASE(14) FOCUS_WAIT_CASE(15)
+        FOCUS_WAIT_CASE(16) FOCUS_WAIT_CASE(17) FOCUS_WAIT_CASE(18) FOCUS_WAIT_CASE(19)
+        FOCUS_WAIT_CASE(20) FOCUS_WAIT_CASE(21) FOCUS_WAIT_CASE(22) FOCUS_WAIT_CASE(23)
+        FOCUS_WAIT_CASE(24) FOCUS_WAIT_CASE(25) FOCUS_WAIT_CASE(26) FOCUS_WAIT_CASE(27)
+        FOCUS_WAIT_CASE(28) FOCUS_WAIT_CASE(29) FOCUS_WAIT_CASE(30) FOCUS_WAIT_CASE(31)
+        FOCUS_WAIT_CASE(32) FOCUS_WAIT_CASE(33) FOCUS_WAIT_CASE(34) FOCUS_WAIT_CASE(35)
+        FOCUS_WAIT_CASE(36) FOCUS_WAIT_CASE(37) FOCUS_WAIT_CASE(38) FOCUS_WAIT_CASE(39)
+        FOCUS_WAIT_CASE(40) FOCUS_WAIT_CASE(41) FOCUS_WAIT_CASE(42) FOCUS_WAIT_CASE(43)
+        FOCUS_WAIT_CASE(44) FOCUS_WAIT_CASE(45) FOCUS_WAIT_CASE(46)
+    default:
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(47));
+        break;
+    }
+#undef FOCUS_WAIT_CASE
+}
+
 // ---------------------------------------------------------------------------
 // dq pass
 
@@ -442,31 +470,43 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
             const int clo = std::max(lo, 0), chi = std::min(hi, 31);
             kmask = qvalid && chi >= clo ? (uint32_t)((2ull << chi) - (1ull << clo)) : 0u;
         }
-        // this lane's 16 keys are 16h .. 16h + 15 of the half
+        // this lane's 16 keys are 16h .. 16h + 15 of the half; a wave whose
+        // queries all take the whole half skips the mask
         const uint32_t mh = kmask >> (16 * h);
+        const bool full = __builtin_amdgcn_ballot_w64(kmask != 0xffffffffu) == 0;
         __builtin_amdgcn_sched_barrier(0);
 
         // dP^T chain with P^T of registers 2i, 2i + 1 after step i, and the
         // K^T fragments read in between
+        auto dp_chain = [&](auto masked) {
 #pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            stream(KS + i);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(KS + i) % 3], dof[i], dp, 0, 0, 0);
-            {
-                static_assert(2 * DB == KS, "one K^T fragment per step");
-                const int db = i / 2, t = i % 2;
-                const uint32_t step = (uint32_t)(8 * t * RB);
-                ktf[db][t] = tr_frag(kl, tro[db][0] + step, tro[db][1] + step);
-            }
+            for (int i = 0; i < KS; ++i) {
+                stream(KS + i);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(KS + i) % 3], dof[i], dp, 0, 0, 0);
+                {
+                    static_assert(2 * DB == KS, "one K^T fragment per step");
+                    const int db = i / 2, t = i % 2;
+                    const uint32_t step = (uint32_t)(8 * t * RB);
+                    ktf[db][t] = tr_frag(kl, tro[db][0] + step, tro[db][1] + step);
+                }
 #pragma unroll
-            for (int e = 0; e < 16 / KS; ++e) {
-                const int r = (16 / KS) * i + e;
-                const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - l2);
-                const int keep = __builtin_amdgcn_sbfe((int)mh, r, 1);  // 0 or -1
-                s[r] = __int_as_float(__float_as_int(pr) & keep);
+                for (int e = 0; e < 16 / KS; ++e) {
+                    const int r = (16 / KS) * i + e;
+                    const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - l2);
+                    if constexpr (decltype(masked)::value) {
+                        const int keep = __builtin_amdgcn_sbfe((int)mh, r, 1);  // 0 or -1
+                        s[r] = __int_as_float(__float_as_int(pr) & keep);
+                    } else {
+                        s[r] = pr;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        };
+        if (full)
+            dp_chain(std::false_type{});
+        else
+            dp_chain(std::true_type{});
         // dS^T = P^T (dP^T - D) as bf16 B fragments
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -701,6 +741,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     dma.init(wave, lane);
     constexpr int DMA_QD = 2 * Dma::LOADS;
     const bool extra = GROUP ? true : (wave == 1 || wave == 2);
+    const int per_tile = DMA_QD + (extra ? 1 : 0);  // this wave's loads per tile
+    constexpr int AHEAD = kDkvStages - 1;             // tiles in flight ahead
     auto issue = [&](int S) {
         int head, origin, valid, owner;
         it_next(it_issue, head, origin, valid, owner);
@@ -887,18 +929,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             for (int t = 0; t < 2; ++t)
                 dk_acc[db] =
                     __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtf[db][t], dsf[t], dk_acc[db], 0, 0, 0);
-        // tile u + 3 into the stage tile u - 1 left (every wave passed the
-        // barrier after it), then: tile u + 1 landed (u + 2 and u + 3 may
-        // still fly) and every wave done with this stage
-        if (u + 3 < T)
+        // tile u + AHEAD into the stage tile u - 1 left (every wave passed
+        // the barrier after it), then: tile u + 1 landed (the tiles after it
+        // may still fly) and every wave done with this stage
+        if (u + AHEAD < T)
             issue(S == 0 ? kDkvStages - 1 : S - 1);
         if (u + 1 < T) {
-            if (u + 3 < T)
-                wait_vm<2 * (DMA_QD + 1), 2 * DMA_QD>(extra);
-            else if (u + 2 < T)
-                wait_vm<DMA_QD + 1, DMA_QD>(extra);
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+            wait_vm_n((std::min(T - 1, u + AHEAD) - u - 1) * per_tile);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
@@ -909,14 +946,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     asm volatile("" ::: "memory");
-    for (int i = 0; i < kDkvStages - 1 && i < T; ++i)
+    for (int i = 0; i < AHEAD && i < T; ++i)
         issue(i);
-    if (T > 2)
-        wait_vm<2 * (DMA_QD + 1), 2 * DMA_QD>(extra);
-    else if (T > 1)
-        wait_vm<DMA_QD + 1, DMA_QD>(extra);
-    else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    wait_vm_n((std::min(T, AHEAD) - 1) * per_tile);
     __syncthreads();
     for (int u = 0, S = 0; u < T; ++u, S = S == kDkvStages - 1 ? 0 : S + 1)
         body(S, u);
