@@ -18,13 +18,17 @@
 // forward's partition carries over: pairs with i - j < w go to the window
 // kernels, the others to the group kernels of the lowest group the two tokens
 // share.  Two passes per partition, neither with atomics:
-//   * dq pass (query-major, like the forward): a block owns 128 query rows
-//     and walks their key tiles; S^T = K Q^T and dP^T = V dO^T put one query
-//     per lane column, dS^T feeds dq^T += K^T dS^T from registers.
-//   * dk/dv pass (key-major): a block owns 128 keys with K and V in
-//     registers and walks the query tiles that see them, for every query head
-//     of the key/value head; S = Q K^T and dP = dO V^T put one key per lane
-//     column, P and dS feed dv^T += dO^T P and dk^T += Q^T dS.
+//   * dq pass (query-major, like the forward): a block of 8 wavefronts owns
+//     128 query rows and walks their 64-key tiles, the two wavefronts of a
+//     SIMD sharing 32 queries and splitting each tile's keys in halves;
+//     S^T = K Q^T and dP^T = V dO^T put one query per lane column, dS^T
+//     feeds dq^T += K^T dS^T from registers, and the halves' sums are added
+//     at the end.
+//   * dk/dv pass (key-major): a block of 4 wavefronts owns 128 keys with K
+//     and V in registers and walks the 32-query tiles that see them, for
+//     every query head of the key/value head; S = Q K^T and dP = dO V^T put
+//     one key per lane column, P and dS feed dv^T += dO^T P and
+//     dk^T += Q^T dS.
 // Each pass writes fp32 partials (per position for the window, per bucket
 // entry for the groups); a merge kernel adds a row's window part and its k
 // group parts and rounds to bf16.
@@ -32,7 +36,7 @@
 // Data movement.  The group passes read copies of their rows gathered into
 // bucket (entry) order by a prepare kernel, so that every staged tile, in
 // both partitions, is a run of consecutive rows.  Tiles go straight from HBM
-// into a three-stage LDS ring by LDS-DMA (two tiles in flight while one is
+// into a four-stage LDS ring by LDS-DMA (three tiles in flight while one is
 // computed; one barrier per tile), row-major with 16-byte chunks XOR-swizzled.
 // v_mfma_f32_32x32x16_bf16 needs both operands contiguous along the
 // reduction index: the row operands (K and V in the dq pass, Q and dO in the
