@@ -256,6 +256,64 @@ def run_sweep(steps: int, warmup: int) -> int:
     return 0
 
 
+# thelatestinai.com Table 7 (K = 4, PG-19; hardware and context unstated):
+# speed-up and pairs retained per top-k, GPT-2 124M and Mistral 7B
+TABLE7_PAGES = {1: {"speedup": 4.0, "pairs_gpt2": 0.26, "pairs_mistral": 0.25},
+                2: {"speedup": 2.0, "pairs_gpt2": 0.60, "pairs_mistral": 0.73},
+                3: {"speedup": 1.3, "pairs_gpt2": 1.00, "pairs_mistral": None},
+                4: {"speedup": 1.0, "pairs_gpt2": 1.00, "pairs_mistral": None}}
+
+
+def run_topk_sweep(n: int, steps: int, warmup: int) -> int:
+    """The top-k trade-off at K = 4: the Focus step for top-k = 1..4 against
+    our dense causal kernel on the 7B-style GQA layer (w = 1024), with the
+    fraction of causal pairs each keeps; one JSON object, a row per top-k.
+    The routing vectors are one draw shared by every top-k."""
+    import torch
+
+    from centroid_gated_sparse_amd import focus as F
+    from centroid_gated_sparse_amd.workloads import (TABLE7_TOPK, qkv_inputs, routing_inputs,
+                                                     seed_for, table7_workload)
+
+    F.lib()
+    base = table7_workload(n, 1)
+    seed = seed_for(base.name)
+    q, k, v = qkv_inputs(base, seed, "cuda")
+    c, r, _ = routing_inputs(base, seed)
+    rt = torch.from_numpy(r).cuda()
+    ct = torch.from_numpy(c).cuda()
+    dws = torch.empty(max(F.focus_dense_workspace_bytes(F.FOCUS_BF16, base.hkv, n, base.d), 16),
+                      dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((base.hq, n), dtype=torch.float32, device="cuda")
+    dense_ms = timed_ms(lambda: F.focus_dense_causal_fwd(q, k, v, base.scale, out, lse, dws),
+                        1, steps)
+    del dws, out, lse
+    dense_pairs = base.hq * n * (n + 1) // 2
+    rows = []
+    for topk in TABLE7_TOPK:
+        wl = table7_workload(n, topk)
+        step, b = make_step(F, wl, q, k, v, rt, ct)
+        focus_ms = timed_ms(step, warmup, steps)
+        surv = int(surviving_pairs(b["groups"].cpu().numpy(), wl.K, wl.window).sum()) * (
+            wl.hq // wl.hkv)
+        rows.append({
+            "topk": topk, "K": wl.K, "n": n, "window": wl.window,
+            "focus_ms": focus_ms, "dense_ms": dense_ms,
+            "speedup_vs_dense": dense_ms / focus_ms,
+            "pairs_kept_vs_dense": surv / dense_pairs,
+            "focus_tflops_surviving": 4.0 * wl.d * surv / (focus_ms / 1e3) / 1e12,
+            "pages_table7": TABLE7_PAGES[topk],
+        })
+        log(f"topk sweep: n={n} top-{topk} focus {focus_ms:.2f} ms dense {dense_ms:.2f} ms "
+            f"-> {dense_ms / focus_ms:.2f}x, pairs kept {surv / dense_pairs:.3f}")
+        del step, b
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "table7_topk", "model": "gqa7b 32/8 heads d128 bf16",
+                      "rows": rows}), flush=True)
+    return 0
+
+
 # fp32 vector rate of one MI355X without packed or fused forms: 256 CUs x
 # 4 SIMDs x 16 lanes, one operation per lane per clock at 2.4 GHz.
 PEAK_F32_VALU_TFLOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -411,6 +469,8 @@ def main() -> int:
                     help="seconds of oracle attention time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--topk-sweep", type=int, default=0, metavar="N",
+                    help="the top-k trade-off at K = 4 (top-1..4) on an N-token layer")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the Table 6 context sweep (Focus vs our dense kernel)")
     ap.add_argument("--train-forward", action="store_true",
@@ -442,6 +502,8 @@ def main() -> int:
 
     if args.sweep:
         return run_sweep(args.steps, args.warmup)
+    if args.topk_sweep:
+        return run_topk_sweep(args.topk_sweep, args.steps, args.warmup)
     if args.project:
         return run_project(max(args.steps, 5), args.warmup)
     if args.backward:

@@ -84,6 +84,15 @@ def table6_workload(n: int, K: int) -> Workload:
                     qkv_std=1.0 / math.sqrt(128))
 
 
+# the top-k trade-off at K = 4 (thelatestinai.com Table 7), on the same layer
+TABLE7_TOPK = (1, 2, 3, 4)
+
+
+def table7_workload(n: int, topk: int) -> Workload:
+    return Workload(f"table7_gqa7b_n{n}_top{topk}", n, 32, 8, 128, 4, topk, 1024, "bf16",
+                    qkv_std=1.0 / math.sqrt(128))
+
+
 def seed_for(name: str) -> int:
     if name in WORKLOAD_ORDER:
         return 1000 + WORKLOAD_ORDER.index(name)
@@ -91,6 +100,8 @@ def seed_for(name: str) -> int:
         for j, K in enumerate(TABLE6_GROUPS):
             if name == f"table6_gqa7b_n{n}_k{K}":
                 return 2000 + 10 * i + j
+    if name.startswith("table7_gqa7b_n"):  # one routing draw per n, shared by every top-k
+        return 3000 + int(name[len("table7_gqa7b_n"):].split("_")[0]) % 997
     return 4242
 
 
