@@ -5,6 +5,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace focus {
@@ -61,6 +63,17 @@ focus_status check_attn(const void *q, const void *k, const void *v, focus_dtype
         return unsupported("head dim must be 64 or 128");
     return FOCUS_OK;
 }
+
+// With 2 top-k > K any two tokens' group sets intersect (pigeonhole), so
+// A(i) is every j <= i and the layer is causal attention.  The window pass
+// then takes every pair (window = n) and the group pass finds none: the same
+// set, evaluated once, without the group pass visiting pairs in several
+// buckets to mask all but the lowest.
+int64_t all_pairs_window(int32_t K, int32_t topk, int64_t n, int64_t window)
+{
+    return 2 * (int64_t)topk > K ? std::max(window, n) : window;
+}
+
 }  // namespace
 
 void set_error(const char *fmt, ...)
@@ -218,7 +231,7 @@ focus_status focus_attn_fwd_part(const void *q, const void *k, const void *v, fo
     FOCUS_REQUIRE(n * (int64_t)topk <= INT32_MAX, "n*topk exceeds int32");
     FOCUS_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
     FOCUS_REQUIRE(parts >= 1 && parts <= FOCUS_PART_ALL, "parts=%d", parts);
-    AttnShape sh{dt, Hq, Hkv, d, K, topk, n, window, scale};
+    AttnShape sh{dt, Hq, Hkv, d, K, topk, n, all_pairs_window(K, topk, n, window), scale};
     const size_t need = attn_workspace_bytes(sh);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return short_workspace(workspace_bytes, need);
@@ -281,7 +294,7 @@ focus_status focus_attn_bwd(const void *q, const void *k, const void *v, const v
     FOCUS_REQUIRE(window >= 0, "window=%lld", (long long)window);
     FOCUS_REQUIRE(n * (int64_t)topk <= INT32_MAX, "n*topk exceeds int32");
     FOCUS_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
-    AttnShape sh{dt, Hq, Hkv, d, K, topk, n, window, scale};
+    AttnShape sh{dt, Hq, Hkv, d, K, topk, n, all_pairs_window(K, topk, n, window), scale};
     const size_t need = attn_bwd_workspace_bytes(sh);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return short_workspace(workspace_bytes, need);

@@ -159,7 +159,9 @@ focus_status focus_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K
  *
  * Each surviving pair is evaluated exactly once: pairs with i - j < w by the
  * window kernel, the others by the group kernel of the lowest group the two
- * tokens share; the parts are joined by a log-sum-exp merge.
+ * tokens share; the parts are joined by a log-sum-exp merge.  When
+ * 2 topk > K any two tokens share a group, A(i) is every j <= i, and the
+ * window kernel takes every pair (as if w = n); focus_attn_bwd does the same.
  *
  *   q           [Hq, n, d]  in dt (FOCUS_BF16 or FOCUS_F32)
  *   k, v        [Hkv, n, d] in dt
