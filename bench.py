@@ -264,11 +264,12 @@ TABLE7_PAGES = {1: {"speedup": 4.0, "pairs_gpt2": 0.26, "pairs_mistral": 0.25},
                 4: {"speedup": 1.0, "pairs_gpt2": 1.00, "pairs_mistral": None}}
 
 
-def run_topk_sweep(n: int, steps: int, warmup: int) -> int:
-    """The top-k trade-off at K = 4: the Focus step for top-k = 1..4 against
-    our dense causal kernel on the 7B-style GQA layer (w = 1024), with the
-    fraction of causal pairs each keeps; one JSON object, a row per top-k.
-    The routing vectors are one draw shared by every top-k."""
+def run_topk_sweep(n: int, K: int, steps: int, warmup: int) -> int:
+    """The top-k trade-off (Table 7 uses K = 4): the Focus step for
+    top-k = 1..4 against our dense causal kernel on the 7B-style GQA layer
+    (w = 1024), with the fraction of causal pairs each keeps; one JSON
+    object, a row per top-k.  The routing vectors are one draw shared by
+    every top-k."""
     import torch
 
     from centroid_gated_sparse_amd import focus as F
@@ -276,7 +277,7 @@ def run_topk_sweep(n: int, steps: int, warmup: int) -> int:
                                                      seed_for, table7_workload)
 
     F.lib()
-    base = table7_workload(n, 1)
+    base = table7_workload(n, 1, K)
     seed = seed_for(base.name)
     q, k, v = qkv_inputs(base, seed, "cuda")
     c, r, _ = routing_inputs(base, seed)
@@ -292,7 +293,7 @@ def run_topk_sweep(n: int, steps: int, warmup: int) -> int:
     dense_pairs = base.hq * n * (n + 1) // 2
     rows = []
     for topk in TABLE7_TOPK:
-        wl = table7_workload(n, topk)
+        wl = table7_workload(n, topk, K)
         step, b = make_step(F, wl, q, k, v, rt, ct)
         focus_ms = timed_ms(step, warmup, steps)
         surv = int(surviving_pairs(b["groups"].cpu().numpy(), wl.K, wl.window).sum()) * (
@@ -303,13 +304,13 @@ def run_topk_sweep(n: int, steps: int, warmup: int) -> int:
             "speedup_vs_dense": dense_ms / focus_ms,
             "pairs_kept_vs_dense": surv / dense_pairs,
             "focus_tflops_surviving": 4.0 * wl.d * surv / (focus_ms / 1e3) / 1e12,
-            "pages_table7": TABLE7_PAGES[topk],
+            "pages_table7": TABLE7_PAGES[topk] if K == 4 else None,
         })
         log(f"topk sweep: n={n} top-{topk} focus {focus_ms:.2f} ms dense {dense_ms:.2f} ms "
             f"-> {dense_ms / focus_ms:.2f}x, pairs kept {surv / dense_pairs:.3f}")
         del step, b
         torch.cuda.empty_cache()
-    print(json.dumps({"sweep": "table7_topk", "model": "gqa7b 32/8 heads d128 bf16",
+    print(json.dumps({"sweep": "table7_topk", "K": K, "model": "gqa7b 32/8 heads d128 bf16",
                       "rows": rows}), flush=True)
     return 0
 
@@ -470,7 +471,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--topk-sweep", type=int, default=0, metavar="N",
-                    help="the top-k trade-off at K = 4 (top-1..4) on an N-token layer")
+                    help="the top-k trade-off (top-1..4) on an N-token layer")
+    ap.add_argument("--topk-K", type=int, default=4, help="centroids for --topk-sweep")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the Table 6 context sweep (Focus vs our dense kernel)")
     ap.add_argument("--train-forward", action="store_true",
@@ -503,7 +505,7 @@ def main() -> int:
     if args.sweep:
         return run_sweep(args.steps, args.warmup)
     if args.topk_sweep:
-        return run_topk_sweep(args.topk_sweep, args.steps, args.warmup)
+        return run_topk_sweep(args.topk_sweep, args.topk_K, args.steps, args.warmup)
     if args.project:
         return run_project(max(args.steps, 5), args.warmup)
     if args.backward:

@@ -88,9 +88,9 @@ def table6_workload(n: int, K: int) -> Workload:
 TABLE7_TOPK = (1, 2, 3, 4)
 
 
-def table7_workload(n: int, topk: int) -> Workload:
-    return Workload(f"table7_gqa7b_n{n}_top{topk}", n, 32, 8, 128, 4, topk, 1024, "bf16",
-                    qkv_std=1.0 / math.sqrt(128))
+def table7_workload(n: int, topk: int, K: int = 4) -> Workload:
+    name = f"table7_gqa7b_n{n}_top{topk}" + ("" if K == 4 else f"_k{K}")
+    return Workload(name, n, 32, 8, 128, K, topk, 1024, "bf16", qkv_std=1.0 / math.sqrt(128))
 
 
 def seed_for(name: str) -> int:
