@@ -137,6 +137,8 @@ SMALL = [
     W("bf16_n63", 63, 2, 2, 64, 4, 2, 5, "bf16"),
     W("bf16_n65", 65, 4, 4, 128, 4, 1, 70, "bf16"),
     W("bf16_n257_w1", 257, 4, 4, 64, 4, 1, 1, "bf16"),
+    # 2 top-k > K: every pair shares a group, all of them in the window pass
+    W("bf16_d128_k4_top3_allpairs", 700, 4, 2, 128, 4, 3, 40, "bf16"),
 ]
 
 
