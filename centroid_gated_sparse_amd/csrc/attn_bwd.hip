@@ -560,6 +560,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
     // barrier), the first adds them and stores.  Lane (m, h), register r of
     // block db holds dq[query m][d].
     __syncthreads();
+    static_assert(sizeof(stg) >= sizeof(float) * 4 * DB * 16 * kWave, "reduction fits the ring");
     float *red = reinterpret_cast<float *>(&stg[0]);  // [4 pairs][DB][16][64 lanes]
     if (kh == 1) {
 #pragma unroll
