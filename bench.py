@@ -197,6 +197,25 @@ def timed_ms(fn, warmup: int, steps: int) -> float:
     return float(np.median(ts))
 
 
+def graph_of(fn):
+    """fn() captured once into a HIP graph (torch's CUDAGraph on ROCm, on a
+    side stream of default priority); returns the graph, whose replay()
+    launches the same kernels on the same buffers."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # the first launches happen outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 # Speed against full attention that the pages report in Table 6 (H100,
 # FlashAttention on both sides; shape and window not stated): context
 # only, printed next to this sweep's own ratio.
@@ -223,8 +242,14 @@ def run_sweep(steps: int, warmup: int) -> int:
                               16), dtype=torch.uint8, device="cuda")
         out = torch.empty_like(q)
         lse = torch.empty((base.hq, n), dtype=torch.float32, device="cuda")
-        dense_ms = timed_ms(lambda: F.focus_dense_causal_fwd(q, k, v, base.scale, out, lse, dws),
-                            1, max(1, min(steps, 2) if n > 300000 else steps))
+        dense_fn = lambda: F.focus_dense_causal_fwd(q, k, v, base.scale, out, lse, dws)  # noqa: E731
+        dense_ms = timed_ms(dense_fn, 1, max(1, min(steps, 2) if n > 300000 else steps))
+        # launch-bound short contexts: the same work replayed from a HIP graph
+        dense_graph_ms = None
+        if n <= 65536:
+            dg = graph_of(dense_fn)
+            dense_graph_ms = timed_ms(dg.replay, 1, steps)
+            del dg
         del dws, out, lse
         for K in TABLE6_GROUPS:
             wl = table6_workload(n, K)
@@ -233,6 +258,11 @@ def run_sweep(steps: int, warmup: int) -> int:
             ct = torch.from_numpy(c).cuda()
             step, b = make_step(F, wl, q, k, v, rt, ct)
             focus_ms = timed_ms(step, warmup, steps)
+            focus_graph_ms = None
+            if dense_graph_ms is not None:
+                fg = graph_of(step)
+                focus_graph_ms = timed_ms(fg.replay, warmup, steps)
+                del fg
             surv = int(surviving_pairs(b["groups"].cpu().numpy(), K, wl.window).sum()) * (
                 wl.hq // wl.hkv)
             dense_pairs = wl.hq * n * (n + 1) // 2
@@ -240,6 +270,9 @@ def run_sweep(steps: int, warmup: int) -> int:
                 "n": n, "K": K, "topk": wl.topk, "window": wl.window,
                 "focus_ms": focus_ms, "dense_ms": dense_ms,
                 "speedup_vs_dense": dense_ms / focus_ms,
+                "focus_graph_ms": focus_graph_ms, "dense_graph_ms": dense_graph_ms,
+                "speedup_vs_dense_graph": (dense_graph_ms / focus_graph_ms
+                                           if focus_graph_ms else None),
                 "focus_tokens_per_s": n / (focus_ms / 1e3),
                 "pairs_kept_vs_dense": surv / dense_pairs,
                 "focus_tflops_surviving": 4.0 * wl.d * surv / (focus_ms / 1e3) / 1e12,
@@ -247,7 +280,9 @@ def run_sweep(steps: int, warmup: int) -> int:
                 "pages_table6_speedup_h100": TABLE6_PAGES[K][i],
             })
             log(f"sweep: n={n} K={K} focus {focus_ms:.2f} ms dense {dense_ms:.2f} ms "
-                f"-> {dense_ms / focus_ms:.2f}x")
+                f"-> {dense_ms / focus_ms:.2f}x" + (
+                    f"; graphs {focus_graph_ms:.3f} / {dense_graph_ms:.3f} ms -> "
+                    f"{dense_graph_ms / focus_graph_ms:.2f}x" if focus_graph_ms else ""))
             del step, b, rt, ct
         del q, k, v
         torch.cuda.empty_cache()
