@@ -139,6 +139,7 @@ SMALL = [
     W("bf16_n257_w1", 257, 4, 4, 64, 4, 1, 1, "bf16"),
     # 2 top-k > K: every pair shares a group, all of them in the window pass
     W("bf16_d128_k4_top3_allpairs", 700, 4, 2, 128, 4, 3, 40, "bf16"),
+    W("f32_d64_k3_top2_allpairs", 350, 2, 1, 64, 3, 2, 16, "f32"),
 ]
 
 
