@@ -167,16 +167,6 @@ struct TileDma {
     }
 };
 
-// "s_waitcnt vmcnt(n) lgkmcnt(0)" for a wave-uniform n known to be a or b
-template <int A, int B>
-__device__ __forceinline__ void wait_vm(bool first)
-{
-    if (first)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(A));
-    else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(B));
-}
-
 // "s_waitcnt vmcnt(n) lgkmcnt(0)" for a wave-uniform n in 0..47 (larger n
 // waits for 47, which is only more conservative)
 __device__ __forceinline__ void wait_vm_n(int n)
@@ -363,6 +353,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
     dma.init(wave, lane);
     constexpr int DMA_KV = 2 * Dma::LOADS;
     const bool extra = GROUP && wave < 2;
+    const int per_tile = DMA_KV + (extra ? 1 : 0);  // this wave's loads per tile
+    constexpr int AHEAD = kDqStages - 1;             // tiles in flight ahead
     auto issue = [&](int S) {
         int origin, valid, owner;
         it_next(it_issue, origin, valid, owner);
@@ -409,7 +401,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
     // One key tile in stage S: S^T = K Q^T, then dP^T = V dO^T with
     // P^T = exp2(S^T c - L log2 e) formed two elements per step (K^T
     // transpose reads in between), dS^T = P^T (dP^T - D), dq^T += K^T dS^T,
-    // then the DMA of tile u + 3 and the end-of-tile barrier.
+    // then the DMA of tile u + AHEAD and the end-of-tile barrier.
     auto body = [&](int S, int u) {
         int origin, valid, owner;
         it_next(it_comp, origin, valid, owner);
@@ -522,17 +514,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[db][t], dsf[t], acc[db], 0, 0, 0);
-        // tile u + 3 into the stage tile u - 1 left, then: tile u + 1
-        // landed (u + 2 and u + 3 may still fly), every wave done with S
-        if (u + 3 < T)
+        // tile u + AHEAD into the stage tile u - 1 left, then: tile u + 1
+        // landed (the tiles after it may still fly), every wave done with S
+        if (u + AHEAD < T)
             issue(S == 0 ? kDqStages - 1 : S - 1);
         if (u + 1 < T) {
-            if (u + 3 < T)
-                wait_vm<2 * (DMA_KV + 1), 2 * DMA_KV>(extra);
-            else if (u + 2 < T)
-                wait_vm<DMA_KV + 1, DMA_KV>(extra);
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+            wait_vm_n((std::min(T - 1, u + AHEAD) - u - 1) * per_tile);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
@@ -543,14 +530,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     asm volatile("" ::: "memory");
-    for (int i = 0; i < kDqStages - 1 && i < T; ++i)
+    for (int i = 0; i < AHEAD && i < T; ++i)
         issue(i);
-    if (T > 2)
-        wait_vm<2 * (DMA_KV + 1), 2 * DMA_KV>(extra);
-    else if (T > 1)
-        wait_vm<DMA_KV + 1, DMA_KV>(extra);
-    else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    wait_vm_n((std::min(T, AHEAD) - 1) * per_tile);
     __syncthreads();
     for (int u = 0, S = 0; u < T; ++u, S = S == kDqStages - 1 ? 0 : S + 1)
         body(S, u);
@@ -801,7 +783,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     // dP = dO V^T with P = exp2(S c - L log2 e) formed two elements per step
     // (Q^T transpose reads in between); dv^T += dO^T P with dS = P (dP - D)
     // formed two elements per step; dk^T += Q^T dS; then the DMA of tile
-    // u + 3 and the end-of-tile barrier.
+    // u + AHEAD and the end-of-tile barrier.
     auto body = [&](int S, int u) {
         int head_c, origin, valid, owner;
         it_next(it_comp, head_c, origin, valid, owner);
