@@ -10,33 +10,35 @@
 // one sub-bucket meets a tile of another with a single owner decision.
 //
 // Three kernels, all bound by HBM and integer only:
-//   count   one wavefront per chunk of kChunk tokens; LDS histogram per wave
+//   count   one wavefront per chunk of tokens; LDS histogram per wave
 //   scan    one block per head: exclusive scan over (sub-bucket, chunk)
 //   scatter one wavefront per chunk; stable ranks from wavefront ballots
+// A scatter wavefront settles one sub-bucket key per pass, so its time grows
+// with the chunk, not with n: short sequences take short chunks (down to one
+// wavefront width) so that there are enough wavefronts to spread them.
 #include "common.hpp"
 
 namespace focus {
 namespace {
 
-constexpr int kChunk = 512;              // tokens per wavefront chunk
+constexpr int kChunkMax = 512;           // tokens per wavefront chunk, long sequences
+constexpr int kChunkMin = 64;            // ... and the shortest chunk
+constexpr int64_t kChunkWaves = 8192;    // wavefronts wanted before chunks shrink
 constexpr int kWavesPerBlock = 4;
+constexpr int kCachedTopk = 4;           // scatter keeps keys in registers up to here
 constexpr int kScanThreads = 1024;
 
 // Lowest and second-lowest group of token t (second = K at top-1).
-__device__ __forceinline__ void two_lowest(const int32_t *gt, int topk, int K, int &lo1,
-                                           int &lo2)
+__device__ __forceinline__ int2 two_lowest(const int32_t *gt, int topk, int K)
 {
-    lo1 = K;
-    lo2 = K;
+    int lo1 = K, lo2 = K;
     for (int s = 0; s < topk; ++s) {
         const int g = gt[s];
-        if (g < lo1) {
-            lo2 = lo1;
-            lo1 = g;
-        } else if (g < lo2) {
-            lo2 = g;
-        }
+        const int hi = max(g, lo1);
+        lo1 = min(g, lo1);
+        lo2 = min(hi, lo2);
     }
+    return make_int2(lo1, lo2);
 }
 
 __device__ __forceinline__ int subbucket(int g, int lo1, int lo2, int K)
@@ -45,10 +47,31 @@ __device__ __forceinline__ int subbucket(int g, int lo1, int lo2, int K)
     return g * (K + 1) + partner;
 }
 
+// Sub-bucket keys of a token's entries, in registers (topk <= TK).  An
+// absent token (valid false) or slot s >= topk gets no key that is used.
+template <int TK>
+__device__ __forceinline__ void entry_keys(const int32_t *gt, int topk, int K, bool valid,
+                                           int (&key)[TK])
+{
+    int g[TK];
+    int lo1 = K, lo2 = K;
+#pragma unroll
+    for (int s = 0; s < TK; ++s) {
+        g[s] = (valid && s < topk) ? gt[s] : K;  // K: no entry
+        const int hi = max(g[s], lo1);
+        lo1 = min(g[s], lo1);
+        lo2 = min(hi, lo2);
+    }
+#pragma unroll
+    for (int s = 0; s < TK; ++s)
+        key[s] = subbucket(g[s], lo1, lo2, K);
+}
+
 // counts[h][sb][chunk]
+template <int TK>
 __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t *__restrict__ groups,
                                                            int64_t n, int K, int topk,
-                                                           int nchunks,
+                                                           int chunk_len, int nchunks,
                                                            int32_t *__restrict__ counts)
 {
     extern __shared__ int32_t hist[];  // [kWavesPerBlock][nsb]
@@ -63,13 +86,21 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t *__rest
     __syncthreads();
     if (chunk < nchunks) {
         const int32_t *gh = groups + (int64_t)h * n * topk;
-        const int64_t t0 = (int64_t)chunk * kChunk;
-        for (int64_t t = t0 + lane; t < t0 + kChunk && t < n; t += kWave) {
+        const int64_t t0 = (int64_t)chunk * chunk_len;
+        for (int64_t t = t0 + lane; t < t0 + chunk_len && t < n; t += kWave) {
             const int32_t *gt = gh + t * topk;
-            int lo1, lo2;
-            two_lowest(gt, topk, K, lo1, lo2);
-            for (int s = 0; s < topk; ++s)
-                atomicAdd(&my[subbucket(gt[s], lo1, lo2, K)], 1);
+            if constexpr (TK > 0) {
+                int key[TK];
+                entry_keys<TK>(gt, topk, K, true, key);
+#pragma unroll
+                for (int s = 0; s < TK; ++s)
+                    if (s < topk)
+                        atomicAdd(&my[key[s]], 1);
+            } else {
+                const int2 lo = two_lowest(gt, topk, K);
+                for (int s = 0; s < topk; ++s)
+                    atomicAdd(&my[subbucket(gt[s], lo.x, lo.y, K)], 1);
+            }
         }
     }
     __syncthreads();
@@ -130,8 +161,13 @@ __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(int32_t *__re
         off[nsb] = carry_s;
 }
 
+// TK > 0: topk <= TK and each lane keeps its entries' sub-bucket keys in
+// registers, so a pass touches memory only for the LDS cursor and the stores.
+// TK == 0 serves any topk and re-reads the group ids each pass.  The count
+// kernel takes the same two forms.
+template <int TK>
 __global__ __launch_bounds__(256) void bucket_scatter_kernel(
-    const int32_t *__restrict__ groups, int64_t n, int K, int topk, int nchunks,
+    const int32_t *__restrict__ groups, int64_t n, int K, int topk, int chunk_len, int nchunks,
     const int32_t *__restrict__ bases, int32_t *__restrict__ tokens,
     int32_t *__restrict__ slot_entry)
 {
@@ -154,14 +190,17 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
     int32_t *th = tokens + (int64_t)h * n * topk;
     int32_t *sh = slot_entry + (int64_t)h * n * topk;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    const int64_t t0 = (int64_t)chunk * kChunk;
-    for (int64_t tb = t0; tb < t0 + kChunk && tb < n; tb += kWave) {
+    const int64_t t0 = (int64_t)chunk * chunk_len;
+    for (int64_t tb = t0; tb < t0 + chunk_len && tb < n; tb += kWave) {
         const int64_t t = tb + lane;
         const bool valid = t < n;
         const int32_t *gt = gh + (valid ? t : tb) * topk;
-        int lo1 = K, lo2 = K;
-        if (valid)
-            two_lowest(gt, topk, K, lo1, lo2);
+        int key[TK > 0 ? TK : 1];
+        int2 lo = make_int2(K, K);
+        if constexpr (TK > 0)
+            entry_keys<TK>(gt, topk, K, valid, key);
+        else if (valid)
+            lo = two_lowest(gt, topk, K);
         uint32_t pending = valid ? (topk >= 32 ? ~0u : ((1u << topk) - 1u)) : 0u;
         // Each pass settles one sub-bucket key X: every lane holding an entry
         // with key X takes rank (cursor[X] + number of lower lanes holding X).
@@ -172,16 +211,27 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
                 break;
             const int leader = __ffsll((unsigned long long)any) - 1;
             int my_key = -1;
-            if (pending != 0) {
-                const int s = __ffs(pending) - 1;
-                my_key = subbucket(gt[s], lo1, lo2, K);
+            if constexpr (TK > 0) {
+#pragma unroll
+                for (int s = TK - 1; s >= 0; --s)
+                    if ((pending >> s) & 1u)
+                        my_key = key[s];
+            } else if (pending != 0) {
+                my_key = subbucket(gt[__ffs(pending) - 1], lo.x, lo.y, K);
             }
-            const int X = __shfl(my_key, leader);
+            const int X = __builtin_amdgcn_readlane(my_key, leader);
             int sx = -1;
-            for (uint32_t p = pending; p != 0; p &= p - 1) {
-                const int s = __ffs(p) - 1;
-                if (subbucket(gt[s], lo1, lo2, K) == X)
-                    sx = s;
+            if constexpr (TK > 0) {
+#pragma unroll
+                for (int s = 0; s < TK; ++s)
+                    if (((pending >> s) & 1u) && key[s] == X)
+                        sx = s;
+            } else {
+                for (uint32_t p = pending; p != 0; p &= p - 1) {
+                    const int s = __ffs(p) - 1;
+                    if (subbucket(gt[s], lo.x, lo.y, K) == X)
+                        sx = s;
+                }
             }
             const uint64_t members = __ballot(sx >= 0);
             const int32_t cursor = my[X];
@@ -202,10 +252,21 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
 
 }  // namespace
 
+// Tokens per chunk: kChunkMax, halved (down to kChunkMin) while the heads
+// have fewer than kChunkWaves chunks between them.
+int bucket_chunk(int H, int64_t n)
+{
+    int c = kChunkMax;
+    while (c > kChunkMin && (int64_t)H * ((n + c - 1) / c) < kChunkWaves)
+        c /= 2;
+    return c;
+}
+
 size_t bucket_workspace_bytes(int H, int64_t n, int K, int topk)
 {
     (void)topk;
-    const int64_t nchunks = (n + kChunk - 1) / kChunk;
+    const int chunk = bucket_chunk(H, n);
+    const int64_t nchunks = (n + chunk - 1) / chunk;
     return align_up((size_t)H * num_subbuckets(K) * nchunks * sizeof(int32_t), 256);
 }
 
@@ -214,12 +275,17 @@ hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int top
                          hipStream_t s)
 {
     const int nsb = num_subbuckets(K);
-    const int nchunks = (int)((n + kChunk - 1) / kChunk);
+    const int chunk = bucket_chunk(H, n);
+    const int nchunks = (int)((n + chunk - 1) / chunk);
     int32_t *counts = static_cast<int32_t *>(ws);
     const dim3 grid((nchunks + kWavesPerBlock - 1) / kWavesPerBlock, H);
     const size_t lds = sizeof(int32_t) * nsb * kWavesPerBlock;
-    hipLaunchKernelGGL(bucket_count_kernel, grid, dim3(kWave * kWavesPerBlock), lds, s,
-                       groups, n, K, topk, nchunks, counts);
+    if (topk <= kCachedTopk)
+        hipLaunchKernelGGL(bucket_count_kernel<kCachedTopk>, grid, dim3(kWave * kWavesPerBlock),
+                           lds, s, groups, n, K, topk, chunk, nchunks, counts);
+    else
+        hipLaunchKernelGGL(bucket_count_kernel<0>, grid, dim3(kWave * kWavesPerBlock), lds, s,
+                           groups, n, K, topk, chunk, nchunks, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -228,8 +294,13 @@ hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int top
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(bucket_scatter_kernel, grid, dim3(kWave * kWavesPerBlock), lds, s,
-                       groups, n, K, topk, nchunks, counts, tokens, slot_entry);
+    if (topk <= kCachedTopk)
+        hipLaunchKernelGGL(bucket_scatter_kernel<kCachedTopk>, grid,
+                           dim3(kWave * kWavesPerBlock), lds, s, groups, n, K, topk, chunk,
+                           nchunks, counts, tokens, slot_entry);
+    else
+        hipLaunchKernelGGL(bucket_scatter_kernel<0>, grid, dim3(kWave * kWavesPerBlock), lds,
+                           s, groups, n, K, topk, chunk, nchunks, counts, tokens, slot_entry);
     return hipGetLastError();
 }
 

@@ -106,6 +106,23 @@ def test_route_forced_ties(K, topk):
     np.testing.assert_array_equal(slot_entry.cpu().numpy(), se_ref)
 
 
+# Bucketing alone on random distinct group ids: the chunk length follows H and
+# n (64 to 512 tokens), and the keys sit in registers up to top-4.
+@pytest.mark.parametrize("H,n,K,topk", [(8, 300001, 8, 3), (2, 5000, 6, 5), (16, 1_000_003, 4, 1),
+                                        (3, 65, 32, 17)])
+def test_bucket_chunk_lengths_bitexact(H, n, K, topk):
+    log(f"bucket H={H} n={n} K={K} top{topk}")
+    rng = np.random.default_rng(n + 7 * K + topk)
+    g = np.argsort(rng.random((H, n, K), dtype=np.float32), axis=-1)[..., :topk]
+    g = np.ascontiguousarray(g, dtype=np.int32)
+    off_ref, tok_ref, se_ref = oracle.bucket(g, K)
+    offsets, tokens, slot_entry = F.focus_bucket(torch.from_numpy(g).to(DEV), K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_ref)
+    np.testing.assert_array_equal(tokens.cpu().numpy(), tok_ref)
+    np.testing.assert_array_equal(slot_entry.cpu().numpy(), se_ref)
+
+
 # ----------------------------------------------------------------------------
 # attention, element by element on shapes the oracle evaluates in full
 
