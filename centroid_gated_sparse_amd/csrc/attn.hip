@@ -612,19 +612,31 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         n_tiles_total = (w > 0) ? (int)((j_last - j_first) / kKeyTile + 1) : 0;
     }
 
-    // iterator over key tiles: (sub-bucket, tile) for the group pass
+    // iterator over key tiles: (sub-bucket, tile) for the group pass.  The
+    // current sub-bucket's start, count and owner flag are block-uniform and
+    // kept in scalar registers; LDS is read only when the iterator steps to
+    // the next sub-bucket, so the common step issues no LDS read (and no
+    // wait) ahead of a tile's loads.
     int it_sub = 0, it_tile = 0;
-    // (values read from LDS are block-uniform: keep them in scalar registers)
     auto uniform = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    int sb_count = 0, sb_start = 0, sb_owner = 0;
+    if (GROUP) {
+        sb_count = uniform(sub_count[0]);
+        sb_start = uniform(sub_start[0]);
+        sb_owner = uniform(sub_owner[0]);
+    }
     auto tile_origin = [&](int &valid, int &owner) -> int64_t {
         if (GROUP) {
-            while (it_tile * kKeyTile >= uniform(sub_count[it_sub])) {
+            while (it_tile * kKeyTile >= sb_count) {
                 ++it_sub;
                 it_tile = 0;
+                sb_count = uniform(sub_count[it_sub]);
+                sb_start = uniform(sub_start[it_sub]);
+                sb_owner = uniform(sub_owner[it_sub]);
             }
-            valid = min(kKeyTile, uniform(sub_count[it_sub]) - it_tile * kKeyTile);
-            owner = uniform(sub_owner[it_sub]);
-            return (int64_t)uniform(sub_start[it_sub]) + (int64_t)it_tile * kKeyTile;
+            valid = min(kKeyTile, sb_count - it_tile * kKeyTile);
+            owner = sb_owner;
+            return (int64_t)sb_start + (int64_t)it_tile * kKeyTile;
         } else {
             valid = kKeyTile;
             owner = 0;
@@ -668,11 +680,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             kpos[2 * kKeyTile + 1] = owner;
         }
     };
-    auto stage_meta = [&](auto I, int &valid, int &owner) {
-        const int *meta = stage(I).key + 2 * kKeyTile;
-        valid = __builtin_amdgcn_readfirstlane(meta[0]);
-        owner = __builtin_amdgcn_readfirstlane(meta[1]);
-    };
     int cur_valid = 0, cur_owner = 0;
     if constexpr (!BF16) {
         if (n_tiles_total > 0) {
@@ -694,6 +701,19 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     auto scores = [&](f32x16 (&s)[2], auto I, int valid, int owner) {
         const int *kpos = stage(I).key;
         const uint32_t *kgm = reinterpret_cast<const uint32_t *>(kpos + kKeyTile);
+        // Does any pair of this tile x wavefront need a mask?  Decided from
+        // the tile's edge position, read before the products: the LDS read
+        // then completes under the MFMAs instead of after them.
+        // (no short-circuit: a branch here would make the wavefront wait
+        // for the read before the products start)
+        bool masked;
+        if (GROUP) {
+            const int last_key = kpos[valid - 1];  // valid >= 1
+            masked = (valid < kKeyTile) | (owner != 0) | (last_key > wq_min - w);
+        } else {
+            const int j0 = kpos[0];
+            masked = !((j0 + kKeyTile - 1 <= wq_min) && (j0 > wq_max - w));
+        }
         TL::qk(s, qf, stage(I).k, lo);
         if constexpr (GATED) {
             // far keys (position <= qpos - gate_w) take the gate; in the
@@ -724,15 +744,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                     }
                 }
             }
-        }
-            // does any pair of this tile x wavefront need a mask?
-        bool masked;
-        if (GROUP) {
-            const int last_key = kpos[valid - 1];
-            masked = (valid < kKeyTile) || owner || (last_key > wq_min - w);
-        } else {
-            const int j0 = kpos[0];
-            masked = !((j0 + kKeyTile - 1 <= wq_min) && (j0 > wq_max - w));
         }
         if (masked) {
             // Register r of lane half h holds key index kb*32 + h*16 + r of
@@ -856,6 +867,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // reads of rows sigma(m) fall in distinct banks.
         constexpr int DMA_A = GATED ? kKeyTile * GA * 2 / 1024 : 0;
         const bool a_wave = GATED && __builtin_amdgcn_readfirstlane(wave) == 0;
+        // valid-key count and owner flag of the tile in each stage: set by
+        // every wavefront when it issues the tile's loads (the iterator runs
+        // in each wavefront), read when the tile is computed; stage indices
+        // are compile-time, so the ring stays in scalar registers
+        int ring_valid[NSTAGE] = {}, ring_owner[NSTAGE] = {};
         auto issue = [&](auto I) {
             int nv, no;
             const int64_t origin = tile_origin(nv, no);
@@ -883,10 +899,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                     }
                 }
             }
-            if (threadIdx.x == 0) {
-                kp[2 * kKeyTile] = nv;
-                kp[2 * kKeyTile + 1] = no;
-            }
+            ring_valid[decltype(I)::value] = nv;
+            ring_owner[decltype(I)::value] = no;
         };
         // end of an interval: everything but the newest tile's loads landed,
         // this interval's LDS traffic done, then the block barrier
@@ -932,9 +946,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 TL::refresh(lo);
                 if (ROLE_A) {
                     if (u < T) {
-                        int valid, owner;
-                        stage_meta(CUR, valid, owner);
-                        scores(s, CUR, valid, owner);
+                        scores(s, CUR, ring_valid[decltype(CUR)::value],
+                               ring_owner[decltype(CUR)::value]);
                         acc.softmax(s, p.c, pf);
                         TL::pv(acc.o, pf, stage(CUR).v, lo);
                     }
@@ -944,9 +957,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                         TL::pv(acc.o, pf, stage(PREV).v, lo);
                     }
                     if (u < T) {
-                        int valid, owner;
-                        stage_meta(CUR, valid, owner);
-                        scores(s, CUR, valid, owner);
+                        scores(s, CUR, ring_valid[decltype(CUR)::value],
+                               ring_owner[decltype(CUR)::value]);
                     }
                 }
                 close_interval(ahead);
