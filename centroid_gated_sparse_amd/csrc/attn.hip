@@ -233,7 +233,7 @@ struct Tile<D, true> {
     // (The sum is taken before rounding: near-uniform rows round their
     // probabilities the same way, and a sum of the rounded values would bias
     // the log-sum-exp by up to ~1e-3.)
-    __device__ static float exp_tile(const f32x16 (&s)[2], float c, float mc, PFrag &pf)
+    __device__ static float exp_tile(const f32x16 (&s)[2], float c, float negm, PFrag &pf)
     {
         float l0 = 0.f, l1 = 0.f;
 #pragma unroll
@@ -243,9 +243,9 @@ struct Tile<D, true> {
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
                     const float p0 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e], c, -mc));
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e], c, negm));
                     const float p1 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e + 1], c, -mc));
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e + 1], c, negm));
                     l0 += p0;
                     l1 += p1;
                     pf.v[kb][kk][e] = (__bf16)p0;
@@ -360,14 +360,14 @@ struct Tile<D, false> {
             }
     }
 
-    __device__ static float exp_tile(const f32x16 (&s)[2], float c, float mc, PFrag &pf)
+    __device__ static float exp_tile(const f32x16 (&s)[2], float c, float negm, PFrag &pf)
     {
         float l = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, negm));
                 pf.s[kb][r] = pr;
                 l += pr;
             }
@@ -382,8 +382,10 @@ struct Tile<D, false> {
 template <class TL>
 struct Acc {
     f32x16 o[TL::DB];
-    float m;  // running max in the scaled log2 domain (may be -inf)
-    float l;  // this lane half's partial row sum
+    float m;     // running max in the scaled log2 domain (may be -inf)
+    float negm;  // exponent offset of P: -m, or 0 while m is -inf
+    float thr;   // (m + kLazyRescale) / c, in raw-logit units
+    float l;     // this lane half's partial row sum
 
     __device__ void init()
     {
@@ -391,11 +393,22 @@ struct Acc {
         for (int db = 0; db < TL::DB; ++db)
             o[db] = f32x16{};
         m = -INFINITY;
+        negm = 0.f;
+        thr = -INFINITY;
         l = 0.f;
     }
 
     // Fold one tile of raw logits into the state; P receives the
     // probabilities for the PV product.
+    //
+    // Lazy rescale: the running max only moves when a row's max grew by
+    // more than 2^8, so P stays below 2^8 and O is rarely rescaled.  The
+    // test needs no exchange between the lane halves: the row max exceeds
+    // the row's threshold exactly when one of its halves does, and the
+    // wavefront takes the update when any lane's does.  Only the update
+    // forms the row max; the threshold and the exponent offset are kept
+    // with m, so a tile that leaves m alone costs the half maxima and one
+    // compare.  (c > 0: the entry points require a positive scale.)
     __device__ void softmax(const f32x16 (&s)[2], float c, typename TL::PFrag &pf)
     {
         float t = -INFINITY;
@@ -404,14 +417,14 @@ struct Acc {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 t = fmaxf(t, s[kb][r]);
-        const float mx = swap_halves_max(t) * c;
-        // Lazy rescale: the running max only moves when a row's max grew by
-        // more than 2^8, so P stays below 2^8 and O is rarely rescaled.
-        if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescale) != 0) {
+        if (__builtin_amdgcn_ballot_w64(t > thr) != 0) {
+            const float mx = swap_halves_max(t) * c;
             const float m_new = fmaxf(m, mx);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
             const float alpha = __builtin_amdgcn_exp2f(m - m_use);
             m = m_new;
+            negm = -m_use;
+            thr = (m_new + kLazyRescale) / c;
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < TL::DB; ++db)
@@ -419,8 +432,7 @@ struct Acc {
                 for (int r = 0; r < 16; ++r)
                     o[db][r] *= alpha;
         }
-        const float mc = (m == -INFINITY) ? 0.f : m;
-        l += TL::exp_tile(s, c, mc, pf);
+        l += TL::exp_tile(s, c, negm, pf);
     }
 };
 
