@@ -866,9 +866,9 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // on the vector ALUs, and the SIMD overlaps the two.  B finishes the
         // last tile in one extra interval.  Tile u lives in stage u % 4; its
         // loads (K, V^T, key positions and group bits, all LDS-DMA) are
-        // issued at the start of interval u - 2 and awaited at the end of
-        // interval u - 1, two intervals of latency cover.  Both roles pass
-        // exactly one barrier per interval.
+        // issued during interval u - 2 (after each role's first phase) and
+        // awaited at the end of interval u - 1.  Both roles pass exactly one
+        // barrier per interval.
         const int T = n_tiles_total;
         // LDS-DMA loads each wavefront issues per tile (waited on by count)
         constexpr int DMA_KV = 2 * TL::LOADS;
@@ -949,23 +949,33 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             constexpr bool ROLE_A = decltype(role_tag)::value;
             f32x16 s[2];
             typename TL::PFrag pf;
-            auto interval = [&](int u, auto PREV, auto CUR, auto AHEAD) {
+            auto interval = [&](int u, auto PREV, auto CUR, auto AHEAD, auto FIRST) {
+                // The loads of tile u + 2 go out after each role's first
+                // phase, not at the interval's start: both wavefronts of a
+                // SIMD leave the barrier together, and issuing then would
+                // hold both off the matrix core at once.
                 const bool ahead = u + 2 < T;
-                if (ahead) {
-                    ++it_tile;
-                    issue(AHEAD);
-                }
+                auto issue_ahead = [&] {
+                    if (ahead) {
+                        ++it_tile;
+                        issue(AHEAD);
+                    }
+                };
                 TL::refresh(lo);
                 if (ROLE_A) {
                     if (u < T) {
                         scores(s, CUR, ring_valid[decltype(CUR)::value],
                                ring_owner[decltype(CUR)::value]);
+                        issue_ahead();
                         acc.softmax(s, p.c, pf);
                         TL::pv(acc.o, pf, stage(CUR).v, lo);
                     }
                 } else {
-                    if (u >= 1) {
+                    if constexpr (decltype(FIRST)::value) {
+                        issue_ahead();
+                    } else {
                         acc.softmax(s, p.c, pf);
+                        issue_ahead();
                         TL::pv(acc.o, pf, stage(PREV).v, lo);
                     }
                     if (u < T) {
@@ -975,14 +985,19 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 }
                 close_interval(ahead);
             };
-            for (int u = 0; u <= T; u += 4) {
-                interval(u, I3{}, I0{}, I2{});
+            // interval 0 (role B has no previous tile to finish) is peeled
+            // off, so that every interval of the unrolled loop has one shape
+            // (an alternative branch there splits the accumulators' live
+            // ranges and spills them)
+            interval(0, I3{}, I0{}, I2{}, std::true_type{});
+            for (int u = 1; u <= T; u += 4) {
+                interval(u, I0{}, I1{}, I3{}, std::false_type{});
                 if (u + 1 <= T)
-                    interval(u + 1, I0{}, I1{}, I3{});
+                    interval(u + 1, I1{}, I2{}, I0{}, std::false_type{});
                 if (u + 2 <= T)
-                    interval(u + 2, I1{}, I2{}, I0{});
+                    interval(u + 2, I2{}, I3{}, I1{}, std::false_type{});
                 if (u + 3 <= T)
-                    interval(u + 3, I2{}, I3{}, I1{});
+                    interval(u + 3, I3{}, I0{}, I2{}, std::false_type{});
             }
         };
         if (__builtin_amdgcn_readfirstlane(wave) < kWavesPerRole)
