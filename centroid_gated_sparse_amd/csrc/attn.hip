@@ -73,7 +73,7 @@ struct Tile<D, true> {
     static constexpr int KCH = D / 8;  // 16-byte chunks per K row
     static constexpr int K_BYTES = kKeyTile * D * 2;
     static constexpr int V_BYTES = D * kKeyTile * 2;
-    static constexpr int LOADS = (K_BYTES / 16) / kThreads;  // per thread, K and V each
+    static constexpr int LOADS = 2 * (K_BYTES / 16) / kThreads;  // per role-A lane, K and V each
 
     struct QFrag {
         bf16x8 v[KS];
@@ -100,9 +100,10 @@ struct Tile<D, true> {
             qf.v[ks] = src[ks * 2 + h];
     }
 
-    // Start the loads of one key tile straight into LDS: K rows row0.. of
-    // kmat and V^T columns row0.. of vmat (both zero-padded past their last
-    // row, so no load needs a clamp).  Each global_load_lds writes 64
+    // Start the loads of one key tile straight into LDS (issued by the four
+    // role-A wavefronts only; role B, on the critical path, issues none):
+    // K rows row0.. of kmat and V^T columns row0.. of vmat (both zero-padded
+    // past their last row, so no load needs a clamp).  Each global_load_lds writes 64
     // consecutive 16-byte LDS slots (one per lane), so every lane fetches the
     // chunk that the swizzled layout keeps in its slot.  Addresses are a
     // block-uniform base (scalar registers) plus a fixed per-lane 32-bit
@@ -117,7 +118,7 @@ struct Tile<D, true> {
         const int wave = threadIdx.x / kWave;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int P = (wave * LOADS + i) * kWave + lane;
+            const int P = ((wave % kWavesPerRole) * LOADS + i) * kWave + lane;
             const int row = P / KCH;
             const int c = (P % KCH) ^ kswz(row);
             st.koff[i] = (uint32_t)((row * D + c * 8) * 2);
@@ -871,7 +872,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // barrier per interval.
         const int T = n_tiles_total;
         // LDS-DMA loads each wavefront issues per tile (waited on by count)
-        constexpr int DMA_KV = 2 * TL::LOADS;
+        // Role B's chain (softmax, PV, QK back to back) sets each interval's
+        // length while role A waits at the barrier, so role A issues all of a
+        // tile's K / V^T loads and role B none.
+        const bool role_a_wave = __builtin_amdgcn_readfirstlane(wave) < kWavesPerRole;
+        constexpr int DMA_KV = 2 * TL::LOADS;  // per role-A wavefront
         const bool key_wave = GROUP && __builtin_amdgcn_readfirstlane(wave) == 0;
         // gated pass: wavefront 0 also loads the keys' assignment rows
         // (GA * 128 bytes per tile, one LDS-DMA load per KB).  LDS slot P
@@ -887,7 +892,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         auto issue = [&](auto I) {
             int nv, no;
             const int64_t origin = tile_origin(nv, no);
-            TL::prefetch(st, p, kvh, origin, stage(I).k, stage(I).v);
+            if (role_a_wave)
+                TL::prefetch(st, p, kvh, origin, stage(I).k, stage(I).v);
             int *kp = stage(I).key;
             if (GROUP) {
                 if (key_wave) {
@@ -927,12 +933,14 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 __builtin_amdgcn_s_waitcnt(0x70 | (DMA_KV + 2));
             else if (a_wave)
                 __builtin_amdgcn_s_waitcnt(0x70 | (DMA_KV + DMA_A));
-            else
+            else if (role_a_wave)
                 __builtin_amdgcn_s_waitcnt(0x70 | DMA_KV);
+            else
+                __builtin_amdgcn_s_waitcnt(0x70);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         };
-        static_assert(!BF16 || TL::LOADS == 1 || TL::LOADS == 2, "vmcnt counts assume 1-2 loads");
+        static_assert(!BF16 || TL::LOADS == 2 || TL::LOADS == 4, "vmcnt counts assume 2-4 loads");
         static_assert(DMA_KV + DMA_A <= 15, "vmcnt immediate holds 4 bits here");
 
         // prologue: tiles 0 and 1 (tile 0's iterator position is current)
