@@ -180,6 +180,36 @@ def test_attention_small_full_rows(wl):
     np.testing.assert_allclose(got, cnt[hk].astype(np.float64), rtol=1e-5)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_rising_logits(d):
+    """Logits that rise along the key positions, by about 60 in log2 units
+    over the sequence: every row's running max moves many times while its
+    keys are scanned (ascending inside each sub-bucket and in the window),
+    so the lazy rescale of the online softmax runs on many tiles of both
+    passes.  Values stay small, so the absolute bound on O is meaningful."""
+    wl = W(f"bf16_d{d}_rising_logits", 1200, 4, 2, d, 4, 2, 64, "bf16")
+    log(f"attention {wl}")
+    seed = 4242 + d
+    c, r, _ = routing_inputs(wl, seed)
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    # q.k grows to about 60 / (scale log2 e) at the last position
+    beta = (60.0 / (wl.scale * math.log2(math.e))) * np.arange(wl.n) / wl.n
+    noise = 0.3 / math.sqrt(d)
+    qn = u[None, None, :] + noise * rng.standard_normal((wl.hq, wl.n, d))
+    kn = beta[None, :, None] * u[None, None, :] + noise * rng.standard_normal((wl.hkv, wl.n, d))
+    vn = rng.standard_normal((wl.hkv, wl.n, d)) / math.sqrt(d)
+    q, k, v = (torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(DEV)
+               for a in (qn, kn, vn))
+    res = gpu_forward(wl, c, r, q, k, v)
+    g_ref, _ = oracle.route(r, c, wl.topk)
+    np.testing.assert_array_equal(res["groups"].cpu().numpy(), g_ref)
+    rh = np.repeat(np.arange(wl.hq, dtype=np.int32), wl.n)
+    rp = np.tile(np.arange(wl.n, dtype=np.int64), wl.hq)
+    check_rows(wl, res, q, k, v, g_ref, rh, rp, wl.name)
+
+
 def test_dense_causal_baseline():
     wl = W("dense", 1000, 8, 2, 128, 1, 1, 1000, "bf16")
     q, k, v = qkv_inputs(wl, 5, DEV)
