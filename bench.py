@@ -95,7 +95,8 @@ def cpu_baseline(wl, seed, q, k, v, groups_np, r, c, budget_s: float):
     import oracle
     from centroid_gated_sparse_amd.workloads import sample_rows, to_bf16_bits
 
-    cores = os.cpu_count() or 1
+    # the OpenMP threads the oracle's row loop runs on, passed explicitly
+    cores = int(os.environ.get("OMP_NUM_THREADS") or 0) or len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     g_ref, _ = oracle.route(r, c, wl.topk)
     oracle.bucket(g_ref, wl.K)
@@ -114,7 +115,7 @@ def cpu_baseline(wl, seed, q, k, v, groups_np, r, c, budget_s: float):
         qn = to_bf16_bits(qrows) if wl.dtype == "bf16" else qrows.cpu().numpy()
         t1 = time.perf_counter()
         _, _, cnt = oracle.attn_rows(qn, kb, vb, g_ref, wl.K, wl.window, wl.scale, rh, rp,
-                                     num_q_heads=wl.hq)
+                                     nthreads=cores, num_q_heads=wl.hq)
         t_attn += time.perf_counter() - t1
         pairs_done += int(cnt.sum())
         done_rows += len(rh)
@@ -503,7 +504,11 @@ def main() -> int:
     ap.add_argument("--workload", default="gqa7b_n1m_k8")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle attention time for the CPU baseline")
+    ap.add_argument("--cpu-budget-other", type=float, default=3.0,
+                    help="seconds of oracle attention time for each other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only --workload (no per-workload blocks for the others)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--topk-sweep", type=int, default=0, metavar="N",
                     help="the top-k trade-off (top-1..4) on an N-token layer")
@@ -549,11 +554,41 @@ def main() -> int:
         return run_train_forward(args.workload, args.steps, args.warmup)
 
     from centroid_gated_sparse_amd import focus as F
-    from centroid_gated_sparse_amd.workloads import (WORKLOADS, qkv_inputs, routing_inputs,
-                                                     seed_for)
+    from centroid_gated_sparse_amd.workloads import WORKLOADS, WORKLOAD_ORDER
 
     F.lib()  # fail loudly before anything else if the HIP library is missing
     wl = WORKLOADS[args.workload]
+    res = measure_workload(F, wl, args.steps, args.warmup, dense=not args.no_dense,
+                           dense_reps=3, cpu_budget=None if args.no_cpu_baseline
+                           else args.cpu_budget, headline=True)
+    result = res.pop("headline")
+    # every other workload of the set, each timed the same way (the 1M-token
+    # layer's buffers are gone by now), as blocks of the same JSON line
+    if not args.no_other_workloads:
+        blocks = {}
+        for name in WORKLOAD_ORDER:
+            if name == wl.name:
+                continue
+            blocks[name] = measure_workload(
+                F, WORKLOADS[name], max(args.steps, 10), max(args.warmup, 2),
+                dense=not args.no_dense, dense_reps=5,
+                cpu_budget=None if args.no_cpu_baseline else args.cpu_budget_other)
+        result["detail"]["workloads"] = blocks
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def measure_workload(F, wl, steps: int, warmup: int, dense: bool, dense_reps: int,
+                     cpu_budget, headline: bool = False) -> dict:
+    """Times `steps` whole Focus steps of one workload (after `warmup`), with
+    per-part HIP events on the launch stream, then our dense causal kernel
+    (median of `dense_reps` launches) and the CPU oracle on sampled rows.
+    Returns the workload's block; with headline=True also the bench's JSON
+    result under "headline".  Frees every device buffer it made."""
+    import torch
+
+    from centroid_gated_sparse_amd.workloads import qkv_inputs, routing_inputs, seed_for
+
     seed = seed_for(wl.name)
     dev = "cuda"
     log(f"bench: workload {wl}")
@@ -562,100 +597,137 @@ def main() -> int:
     ct = torch.from_numpy(c).to(dev)
     q, k, v = qkv_inputs(wl, seed, dev)
     step, bufs = make_step(F, wl, q, k, v, rt, ct)
-    groups, aws = bufs["groups"], bufs["aws"]
     H, n, K, topk = wl.hkv, wl.n, wl.K, wl.topk
     dt_code = F.FOCUS_BF16 if wl.dtype == "bf16" else F.FOCUS_F32
-    out, lse = bufs["out"], bufs["lse"]
-    log(f"bench: workspace {aws.numel() / 2**30:.2f} GiB")
+    log(f"bench: workspace {bufs['aws'].numel() / 2**30:.2f} GiB")
     names = ["route", "bucket", "prepare", "group", "window"]
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step()
         torch.cuda.synchronize()
-        log(f"bench: warmup {i + 1}/{args.warmup} done")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
-              for _ in range(args.steps)]
+        if headline:
+            log(f"bench: warmup {i + 1}/{warmup} done")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(f"bench: {args.steps} steps in {wall:.3f} s")
+    log(f"bench: {wl.name}: {steps} steps in {wall:.3f} s")
     part_ms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events]))
                for j, nm in enumerate(names)}
+    groups_np = bufs["groups"].cpu().numpy()
 
     # algorithmic work: 4*d FLOPs (QK^T and PV) per surviving pair
-    pairs_h = surviving_pairs(groups.cpu().numpy(), K, wl.window)     # per routing head
+    pairs_h = surviving_pairs(groups_np, K, wl.window)     # per routing head
     ratio = wl.hq // H
     surv = int(pairs_h.sum()) * ratio
     win = window_pairs(n, wl.window) * wl.hq
     far = surv - win
     flops_group = 4.0 * wl.d * far
     flops_all = 4.0 * wl.d * surv
-    group_s = part_ms["group"] / 1e3
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = flops_group / group_s / 1e12
-    ms_per_step = wall / args.steps * 1e3
-    result = {
-        "metric": METRIC,
-        "value": n / (wall / args.steps),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    group_tflops = flops_group / (part_ms["group"] / 1e3) / 1e12
+    attn_ms = part_ms["group"] + part_ms["window"]
+    attn_tflops = flops_all / (attn_ms / 1e3) / 1e12
+    ms_per_step = wall / steps * 1e3
+    # HBM bytes the method must move: routing reads r and writes groups and
+    # gmask; bucketing reads the group ids twice and writes tokens and slots
+    route_bytes = H * n * (16 * 4 + 4 * topk + 4)
+    bucket_bytes = H * n * topk * 16
+    block = {
+        "n": n, "q_heads": wl.hq, "kv_heads": H, "head_dim": wl.d, "centroids": K,
+        "topk": topk, "window": wl.window, "dtype": wl.dtype, "steps": steps,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic",
-        "config": {"workload": wl.name, "n": n, "q_heads": wl.hq, "kv_heads": H,
-                   "head_dim": wl.d, "centroids": K, "topk": topk, "window": wl.window,
-                   "batch": 1, "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": recorded_traffic(wl.name),
-                     "kernel": "attn_kernel group pass (focus_attn_fwd part GROUP)"},
-        "detail": {
-            "part_ms": part_ms,
-            "surviving_pairs": surv,
-            "far_pairs": far,
-            "window_pairs": win,
-            "pairs_kept_vs_dense": surv / (wl.hq * n * (n + 1) / 2),
-            "attn_tflops_surviving": flops_all / ((part_ms["group"] + part_ms["window"]) / 1e3)
-            / 1e12,
-            "step_tflops_surviving": flops_all / (ms_per_step / 1e3) / 1e12,
-        },
+        "tokens_per_s": n / (wall / steps),
+        "part_ms": part_ms,
+        "window_merge_ms": part_ms["window"],
+        "group_kernel": {"tflops": group_tflops, "frac": group_tflops / peak, "peak": peak,
+                         "far_pairs": far},
+        "group_plus_window": {"tflops": attn_tflops, "frac": attn_tflops / peak,
+                              "surviving_pairs": surv},
+        "step_tflops_surviving": flops_all / (ms_per_step / 1e3) / 1e12,
+        "pairs_kept_vs_dense": surv / (wl.hq * n * (n + 1) / 2),
+        "route_gbs": route_bytes / (part_ms["route"] / 1e3) / 1e9,
+        "bucket_gbs": bucket_bytes / (part_ms["bucket"] / 1e3) / 1e9,
     }
+    log(f"bench: {wl.name}: {ms_per_step:.3f} ms/step, group {group_tflops:.0f} TFLOP/s "
+        f"({group_tflops / peak:.1%}), group+window {attn_tflops / peak:.1%}")
 
-    if not args.no_dense:
+    headline_result = None
+    if headline:
+        headline_result = {
+            "metric": METRIC,
+            "value": n / (wall / steps),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": steps,
+            "warmup": warmup,
+            "ms_per_step": ms_per_step,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": wl.dtype,
+            "data": "synthetic",
+            "config": {"workload": wl.name, "n": n, "q_heads": wl.hq, "kv_heads": H,
+                       "head_dim": wl.d, "centroids": K, "topk": topk, "window": wl.window,
+                       "batch": 1, "parallelism": "single-gpu"},
+            "roofline": {"bound": "mfma", "achieved": group_tflops, "peak": peak,
+                         "unit": "TFLOP/s", "frac": group_tflops / peak,
+                         "traffic": recorded_traffic(wl.name),
+                         "kernel": "attn_kernel group pass (focus_attn_fwd part GROUP): "
+                                   "4 d FLOPs per surviving far pair over its event time",
+                         "group_plus_window_frac": attn_tflops / peak},
+            "detail": {
+                "part_ms": part_ms,
+                "surviving_pairs": surv,
+                "far_pairs": far,
+                "window_pairs": win,
+                "pairs_kept_vs_dense": block["pairs_kept_vs_dense"],
+                "attn_tflops_surviving": attn_tflops,
+                "step_tflops_surviving": block["step_tflops_surviving"],
+                "route_gbs": block["route_gbs"],
+                "bucket_gbs": block["bucket_gbs"],
+            },
+        }
+
+    # free the Focus buffers (the 1M-token workspace is 44 GiB) before the
+    # dense baseline and the oracle
+    del step, bufs
+    torch.cuda.empty_cache()
+    if dense:
         dws = torch.empty(max(F.focus_dense_workspace_bytes(dt_code, H, n, wl.d), 16),
                           dtype=torch.uint8, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        F.focus_dense_causal_fwd(q, k, v, wl.scale, out, lse, dws)
-        torch.cuda.synchronize()
-        e0.record()
-        F.focus_dense_causal_fwd(q, k, v, wl.scale, out, lse, dws)
-        e1.record()
-        torch.cuda.synchronize()
-        dense_ms = e0.elapsed_time(e1)
+        out = torch.empty_like(q)
+        lse = torch.empty((wl.hq, n), dtype=torch.float32, device=dev)
+        dense_ms = timed_ms(lambda: F.focus_dense_causal_fwd(q, k, v, wl.scale, out, lse, dws),
+                            1, dense_reps)
         dense_flops = 4.0 * wl.d * wl.hq * n * (n + 1) / 2
-        result["detail"]["dense_causal"] = {
+        dense_block = {
             "ms": dense_ms,
+            "launches": dense_reps,
+            "timing": f"median of {dense_reps} launches after one warm-up",
             "tflops": dense_flops / (dense_ms / 1e3) / 1e12,
+            "frac": dense_flops / (dense_ms / 1e3) / 1e12 / peak,
             "focus_step_speedup": dense_ms / ms_per_step,
         }
-        del dws
-        log(f"bench: dense causal {dense_ms:.1f} ms")
-
-    if not args.no_cpu_baseline:
-        del aws, out, lse, bufs, step
+        block["dense_causal"] = dense_block
+        if headline_result is not None:
+            headline_result["detail"]["dense_causal"] = dense_block
+        del dws, out, lse
         torch.cuda.empty_cache()
-        result["cpu_baseline"] = cpu_baseline(wl, seed, q, k, v, groups.cpu().numpy(), r, c,
-                                              args.cpu_budget)
-    print(json.dumps(result), flush=True)
-    return 0
+        log(f"bench: {wl.name}: dense causal {dense_ms:.2f} ms")
+    if cpu_budget is not None:
+        cpu = cpu_baseline(wl, seed, q, k, v, groups_np, r, c, cpu_budget)
+        block["cpu_oracle"] = cpu
+        if headline_result is not None:
+            headline_result["cpu_baseline"] = cpu
+    del q, k, v, rt, ct
+    torch.cuda.empty_cache()
+    if headline_result is not None:
+        block["headline"] = headline_result
+    return block
 
 
 if __name__ == "__main__":

@@ -17,7 +17,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libfocus.so"
-SOURCES = ["route.hip", "bucket.hip", "attn.hip", "attn_bwd.hip", "attn_train.hip", "api.hip"]
+SOURCES = ["route.hip", "bucket.hip", "check.hip", "attn.hip", "attn_bwd.hip", "attn_train.hip",
+           "api.hip"]
 ARCH = os.environ.get("FOCUS_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -3,6 +3,7 @@
 // kernel launchers.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include <algorithm>
@@ -72,6 +73,34 @@ focus_status check_attn(const void *q, const void *k, const void *v, focus_dtype
 int64_t all_pairs_window(int32_t K, int32_t topk, int64_t n, int64_t window)
 {
     return 2 * (int64_t)topk > K ? std::max(window, n) : window;
+}
+
+// FOCUS_DEBUG=1 in the environment (read at every call, so a process can
+// switch it on and off) makes the entry points that index rows through a
+// bucketing check it first.
+bool debug_checks()
+{
+    const char *v = std::getenv("FOCUS_DEBUG");
+    return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+// Runs the bucketing check on the stream (synchronously) with the first bytes
+// of `ws` as its flag word; INVALID_ARGUMENT names the failed checks.
+focus_status check_buckets(const uint32_t *gmask, const int32_t *offsets, const int32_t *tokens,
+                           const int32_t *slot_entry, int32_t H, int64_t n, int32_t K,
+                           int32_t topk, void *ws, hipStream_t stream)
+{
+    uint32_t found = 0u;
+    hipError_t e = launch_check_buckets(gmask, offsets, tokens, slot_entry, H, n, K, topk, ws,
+                                        stream, &found);
+    if (e != hipSuccess)
+        return hip_failure(e, "bucket check");
+    if (found == 0u)
+        return FOCUS_OK;
+    return invalid("buckets inconsistent with the routing:%s%s%s%s",
+                   (found & 1u) ? " offsets" : "", (found & 2u) ? " tokens" : "",
+                   (found & 4u) ? " groups/partners/gmask" : "",
+                   (found & 8u) ? " slot_entry" : "");
 }
 
 }  // namespace
@@ -205,6 +234,34 @@ size_t focus_attn_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64
     return attn_workspace_bytes(sh);
 }
 
+size_t focus_attn_fwd_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
+                                      int32_t d, int32_t K, int32_t topk)
+{
+    return focus_attn_workspace_bytes(dt, Hq, Hkv, n, d, K, topk);
+}
+
+focus_status focus_check_buckets(const uint32_t *gmask, const int32_t *offsets,
+                                 const int32_t *tokens, const int32_t *slot_entry, int32_t H,
+                                 int64_t n, int32_t K, int32_t topk, void *workspace,
+                                 size_t workspace_bytes, focus_stream stream)
+{
+    g_last_error[0] = 0;
+    FOCUS_PTR(gmask);
+    FOCUS_PTR(offsets);
+    FOCUS_PTR(tokens);
+    FOCUS_PTR(slot_entry);
+    FOCUS_REQUIRE(H >= 1 && n >= 1 && K >= 1, "H=%d n=%lld K=%d", H, (long long)n, K);
+    if (K > kMaxGroups)
+        return unsupported("at most 32 centroids");
+    FOCUS_REQUIRE(topk >= 1 && topk <= K, "topk=%d K=%d", topk, K);
+    FOCUS_REQUIRE(n * (int64_t)topk <= INT32_MAX, "n*topk exceeds int32");
+    if (workspace == nullptr || workspace_bytes < FOCUS_CHECK_WORKSPACE_BYTES ||
+        !aligned16(workspace))
+        return short_workspace(workspace_bytes, FOCUS_CHECK_WORKSPACE_BYTES);
+    return check_buckets(gmask, offsets, tokens, slot_entry, H, n, K, topk, workspace,
+                         static_cast<hipStream_t>(stream));
+}
+
 focus_status focus_attn_fwd_part(const void *q, const void *k, const void *v, focus_dtype dt,
                                  int32_t Hq, int32_t Hkv, int64_t n, int32_t d,
                                  const uint32_t *gmask, const int32_t *offsets,
@@ -235,6 +292,13 @@ focus_status focus_attn_fwd_part(const void *q, const void *k, const void *v, fo
     const size_t need = attn_workspace_bytes(sh);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return short_workspace(workspace_bytes, need);
+    // (the check's flag word sits in workspace bytes that PREPARE rewrites)
+    if ((parts & FOCUS_PART_PREPARE) && debug_checks()) {
+        st = check_buckets(gmask, offsets, tokens, slot_entry, Hkv, n, K, topk, workspace,
+                           static_cast<hipStream_t>(stream));
+        if (st != FOCUS_OK)
+            return st;
+    }
     hipError_t e = launch_attn(sh, q, k, v, gmask, offsets, tokens, slot_entry, out, lse,
                                workspace, parts, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_attn_fwd launch");
@@ -298,6 +362,12 @@ focus_status focus_attn_bwd(const void *q, const void *k, const void *v, const v
     const size_t need = attn_bwd_workspace_bytes(sh);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return short_workspace(workspace_bytes, need);
+    if (debug_checks()) {
+        st = check_buckets(gmask, offsets, tokens, slot_entry, Hkv, n, K, topk, workspace,
+                           static_cast<hipStream_t>(stream));
+        if (st != FOCUS_OK)
+            return st;
+    }
     hipError_t e = launch_attn_bwd(sh, q, k, v, out, lse, dout, gmask, offsets, tokens,
                                    slot_entry, dq, dk, dv, workspace,
                                    static_cast<hipStream_t>(stream));

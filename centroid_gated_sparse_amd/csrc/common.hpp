@@ -44,6 +44,13 @@ hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int top
                          int32_t *offsets, int32_t *tokens, int32_t *slot_entry,
                          void *ws, hipStream_t s);
 
+// ---- check.hip: consistency of a bucketing with its routing (synchronous:
+// waits for the stream, then stores the failed-check bits in *found)
+hipError_t launch_check_buckets(const uint32_t *gmask, const int32_t *offsets,
+                                const int32_t *tokens, const int32_t *slot_entry, int H,
+                                int64_t n, int K, int topk, void *ws, hipStream_t s,
+                                uint32_t *found);
+
 // ---- attn.hip
 struct AttnShape {
     focus_dtype dt;

@@ -4,7 +4,7 @@ the library's HIP kernels.  Raises if the library has not been built or a
 call returns an error status.
 
 The call names match the C ABI: focus_route, focus_route_project,
-focus_bucket, focus_attn_fwd (+ focus_attn_fwd_part), focus_attn_bwd,
+focus_bucket, focus_check_buckets, focus_attn_fwd (+ focus_attn_fwd_part), focus_attn_bwd,
 focus_sinkhorn, focus_gated_attn_fwd, focus_dense_causal_fwd.  ``focus_forward`` chains
 the three calls and allocates outputs and workspaces with torch.
 """
@@ -21,12 +21,14 @@ PART_PREPARE = 1
 PART_GROUP = 2
 PART_WINDOW = 4
 PART_ALL = 7
+CHECK_WORKSPACE_BYTES = 256  # FOCUS_CHECK_WORKSPACE_BYTES
 
 # exported symbols (all declared in include/focus.h)
 SYMBOLS = (
     "focus_status_string", "focus_last_error", "focus_abi_version",
     "focus_route", "focus_route_project", "focus_bucket_workspace_bytes", "focus_bucket",
-    "focus_attn_workspace_bytes", "focus_attn_fwd", "focus_attn_fwd_part",
+    "focus_attn_fwd_workspace_bytes", "focus_attn_workspace_bytes", "focus_check_buckets",
+    "focus_attn_fwd", "focus_attn_fwd_part",
     "focus_dense_workspace_bytes", "focus_dense_causal_fwd",
     "focus_attn_bwd_workspace_bytes", "focus_attn_bwd",
     "focus_sinkhorn_workspace_bytes", "focus_sinkhorn", "focus_gated_attn_workspace_bytes",
@@ -65,8 +67,10 @@ def lib() -> ctypes.CDLL:
     L.focus_bucket_workspace_bytes.argtypes = [i32, i64, i32, i32]
     L.focus_bucket_workspace_bytes.restype = sz
     L.focus_bucket.argtypes = [P, i32, i64, i32, i32, P, P, P, P, sz, P]
-    L.focus_attn_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i64, i32, i32, i32]
-    L.focus_attn_workspace_bytes.restype = sz
+    for name in ("focus_attn_fwd_workspace_bytes", "focus_attn_workspace_bytes"):
+        getattr(L, name).argtypes = [ctypes.c_int, i32, i32, i64, i32, i32, i32]
+        getattr(L, name).restype = sz
+    L.focus_check_buckets.argtypes = [P, P, P, P, i32, i64, i32, i32, P, sz, P]
     attn = [P, P, P, ctypes.c_int, i32, i32, i64, i32, P, P, P, P, i32, i32, i64, f32,
             P, P, P, sz]
     L.focus_attn_fwd.argtypes = attn + [P]
@@ -86,7 +90,8 @@ def lib() -> ctypes.CDLL:
     L.focus_gated_attn_workspace_bytes.restype = sz
     L.focus_gated_attn_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i32, i64, i32, P, i32, i64,
                                        f32, f32, P, P, P, sz, P]
-    for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_attn_fwd",
+    for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_check_buckets",
+                 "focus_attn_fwd",
                  "focus_attn_fwd_part", "focus_dense_causal_fwd", "focus_attn_bwd",
                  "focus_sinkhorn", "focus_gated_attn_fwd"):
         getattr(L, name).restype = ctypes.c_int
@@ -200,9 +205,29 @@ def focus_bucket(groups, K: int, offsets=None, tokens=None, slot_entry=None, wor
     return offsets, tokens, slot_entry
 
 
+def focus_attn_fwd_workspace_bytes(dtype_code: int, Hq: int, Hkv: int, n: int, d: int, K: int,
+                                   topk: int) -> int:
+    return int(lib().focus_attn_fwd_workspace_bytes(dtype_code, Hq, Hkv, n, d, K, topk))
+
+
 def focus_attn_workspace_bytes(dtype_code: int, Hq: int, Hkv: int, n: int, d: int, K: int,
                                topk: int) -> int:
+    """The same query as focus_attn_fwd_workspace_bytes, under its earlier name."""
     return int(lib().focus_attn_workspace_bytes(dtype_code, Hq, Hkv, n, d, K, topk))
+
+
+def focus_check_buckets(gmask, offsets, tokens, slot_entry, K: int, workspace=None,
+                        stream=None) -> None:
+    """Raise FocusError (INVALID_ARGUMENT) unless (offsets, tokens, slot_entry)
+    is the bucketing of the routing behind gmask; waits for the stream."""
+    import torch
+
+    H, n, topk = slot_entry.shape
+    if workspace is None:
+        workspace = torch.empty(CHECK_WORKSPACE_BYTES, dtype=torch.uint8, device=gmask.device)
+    _check("focus_check_buckets", lib().focus_check_buckets(
+        _ptr(gmask), _ptr(offsets), _ptr(tokens), _ptr(slot_entry), H, n, K, topk,
+        _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def focus_attn_fwd_part(q, k, v, gmask, offsets, tokens, slot_entry, K: int, window: int,
@@ -233,7 +258,7 @@ def focus_attn_fwd(q, k, v, gmask, offsets, tokens, slot_entry, K: int, window: 
     if lse is None:
         lse = torch.empty((Hq, n), dtype=torch.float32, device=q.device)
     if workspace is None:
-        need = focus_attn_workspace_bytes(_dtype_code(q), Hq, Hkv, n, d, K, topk)
+        need = focus_attn_fwd_workspace_bytes(_dtype_code(q), Hq, Hkv, n, d, K, topk)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check("focus_attn_fwd", lib().focus_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), Hq, Hkv, n, d, _ptr(gmask), _ptr(offsets),

@@ -144,9 +144,14 @@ def qkv_inputs(wl: Workload, seed: int, device="cpu"):
     return draw(wl.hq), draw(wl.hkv), draw(wl.hkv)
 
 
-def sample_rows(wl: Workload, seed: int, count: int):
+def sample_rows(wl: Workload, seed: int, count: int, heads_per_pos: int = 1):
     """Seeded (query head, position) samples: the window and sequence edges
-    first, then distinct random positions, each with a random query head."""
+    first, then distinct random positions, each with a random query head.
+
+    With heads_per_pos > 1 every sampled position is taken with that many
+    distinct random query heads (count positions, count * heads_per_pos
+    rows); the first head of each position is the one heads_per_pos = 1
+    would give."""
     _, _, _, _, s_rows = _streams(seed)
     rng = np.random.default_rng(s_rows)
     n, w = wl.n, wl.window
@@ -157,7 +162,15 @@ def sample_rows(wl: Workload, seed: int, count: int):
     extra = rng.choice(pool, size=min(want, pool.size), replace=False)
     pos = np.concatenate([np.asarray(fixed, np.int64), np.sort(extra).astype(np.int64)])
     heads = rng.integers(0, wl.hq, size=pos.size).astype(np.int32)
-    return heads, pos
+    if heads_per_pos <= 1:
+        return heads, pos
+    hp = min(heads_per_pos, wl.hq)
+    more = np.empty((pos.size, hp), np.int32)
+    more[:, 0] = heads
+    for i in range(pos.size):  # the other heads: distinct, drawn without replacement
+        others = np.delete(np.arange(wl.hq, dtype=np.int32), heads[i])
+        more[i, 1:] = rng.choice(others, size=hp - 1, replace=False)
+    return more.reshape(-1), np.repeat(pos, hp)
 
 
 def to_bf16_bits(t) -> np.ndarray:

@@ -137,7 +137,14 @@ focus_status focus_route_project(const void *x, focus_dtype xdt, int64_t n, int3
  *
  *   groups      int32 [H, n, topk]      from focus_route
  *   offsets     int32 [H, K*(K+1)+1]    out: first entry of each sub-bucket;
- *                                        offsets[h][K*(K+1)] = n * topk
+ *                                        offsets[h][K*(K+1)] = n * topk.
+ *                                        Group g's entries are the run from
+ *                                        offsets[h][g*(K+1)] to
+ *                                        offsets[h][(g+1)*(K+1)] (a stride of
+ *                                        K + 1): every token holding g, each
+ *                                        once, ascending by position inside
+ *                                        each partner sub-bucket (not across
+ *                                        the whole group)
  *   tokens      int32 [H, n*topk]       out: position of each entry
  *   slot_entry  int32 [H, n, topk]      out: entry index of (t, groups[t][s])
  *   workspace   >= focus_bucket_workspace_bytes(...) bytes of device memory
@@ -150,6 +157,35 @@ focus_status focus_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K
                           int32_t topk, int32_t *offsets, int32_t *tokens,
                           int32_t *slot_entry, void *workspace, size_t workspace_bytes,
                           focus_stream stream);
+
+/*
+ * focus_check_buckets — checks that a bucketing is the one focus_bucket builds
+ * from the routing behind gmask, reading every array only inside its extent
+ * (every value is range-tested before it serves as an index):
+ *   offsets     start at 0, never decrease, end at n * topk;
+ *   tokens      in [0, n), strictly ascending inside each sub-bucket;
+ *   groups      each entry's group is a bit of its token's gmask, its
+ *               sub-bucket's partner is the token's lowest other group (K at
+ *               top-1), and every gmask holds exactly topk bits below K;
+ *   slot_entry  slot_entry[t][s] is an entry of token t, and the groups of a
+ *               token's topk entries are exactly its gmask bits.
+ *   gmask, offsets, tokens, slot_entry   as passed to focus_attn_fwd
+ *   workspace   >= FOCUS_CHECK_WORKSPACE_BYTES bytes of device memory
+ * The call is synchronous: it waits for `stream` and returns FOCUS_OK, or
+ * INVALID_ARGUMENT naming the failed checks in focus_last_error().  With
+ * FOCUS_DEBUG=1 in the environment (read at every call), focus_attn_fwd (when
+ * its parts include PREPARE) and focus_attn_bwd run this check on their own
+ * workspace before launching anything that reads rows through the buckets,
+ * and return its status; such calls then synchronise the stream and cannot be
+ * captured into a graph.
+ * (Technical Summary, Key Contributions 5: the within-group call needs the
+ * tokens gathered by group; this validates that gathering.)
+ */
+#define FOCUS_CHECK_WORKSPACE_BYTES 256
+focus_status focus_check_buckets(const uint32_t *gmask, const int32_t *offsets,
+                                 const int32_t *tokens, const int32_t *slot_entry, int32_t H,
+                                 int64_t n, int32_t K, int32_t topk, void *workspace,
+                                 size_t workspace_bytes, focus_stream stream);
 
 /*
  * focus_attn_fwd — exact softmax over A(i) for every query head and row
@@ -170,20 +206,29 @@ focus_status focus_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K
  *   window      w >= 0; w = 0 keeps only group pairs (a token always shares
  *               its own groups, so every row keeps itself); w >= n is dense
  *               causal attention
- *   scale       logit scale (1/sqrt(d) for standard attention)
+ *   scale       logit scale (1/sqrt(d) for standard attention); must be
+ *               positive and finite: the kernels keep a row's running max in
+ *               raw-logit units and decide a lazy rescale there, which takes
+ *               the order of scaled logits to be that of raw ones
  *   out         [Hq, n, d] in dt: softmax-weighted values, bf16 rounded to
  *               nearest even
  *   lse         fp32 [Hq, n]: natural log of sum_j exp(scale * q_i . k_j)
- *   workspace   >= focus_attn_workspace_bytes(...) bytes
+ *   workspace   >= focus_attn_fwd_workspace_bytes(...) bytes
+ *               (focus_attn_workspace_bytes is the same query under its
+ *               earlier name)
  * Errors: INVALID_ARGUMENT for null pointers, n < 1, Hq % Hkv != 0,
- * topk not in [1, K], window < 0, n*topk > INT32_MAX; UNSUPPORTED for
- * d not in {64, 128} or K > 32; WORKSPACE if short.  Buckets that were not
- * built from the routing that produced gmask are undefined input.
+ * topk not in [1, K], window < 0, n*topk > INT32_MAX, scale <= 0; UNSUPPORTED
+ * for d not in {64, 128} or K > 32; WORKSPACE if short.  Buckets that were not
+ * built from the routing that produced gmask are undefined input, unless
+ * FOCUS_DEBUG=1 (see focus_check_buckets), which turns them into
+ * INVALID_ARGUMENT before anything is launched.
  *
  * focus_attn_fwd_part runs a subset of the same work (a focus_part bitmask);
  * the parts must run in the order PREPARE, GROUP, WINDOW on the same
  * workspace, and focus_attn_fwd equals focus_attn_fwd_part(..., FOCUS_PART_ALL).
  */
+size_t focus_attn_fwd_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
+                                      int32_t d, int32_t K, int32_t topk);
 size_t focus_attn_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
                                   int32_t d, int32_t K, int32_t topk);
 focus_status focus_attn_fwd(const void *q, const void *k, const void *v, focus_dtype dt,
@@ -231,8 +276,9 @@ focus_status focus_attn_fwd_part(const void *q, const void *k, const void *v,
  * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are
  * rounded to bf16 as MFMA operands; outputs rounded to nearest even.
  * Deterministic (no atomics): two runs give the same bits.
- * Errors: INVALID_ARGUMENT as focus_attn_fwd; UNSUPPORTED for dt other than
- * FOCUS_BF16, d not in {64, 128} or K > 32; WORKSPACE if short.
+ * Errors: INVALID_ARGUMENT as focus_attn_fwd (FOCUS_DEBUG=1 checks the
+ * buckets first, as there); UNSUPPORTED for dt other than FOCUS_BF16, d not
+ * in {64, 128} or K > 32; WORKSPACE if short.
  */
 size_t focus_attn_bwd_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
                                       int32_t d, int32_t K, int32_t topk);
@@ -298,7 +344,10 @@ focus_status focus_gated_attn_fwd(const void *q, const void *k, const void *v, f
  * focus_dense_causal_fwd — plain causal attention (every j <= i) with the
  * same window kernel and layouts; the dense baseline that Focus is compared
  * against (thelatestinai.com Table 6 compares against full attention).
- * Not part of the method.  Arguments as in focus_attn_fwd.
+ * Not part of the method.  Arguments as in focus_attn_fwd; unlike a plain
+ * attention call it takes a workspace (>= focus_dense_workspace_bytes(...)
+ * bytes), where the keys are copied zero-padded and the values transposed,
+ * the layouts the window kernel reads.
  */
 size_t focus_dense_workspace_bytes(focus_dtype dt, int32_t Hkv, int64_t n, int32_t d);
 focus_status focus_dense_causal_fwd(const void *q, const void *k, const void *v,

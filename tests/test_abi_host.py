@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(F.SYMBOLS)
@@ -54,6 +54,10 @@ def test_workspace_sizes(L):
     assert F.focus_attn_workspace_bytes(F.FOCUS_BF16, hq, hkv, n, 96, K, k) == 0
     assert F.focus_attn_workspace_bytes(F.FOCUS_BF16, 6, 4, n, d, K, k) == 0
     assert F.focus_dense_workspace_bytes(F.FOCUS_F32, 2, 512, 64) > 0
+    # the workspace query under both of its names
+    for args in [(F.FOCUS_BF16, hq, hkv, n, d, K, k), (F.FOCUS_F32, 2, 2, 512, 64, 4, 1),
+                 (F.FOCUS_BF16, hq, hkv, n, 96, K, k)]:
+        assert F.focus_attn_fwd_workspace_bytes(*args) == F.focus_attn_workspace_bytes(*args)
 
 
 # An aligned non-null address.  Every call below carries at least one invalid
@@ -206,3 +210,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(F, "LIB_PATH", tmp_path / "missing.so")
     with pytest.raises(RuntimeError, match="not built"):
         F.lib()
+
+
+@no_gpu
+def test_check_buckets_rejects_bad_arguments(L):
+    # gmask, offsets, tokens, slot_entry, H, n, K, topk, workspace, bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, 8, 1000, 8, 2, FAKE, F.CHECK_WORKSPACE_BYTES, None]
+
+    def call(**over):
+        a = list(ok)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return L.focus_check_buckets(*a)
+
+    assert call(a0=None) == 1                      # gmask null
+    assert call(a2=FAKE + 4) == 1                  # tokens misaligned
+    assert call(a4=0) == 1                         # H < 1
+    assert call(a5=0) == 1                         # n < 1
+    assert call(a6=33) == 2                        # K > 32
+    assert call(a7=9) == 1                         # topk > K
+    assert call(a5=1 << 31) == 1                   # n * topk > INT32_MAX
+    assert call(a8=None) == 3                      # no workspace
+    assert call(a9=F.CHECK_WORKSPACE_BYTES - 1) == 3
+

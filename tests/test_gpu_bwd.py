@@ -65,6 +65,11 @@ CASES = [
     W("bwd_gqa4_d128_top2_n1100", 1100, 8, 2, 128, 4, 2, 64, "bf16", qkv_std=0.3),
     # 2 top-k > K: every pair shares a group, all of them in the window pass
     W("bwd_d128_k4_top3_allpairs", 500, 4, 2, 128, 4, 3, 24, "bf16", qkv_std=0.6),
+    # K = 16 and 32 (thelatestinai.com Table 9): up to 1056 partner
+    # sub-buckets per head; at top-3 the per-key owner test runs in both passes
+    W("bwd_gqa_d128_k16_top3_owner", 900, 4, 2, 128, 16, 3, 16, "bf16", qkv_std=0.5),
+    W("bwd_gqa_d128_k32_top2", 1200, 4, 1, 128, 32, 2, 32, "bf16", qkv_std=0.5),
+    W("bwd_mha_d64_k32_top3_owner", 800, 2, 2, 64, 32, 3, 8, "bf16", qkv_std=0.7),
 ]
 
 

@@ -126,6 +126,16 @@ def test_bucket_chunk_lengths_bitexact(H, n, K, topk):
 # ----------------------------------------------------------------------------
 # attention, element by element on shapes the oracle evaluates in full
 
+def skewed(K):
+    """Group frequencies falling geometrically (ratio 0.8) over K groups."""
+    p = 0.8 ** np.arange(K)
+    return tuple(float(x) for x in p / p.sum())
+
+
+SKEW16 = skewed(16)
+SKEW32 = skewed(32)
+
+
 def W(name, n, hq, hkv, d, K, topk, w, dtype, **kw):
     std = 1.0 if dtype == "f32" else 1.0 / math.sqrt(d)
     kw.setdefault("qkv_std", std)
@@ -157,6 +167,19 @@ SMALL = [
     # 2 top-k > K: every pair shares a group, all of them in the window pass
     W("bf16_d128_k4_top3_allpairs", 700, 4, 2, 128, 4, 3, 40, "bf16"),
     W("f32_d64_k3_top2_allpairs", 350, 2, 1, 64, 3, 2, 16, "f32"),
+    # K = 16 and 32 (thelatestinai.com Table 9 ablates K up to 32): K + 1
+    # partner sub-buckets per group, up to 1056 per head; skewed group
+    # frequencies make crowded and near-empty buckets side by side, and at
+    # top-3 (2 top-k <= K) the per-key owner test runs on the tiles whose
+    # partner is below g
+    W("bf16_d128_gqa4_k16_top2", 1500, 8, 2, 128, 16, 2, 48, "bf16", z_probs=SKEW16),
+    W("bf16_d128_gqa4_k16_top3_owner", 1500, 8, 2, 128, 16, 3, 40, "bf16", z_probs=SKEW16),
+    W("bf16_d128_gqa4_k32_top2", 2500, 8, 2, 128, 32, 2, 64, "bf16", z_probs=SKEW32),
+    W("bf16_d128_gqa4_k32_top3_owner", 2500, 8, 2, 128, 32, 3, 64, "bf16", z_probs=SKEW32),
+    W("bf16_d64_k32_top3_owner", 1200, 4, 4, 64, 32, 3, 16, "bf16", z_probs=SKEW32),
+    # fp32 path: pure group attention, and the owner test at top-3 of 8
+    W("f32_d64_w0", 600, 2, 2, 64, 4, 2, 0, "f32"),
+    W("f32_d128_k8_top3_owner", 500, 4, 2, 128, 8, 3, 24, "f32"),
 ]
 
 
@@ -244,8 +267,12 @@ def test_parts_and_determinism():
 # the workloads at full size: sampled rows against the oracle, every row
 # against the exact count
 
+# sampled positions per workload (None: every row) and query heads checked at
+# each position; the 1M-token workload is checked on 4096 seeded positions,
+# three query heads each
 SAMPLED_ROWS = {"tiny_fp32_n512": None, "gpt2_n8k": 2048, "gpt2_n64k": 4096,
-                "gqa7b_n128k_skew": 4096, "gqa7b_n1m_k8": 1024}
+                "gqa7b_n128k_skew": 4096, "gqa7b_n1m_k8": 4096}
+HEADS_PER_POS = {"gqa7b_n1m_k8": 3}
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -263,7 +290,7 @@ def test_workload_full_size(name):
         rh = np.repeat(np.arange(wl.hq, dtype=np.int32), wl.n)
         rp = np.tile(np.arange(wl.n, dtype=np.int64), wl.hq)
     else:
-        rh, rp = sample_rows(wl, seed, nrows)
+        rh, rp = sample_rows(wl, seed, nrows, HEADS_PER_POS.get(name, 1))
     log(f"workload {name}: oracle on {len(rh)} rows")
     check_rows(wl, res, q, k, v, g_ref, rh, rp, name)
     del res

@@ -182,9 +182,12 @@ def _run(q, k, v, groups, K, w, scale):
     return oracle.attn_full(q, k, v, groups, K, w, scale)
 
 
-@pytest.mark.parametrize("case", ["K1", "window_ge_n", "topk_majority", "same_sets"])
+DENSE_CASE_SEEDS = {"K1": 1101, "window_ge_n": 1102, "topk_majority": 1103, "same_sets": 1104}
+
+
+@pytest.mark.parametrize("case", list(DENSE_CASE_SEEDS))
 def test_attn_reduces_to_dense_causal(case):
-    rng = np.random.default_rng(hash(case) % 2**32)
+    rng = np.random.default_rng(DENSE_CASE_SEEDS[case])
     hq, hkv, n, d = 4, 2, 150, 32
     q, k, v = _rand_qkv(rng, hq, hkv, n, d)
     scale = 1 / math.sqrt(d)
