@@ -234,6 +234,39 @@ size_t focus_attn_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64
     return attn_workspace_bytes(sh);
 }
 
+focus_status focus_bucket_noalloc(const int32_t *groups, int32_t H, int64_t n, int32_t K,
+                                  int32_t topk, int32_t *offsets, int32_t *tokens,
+                                  int32_t *slot_entry, focus_stream stream)
+{
+    g_last_error[0] = 0;
+    FOCUS_PTR(groups);
+    FOCUS_PTR(offsets);
+    FOCUS_PTR(tokens);
+    FOCUS_PTR(slot_entry);
+    FOCUS_REQUIRE(H >= 1 && n >= 1 && K >= 1, "H=%d n=%lld K=%d", H, (long long)n, K);
+    if (K > kMaxGroups)
+        return unsupported("at most 32 centroids");
+    FOCUS_REQUIRE(topk >= 1 && topk <= K, "topk=%d K=%d", topk, K);
+    FOCUS_REQUIRE(n * (int64_t)topk <= INT32_MAX, "n*topk exceeds int32");
+    const size_t need = bucket_workspace_bytes(H, n, K, topk);
+    if (need > FOCUS_BUCKET_NOALLOC_SCRATCH_BYTES) {
+        set_error("focus_bucket_noalloc: this shape needs %zu bytes of count scratch, more "
+                  "than the library's fixed %zu (use focus_bucket with a workspace)",
+                  need, (size_t)FOCUS_BUCKET_NOALLOC_SCRATCH_BYTES);
+        return FOCUS_ERR_WORKSPACE;
+    }
+    void *ws = nullptr;
+    size_t have = 0;
+    hipError_t e = bucket_noalloc_scratch(&ws, &have);
+    if (e != hipSuccess)
+        return hip_failure(e, "focus_bucket_noalloc scratch address");
+    if (have < need)
+        return short_workspace(have, need);
+    e = launch_bucket(groups, H, n, K, topk, offsets, tokens, slot_entry, ws,
+                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_bucket_noalloc launch");
+}
+
 size_t focus_attn_fwd_workspace_bytes(focus_dtype dt, int32_t Hq, int32_t Hkv, int64_t n,
                                       int32_t d, int32_t K, int32_t topk)
 {

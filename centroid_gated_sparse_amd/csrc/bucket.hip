@@ -16,6 +16,8 @@
 // A scatter wavefront settles one sub-bucket key per pass, so its time grows
 // with the chunk, not with n: short sequences take short chunks (down to one
 // wavefront width) so that there are enough wavefronts to spread them.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace focus {
@@ -250,7 +252,41 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
     }
 }
 
+// Scratch of focus_bucket_noalloc: the per-chunk sub-bucket counts, one int
+// per (head, sub-bucket, chunk), as the workspace of focus_bucket holds them.
+// Each device the library runs on keeps its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not the device array:
+// the device address comes from hipGetSymbolAddress (bucket_noalloc_scratch).
+static __device__ __align__(256) int32_t scratch[FOCUS_BUCKET_NOALLOC_SCRATCH_BYTES / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+// Device address of this device's scratch array, looked up once per device
+// (with that device current) and kept.
+hipError_t bucket_noalloc_scratch(void **ptr, size_t *bytes)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
 
 // Tokens per chunk: kChunkMax, halved (down to kChunkMin) while the heads
 // have fewer than kChunkWaves chunks between them.

@@ -43,6 +43,8 @@ size_t bucket_workspace_bytes(int H, int64_t n, int K, int topk);
 hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int topk,
                          int32_t *offsets, int32_t *tokens, int32_t *slot_entry,
                          void *ws, hipStream_t s);
+// device address and size of the current device's focus_bucket_noalloc scratch
+hipError_t bucket_noalloc_scratch(void **ptr, size_t *bytes);
 
 // ---- check.hip: consistency of a bucketing with its routing (synchronous:
 // waits for the stream, then stores the failed-check bits in *found)

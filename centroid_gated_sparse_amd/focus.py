@@ -27,6 +27,7 @@ CHECK_WORKSPACE_BYTES = 256  # FOCUS_CHECK_WORKSPACE_BYTES
 SYMBOLS = (
     "focus_status_string", "focus_last_error", "focus_abi_version",
     "focus_route", "focus_route_project", "focus_bucket_workspace_bytes", "focus_bucket",
+    "focus_bucket_noalloc",
     "focus_attn_fwd_workspace_bytes", "focus_attn_workspace_bytes", "focus_check_buckets",
     "focus_attn_fwd", "focus_attn_fwd_part",
     "focus_dense_workspace_bytes", "focus_dense_causal_fwd",
@@ -67,6 +68,7 @@ def lib() -> ctypes.CDLL:
     L.focus_bucket_workspace_bytes.argtypes = [i32, i64, i32, i32]
     L.focus_bucket_workspace_bytes.restype = sz
     L.focus_bucket.argtypes = [P, i32, i64, i32, i32, P, P, P, P, sz, P]
+    L.focus_bucket_noalloc.argtypes = [P, i32, i64, i32, i32, P, P, P, P]
     for name in ("focus_attn_fwd_workspace_bytes", "focus_attn_workspace_bytes"):
         getattr(L, name).argtypes = [ctypes.c_int, i32, i32, i64, i32, i32, i32]
         getattr(L, name).restype = sz
@@ -90,7 +92,8 @@ def lib() -> ctypes.CDLL:
     L.focus_gated_attn_workspace_bytes.restype = sz
     L.focus_gated_attn_fwd.argtypes = [P, P, P, ctypes.c_int, i32, i32, i64, i32, P, i32, i64,
                                        f32, f32, P, P, P, sz, P]
-    for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_check_buckets",
+    for name in ("focus_route", "focus_route_project", "focus_bucket", "focus_bucket_noalloc",
+                 "focus_check_buckets",
                  "focus_attn_fwd",
                  "focus_attn_fwd_part", "focus_dense_causal_fwd", "focus_attn_bwd",
                  "focus_sinkhorn", "focus_gated_attn_fwd"):
@@ -202,6 +205,30 @@ def focus_bucket(groups, K: int, offsets=None, tokens=None, slot_entry=None, wor
     _check("focus_bucket", lib().focus_bucket(_ptr(groups), H, n, K, topk, _ptr(offsets),
                                               _ptr(tokens), _ptr(slot_entry), _ptr(workspace),
                                               workspace.numel(), _stream(stream)))
+    return offsets, tokens, slot_entry
+
+
+BUCKET_NOALLOC_SCRATCH_BYTES = 16 << 20  # FOCUS_BUCKET_NOALLOC_SCRATCH_BYTES
+
+
+def focus_bucket_noalloc(groups, K: int, offsets=None, tokens=None, slot_entry=None,
+                         stream=None):
+    """focus_bucket without a workspace (the library's fixed per-device
+    scratch holds the counts).  The C call allocates nothing; this wrapper
+    allocates only the outputs that are not passed in."""
+    import torch
+
+    H, n, topk = groups.shape
+    dev = groups.device
+    if offsets is None:
+        offsets = torch.empty((H, K * (K + 1) + 1), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((H, n * topk), dtype=torch.int32, device=dev)
+    if slot_entry is None:
+        slot_entry = torch.empty((H, n, topk), dtype=torch.int32, device=dev)
+    _check("focus_bucket_noalloc", lib().focus_bucket_noalloc(
+        _ptr(groups), H, n, K, topk, _ptr(offsets), _ptr(tokens), _ptr(slot_entry),
+        _stream(stream)))
     return offsets, tokens, slot_entry
 
 

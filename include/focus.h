@@ -159,6 +159,26 @@ focus_status focus_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K
                           focus_stream stream);
 
 /*
+ * focus_bucket_noalloc — focus_bucket for callers that cannot allocate device
+ * memory or pass a workspace (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs and errors as
+ * focus_bucket, minus the workspace: the per-chunk counts go to a fixed
+ * scratch array inside the library, FOCUS_BUCKET_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) on each device it runs on, held until the process ends.  Shapes
+ * whose focus_bucket_workspace_bytes(H, n, K, topk) exceeds that return
+ * FOCUS_ERR_WORKSPACE with nothing launched (for example H = 8, n = 1M, K = 8,
+ * topk = 2 needs 4.5 MiB and fits; K = 32 at that n does not).  The call
+ * allocates nothing.  Every call on a device shares that device's scratch,
+ * and each call rewrites every count it reads (nothing has to start at
+ * zero); calls that overlap on one device (other streams or threads) race
+ * and must be serialised by the caller.
+ */
+#define FOCUS_BUCKET_NOALLOC_SCRATCH_BYTES (16u << 20)
+focus_status focus_bucket_noalloc(const int32_t *groups, int32_t H, int64_t n, int32_t K,
+                                  int32_t topk, int32_t *offsets, int32_t *tokens,
+                                  int32_t *slot_entry, focus_stream stream);
+
+/*
  * focus_check_buckets — checks that a bucketing is the one focus_bucket builds
  * from the routing behind gmask, reading every array only inside its extent
  * (every value is range-tested before it serves as an index):

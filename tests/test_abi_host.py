@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(F.SYMBOLS)
@@ -233,3 +233,21 @@ def test_check_buckets_rejects_bad_arguments(L):
     assert call(a8=None) == 3                      # no workspace
     assert call(a9=F.CHECK_WORKSPACE_BYTES - 1) == 3
 
+
+@no_gpu
+def test_bucket_noalloc_rejects_bad_arguments(L):
+    # groups, H, n, K, topk, offsets, tokens, slot_entry, stream
+    ok = [FAKE, 2, 100, 4, 2, FAKE, FAKE, FAKE, None]
+    bad = list(ok); bad[0] = None
+    assert L.focus_bucket_noalloc(*bad) == 1       # groups null
+    bad = list(ok); bad[4] = 5
+    assert L.focus_bucket_noalloc(*bad) == 1       # topk > K
+    bad = list(ok); bad[3] = 40
+    assert L.focus_bucket_noalloc(*bad) == 2       # K > 32
+    bad = list(ok); bad[2] = 1 << 31
+    assert L.focus_bucket_noalloc(*bad) == 1       # n * topk > INT32_MAX
+    # beyond the fixed scratch: 8 heads of 1M tokens at K = 32 need 66 MiB of counts
+    big = [FAKE, 8, 1 << 20, 32, 2, FAKE, FAKE, FAKE, None]
+    assert F.focus_bucket_workspace_bytes(8, 1 << 20, 32, 2) > F.BUCKET_NOALLOC_SCRATCH_BYTES
+    assert L.focus_bucket_noalloc(*big) == 3
+    assert b"scratch" in L.focus_last_error()
