@@ -99,6 +99,17 @@ struct Tile<D, true> {
         for (int ks = 0; ks < KS; ++ks)
             qf.v[ks] = src[ks * 2 + h];
     }
+    // sum of squares of the query elements this lane holds (half of them)
+    __device__ static float q_sq_half(const QFrag &qf)
+    {
+        float a = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                a = __builtin_fmaf((float)qf.v[ks][e], (float)qf.v[ks][e], a);
+        return a;
+    }
 
     // Start the loads of one key tile straight into LDS (issued by the four
     // role-A wavefronts only; role B, on the critical path, issues none):
@@ -286,6 +297,14 @@ struct Tile<D, false> {
         for (int ks = 0; ks < KS; ++ks)
             qf.v[ks] = q[row_off + ks * 2 + h];
     }
+    __device__ static float q_sq_half(const QFrag &qf)
+    {
+        float a = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a = __builtin_fmaf(qf.v[ks], qf.v[ks], a);
+        return a;
+    }
 
     __device__ static void prefetch(Staged &st, const Params &p, int kvh, int64_t row0, char *,
                                     char *)
@@ -399,39 +418,55 @@ struct Acc {
         l = 0.f;
     }
 
+    // Fixed exponent offset: m is set once to a bound on every logit of the
+    // wavefront's rows (see kFixedOffsetMax) and never moves.
+    __device__ void init_fixed(float m_bound)
+    {
+        init();
+        m = m_bound;
+        negm = -m_bound;
+    }
+
     // Fold one tile of raw logits into the state; P receives the
     // probabilities for the PV product.
     //
-    // Lazy rescale: the running max only moves when a row's max grew by
-    // more than 2^8, so P stays below 2^8 and O is rarely rescaled.  The
-    // test needs no exchange between the lane halves: the row max exceeds
-    // the row's threshold exactly when one of its halves does, and the
-    // wavefront takes the update when any lane's does.  Only the update
-    // forms the row max; the threshold and the exponent offset are kept
-    // with m, so a tile that leaves m alone costs the half maxima and one
-    // compare.  (c > 0: the entry points require a positive scale.)
+    // FIXED: the offset is a bound on the logits, so P <= 1 and nothing is
+    // ever rescaled: the tile costs its exponentials, their sum and the bf16
+    // conversion.
+    //
+    // Otherwise a lazy rescale: the running max only moves when a row's max
+    // grew by more than 2^8, so P stays below 2^8 and O is rarely rescaled.
+    // The test needs no exchange between the lane halves: the row max
+    // exceeds the row's threshold exactly when one of its halves does, and
+    // the wavefront takes the update when any lane's does.  Only the update
+    // forms the row max; the threshold and the exponent offset are kept with
+    // m, so a tile that leaves m alone costs the half maxima and one compare.
+    // (c > 0: the entry points require a positive scale.)
+    template <bool FIXED>
     __device__ void softmax(const f32x16 (&s)[2], float c, typename TL::PFrag &pf)
     {
-        float t = -INFINITY;
+        if constexpr (!FIXED) {
+            float t = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                t = fmaxf(t, s[kb][r]);
-        if (__builtin_amdgcn_ballot_w64(t > thr) != 0) {
-            const float mx = swap_halves_max(t) * c;
-            const float m_new = fmaxf(m, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-            m = m_new;
-            negm = -m_use;
-            thr = (m_new + kLazyRescale) / c;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < TL::DB; ++db)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    o[db][r] *= alpha;
+                    t = fmaxf(t, s[kb][r]);
+            if (__builtin_amdgcn_ballot_w64(t > thr) != 0) {
+                const float mx = swap_halves_max(t) * c;
+                const float m_new = fmaxf(m, mx);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+                m = m_new;
+                negm = -m_use;
+                thr = (m_new + kLazyRescale) / c;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < TL::DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        o[db][r] *= alpha;
+            }
         }
         l += TL::exp_tile(s, c, negm, pf);
     }
@@ -579,8 +614,30 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             aq[j] = arow[2 * j + h];
     }
 
+    // |q_i . k_j| <= |q_i| kmax for every key of this key/value head (the
+    // largest of the per-block maxima the prepare pass left); the margin
+    // covers the rounding of the norms and of the products' fp32 sums.
+    // Lanes without a query row take -inf: they never bound the wavefront.
+    float kmax = p.kpart[(int64_t)kvh * kNormBlocks + lane % kNormBlocks];
+#pragma unroll
+    for (int o = kNormBlocks / 2; o >= 1; o >>= 1)
+        kmax = fmaxf(kmax, __shfl_xor(kmax, o));
+    float qbound = qvalid ? __builtin_sqrtf(swap_halves_sum(TL::q_sq_half(qf))) : 0.f;
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1)
+        qbound = fmaxf(qbound, __shfl_xor(qbound, o));
+    // every scaled logit of this wavefront lies in [-mb, mb] (log2 units)
+    const float mb = __uint_as_float(__builtin_amdgcn_readfirstlane(
+        __float_as_uint(p.c * qbound * kmax * (1.f + 1.f / 256.f))));
+    // With mb <= kFixedOffsetMax the offset m = mb needs no running max:
+    // every P = 2^(c s - mb) lies in [2^-2mb, 1], inside the normal range of
+    // fp32 and bf16, and fp32 keeps its relative precision at any scale.
+    const bool fixed_offset = BF16 && mb <= kFixedOffsetMax;
     Acc<TL> acc;
-    acc.init();
+    if (fixed_offset)
+        acc.init_fixed(mb);
+    else
+        acc.init();
 
     // ---- key tile schedule
     const int w = p.window;
@@ -823,7 +880,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // `nxt`; one barrier per tile.  The two LDS buffers are distinct
         // arrays and the loop is unrolled by two, so each LDS read names one
         // buffer and each LDS write the other.
-        auto step = [&](int t, auto CUR, auto NXT) {
+        auto step = [&](int t, auto CUR, auto NXT, auto FIXED) {
             const int valid = cur_valid;
             const int owner = cur_owner;
             const bool has_next = t + 1 < n_tiles_total;
@@ -843,7 +900,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             TL::refresh(lo);
             scores(s, CUR, valid, owner);
             typename TL::PFrag pf;
-            acc.softmax(s, p.c, pf);
+            acc.template softmax<decltype(FIXED)::value>(s, p.c, pf);
             TL::pv(acc.o, pf, stage(CUR).v, lo);
             if (has_next) {
                 TL::land(st, stage(NXT).k, stage(NXT).v);
@@ -852,11 +909,15 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         };
-        for (int t = 0; t < n_tiles_total; t += 2) {
-            step(t, I0{}, I1{});
-            if (t + 1 < n_tiles_total)
-                step(t + 1, I1{}, I0{});
-        }
+        auto loop = [&](auto FIXED) {
+            for (int t = 0; t < n_tiles_total; t += 2) {
+                step(t, I0{}, I1{}, FIXED);
+                if (t + 1 < n_tiles_total)
+                    step(t + 1, I1{}, I0{}, FIXED);
+            }
+        };
+        // (one loop, the lazy rescale, keeps the fp32 registers within bounds)
+        loop(std::false_type{});
     } else {
         // Two-role (staggered) schedule.  Each SIMD runs one wavefront of
         // role A (waves 0-3) and one of role B (waves 4-7); one block barrier
@@ -953,8 +1014,9 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         __builtin_amdgcn_s_waitcnt(0x70);
         __syncthreads();
 
-        auto run = [&](auto role_tag) {
+        auto run = [&](auto role_tag, auto fixed_tag) {
             constexpr bool ROLE_A = decltype(role_tag)::value;
+            constexpr bool FIXED = decltype(fixed_tag)::value;
             f32x16 s[2];
             typename TL::PFrag pf;
             auto interval = [&](int u, auto PREV, auto CUR, auto AHEAD, auto FIRST) {
@@ -975,14 +1037,14 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                         scores(s, CUR, ring_valid[decltype(CUR)::value],
                                ring_owner[decltype(CUR)::value]);
                         issue_ahead();
-                        acc.softmax(s, p.c, pf);
+                        acc.template softmax<FIXED>(s, p.c, pf);
                         TL::pv(acc.o, pf, stage(CUR).v, lo);
                     }
                 } else {
                     if constexpr (decltype(FIRST)::value) {
                         issue_ahead();
                     } else {
-                        acc.softmax(s, p.c, pf);
+                        acc.template softmax<FIXED>(s, p.c, pf);
                         issue_ahead();
                         TL::pv(acc.o, pf, stage(PREV).v, lo);
                     }
@@ -1008,10 +1070,17 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                     interval(u + 3, I3{}, I0{}, I2{}, std::false_type{});
             }
         };
-        if (__builtin_amdgcn_readfirstlane(wave) < kWavesPerRole)
-            run(std::true_type{});
-        else
-            run(std::false_type{});
+        if (__builtin_amdgcn_readfirstlane(wave) < kWavesPerRole) {
+            if (fixed_offset)
+                run(std::true_type{}, std::true_type{});
+            else
+                run(std::true_type{}, std::false_type{});
+        } else {
+            if (fixed_offset)
+                run(std::false_type{}, std::true_type{});
+            else
+                run(std::false_type{}, std::false_type{});
+        }
     }
 
     if (!wave_active)
@@ -1140,6 +1209,58 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const T *__restrict__ 
     }
 }
 
+// Largest Euclidean norm of the rows of x [H][n][D] (the keys), as
+// kNormBlocks partial maxima per head: kpart[h][b] covers rows b, b + B, ...
+// of head h (B = rows per block pass times kNormBlocks).  Each row is read by
+// CH consecutive lanes, 16 bytes each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void key_norm_kernel(const T *__restrict__ x, int64_t n,
+                                                       float *__restrict__ kpart)
+{
+    constexpr int CH = D * (int)sizeof(T) / 16;  // 8, 16 or 32 lanes per row
+    constexpr int RPB = 256 / CH;                // rows per block pass
+    const int h = blockIdx.y;
+    const int c = threadIdx.x % CH;
+    float best = 0.f;
+    for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / CH; r < n;
+         r += (int64_t)gridDim.x * RPB) {
+        const uint4 v = reinterpret_cast<const uint4 *>(x + ((int64_t)h * n + r) * D)[c];
+        float ss = 0.f;
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+                ss = __builtin_fmaf(lo, lo, ss);
+                ss = __builtin_fmaf(hi, hi, ss);
+            }
+        } else {
+            const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                __uint_as_float(v.w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ss = __builtin_fmaf(f[i], f[i], ss);
+        }
+#pragma unroll
+        for (int o = 1; o < CH; o <<= 1)  // the CH lanes of one row
+            ss += __shfl_xor(ss, o);
+        best = fmaxf(best, ss);
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1)
+        best = fmaxf(best, __shfl_xor(best, o));
+    __shared__ float wmax[256 / kWave];
+    if (threadIdx.x % kWave == 0)
+        wmax[threadIdx.x / kWave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = wmax[0];
+        for (int i = 1; i < 256 / kWave; ++i)
+            b = fmaxf(b, wmax[i]);
+        kpart[(int64_t)h * kNormBlocks + blockIdx.x] = __builtin_sqrtf(b);
+    }
+}
+
 // bf16 transpose-gather: dst[h][d][col] = src[h][idx(col)][d] for col < cols,
 // zero up to cols_pad.  One block per (head, 64-column tile).
 template <int D>
@@ -1241,7 +1362,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
 struct Layout {
     int hpb, nhg, rows_group, max_tiles;
     int64_t E, e_pad, n_pad;
-    size_t kb, vb, kp, vt, etok, egm, po, pl, tiles, ntiles, total;
+    size_t kb, vb, kp, vt, etok, egm, po, pl, tiles, ntiles, kpart, total;
 };
 
 int heads_per_block(int ratio)
@@ -1281,6 +1402,7 @@ Layout make_layout(const AttnShape &sh)
     L.pl = take((size_t)sh.hq * L.E * 4);
     L.tiles = take((size_t)sh.hkv * L.max_tiles * sizeof(int4));
     L.ntiles = take((size_t)sh.hkv * sizeof(int32_t));
+    L.kpart = take((size_t)sh.hkv * kNormBlocks * sizeof(float));
     L.total = off;
     return L;
 }
@@ -1349,6 +1471,29 @@ hipError_t launch_transpose(int d, const __bf16 *src, const int32_t *tokens, int
     return hipGetLastError();
 }
 
+hipError_t launch_key_norms(int d, bool bf16, const void *k, int64_t n, int H, float *kpart,
+                            hipStream_t s)
+{
+    const dim3 grid(kNormBlocks, (unsigned)H);
+    if (bf16) {
+        auto K = static_cast<const __bf16 *>(k);
+        if (d == 64)
+            hipLaunchKernelGGL((key_norm_kernel<__bf16, 64>), grid, dim3(256), 0, s, K, n, kpart);
+        else
+            hipLaunchKernelGGL((key_norm_kernel<__bf16, 128>), grid, dim3(256), 0, s, K, n, kpart);
+    } else {
+        auto K = static_cast<const float *>(k);
+        if (d == 64)
+            hipLaunchKernelGGL((key_norm_kernel<float, 64>), grid, dim3(256), 0, s, K, n, kpart);
+        else
+            hipLaunchKernelGGL((key_norm_kernel<float, 128>), grid, dim3(256), 0, s, K, n, kpart);
+    }
+    return hipGetLastError();
+}
+
+// bytes of the key-norm partial maxima, at the end of the dense workspaces
+size_t kpart_bytes(int hkv) { return align_up((size_t)hkv * kNormBlocks * sizeof(float), 256); }
+
 }  // namespace
 
 size_t attn_workspace_bytes(const AttnShape &sh) { return make_layout(sh).total; }
@@ -1356,10 +1501,10 @@ size_t attn_workspace_bytes(const AttnShape &sh) { return make_layout(sh).total;
 size_t dense_workspace_bytes(const AttnShape &sh)
 {
     if (sh.dt != FOCUS_BF16)
-        return 256;
+        return kpart_bytes(sh.hkv);
     const int64_t n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
-    // transposed values and a zero-padded copy of the keys
-    return 2 * align_up((size_t)sh.hkv * sh.d * n_pad * 2, 256);
+    // transposed values, a zero-padded copy of the keys, the key norms
+    return 2 * align_up((size_t)sh.hkv * sh.d * n_pad * 2, 256) + kpart_bytes(sh.hkv);
 }
 
 hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const void *v,
@@ -1413,6 +1558,9 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
         hipLaunchKernelGGL(plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets,
                            num_subbuckets(sh.K), L.rows_group, L.max_tiles, tiles, ntiles);
         e = hipGetLastError();
+        if (e == hipSuccess)
+            e = launch_key_norms(sh.d, bf16, k, sh.n, sh.hkv,
+                                 reinterpret_cast<float *>(w + L.kpart), s);
         if (e != hipSuccess)
             return e;
     }
@@ -1430,6 +1578,7 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
     p.slot_entry = slot_entry;
     p.out = out;
     p.lse = lse;
+    p.kpart = reinterpret_cast<const float *>(w + L.kpart);
 
     if (parts & FOCUS_PART_GROUP) {
         Params g = p;
@@ -1483,6 +1632,14 @@ size_t gated_dense_workspace_bytes(const AttnShape &sh)
            align_up((size_t)sh.hkv * n_pad * kGateGroups * 2, 256);
 }
 
+namespace {
+// the key norms sit at the end of a dense workspace of `bytes` bytes
+float *dense_kpart(void *ws, size_t bytes, int hkv)
+{
+    return reinterpret_cast<float *>(static_cast<char *>(ws) + bytes - kpart_bytes(hkv));
+}
+}  // namespace
+
 hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k, const void *v,
                               const float *assign, float lambda, void *out, float *lse, void *ws,
                               hipStream_t s)
@@ -1509,6 +1666,9 @@ hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k,
     hipLaunchKernelGGL(gate_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        assign, sh.n, n_pad, sh.K, ga, total, apack);
     e = hipGetLastError();
+    float *kpart = dense_kpart(ws, gated_dense_workspace_bytes(sh), sh.hkv);
+    if (e == hipSuccess)
+        e = launch_key_norms(sh.d, true, k, sh.n, sh.hkv, kpart, s);
     if (e != hipSuccess)
         return e;
     Params p = base_params(d, L);
@@ -1525,6 +1685,7 @@ hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k,
     p.apack = apack;
     p.gate_w = (int)std::min<int64_t>(sh.window, sh.n);
     p.lam2 = lambda * kLog2e;
+    p.kpart = kpart;
     if (ga == 16)
         return sh.d == 64 ? launch_attn_kernel<64, true, false, 16>(p, s)
                           : launch_attn_kernel<128, true, false, 16>(p, s);
@@ -1555,8 +1716,13 @@ hipError_t launch_dense(const AttnShape &sh, const void *q, const void *k, const
         if (e != hipSuccess)
             return e;
     }
+    float *kpart = dense_kpart(ws, dense_workspace_bytes(sh), sh.hkv);
+    e = launch_key_norms(sh.d, bf16, k, sh.n, sh.hkv, kpart, s);
+    if (e != hipSuccess)
+        return e;
     Params p = base_params(d, L);
     p.q = q;
+    p.kpart = kpart;
     p.kmat = bf16 ? (const void *)kp : k;
     p.vmat = bf16 ? (const void *)vt : v;
     p.krows = bf16 ? n_pad : sh.n;

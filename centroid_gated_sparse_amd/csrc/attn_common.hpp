@@ -13,6 +13,9 @@ constexpr int kKeyTile = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;
+// Largest logit bound (scaled, log2 units) for which the softmax may use the
+// bound itself as its fixed exponent offset: P >= 2^-120 stays normal.
+constexpr float kFixedOffsetMax = 60.0f;
 constexpr int kXcds = 8;
 
 struct Params {
@@ -51,7 +54,12 @@ struct Params {
     const void *apack;
     int gate_w;
     float lam2;  // lambda * log2(e)
+    // per key/value head, kNormBlocks partial maxima of the keys' Euclidean
+    // norms (their largest bounds every key of the head)
+    const float *kpart;
 };
+
+constexpr int kNormBlocks = 64;
 
 constexpr int kGateGroups = 32;  // widest assignment row of the gated pass
 

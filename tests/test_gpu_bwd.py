@@ -39,10 +39,34 @@ def gpu_backward(wl, c, r, q, k, v, dout):
     return res, (dq, dk, dv)
 
 
-def check_grads(tag, got, ref):
+def zero_ref_bound(name, wl, q, k, v, dout):
+    """Largest error a gradient whose exact value is zero may show: the
+    bound on one pair's term, times the rounding of the bf16 P and O that
+    D_i = dO_i . O_i and dS = P (dP - D) pass on (2^-9 each, 2^-7 with room).
+    A row attending to a single key has dS = 0 exactly, so its dq (and, with
+    n = 1, dk) is zero; the GPU's P is 2^(c s - m) rounded to bf16, and
+    unless m happens to equal that key's logit the rounding leaves
+    |D_i - dP_i| of order 2^-9 |dO_i| |v|."""
+    f = lambda t: t.float().cpu().double().numpy()
+    row = np.linalg.norm(f(dout), axis=-1).max() * np.linalg.norm(f(v), axis=-1).max()
+    other = {"dq": k, "dk": q}[name]
+    return 2.0 ** -7 * wl.scale * row * np.abs(f(other)).max()
+
+
+def check_grads(tag, got, ref, zero_bounds=None):
+    """Bar per gradient: max|d| <= MAX_TOL * max|ref| and normwise <= NORM_TOL;
+    a gradient whose reference is exactly zero everywhere is held to
+    zero_bounds[name] instead (see zero_ref_bound)."""
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         gv = g.float().cpu().double().numpy()
         assert np.isfinite(gv).all(), f"{tag} {name} not finite"
+        if not np.any(r):
+            bound = zero_bounds[name]
+            err = np.abs(gv).max()
+            log(f"[{tag}] {name}: reference exactly zero, max|g| = {err:.3e} "
+                f"(bound {bound:.3e})")
+            assert err <= bound, f"{tag} {name}"
+            continue
         scale = max(np.abs(r).max(), 1e-30)
         err_max = np.abs(gv - r).max() / scale
         err_norm = np.linalg.norm(gv - r) / max(np.linalg.norm(r), 1e-30)
@@ -85,7 +109,8 @@ def test_backward_small_all_rows(wl):
     assert np.array_equal(res["groups"].cpu().numpy(), g_ref)
     ref = oracle.attn_bwd(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v),
                           to_bf16_bits(dout), g_ref, wl.K, wl.window, wl.scale)
-    check_grads(wl.name, got, ref)
+    zb = {nm: zero_ref_bound(nm, wl, q, k, v, dout) for nm in ("dq", "dk")}
+    check_grads(wl.name, got, ref, zb)
 
 
 def test_backward_deterministic():
