@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     // With mb <= kFixedOffsetMax the offset m = mb needs no running max:
     // every P = 2^(c s - mb) lies in [2^-2mb, 1], inside the normal range of
     // fp32 and bf16, and fp32 keeps its relative precision at any scale.
-    const bool fixed_offset = BF16 && mb <= kFixedOffsetMax;
+    const bool fixed_offset = BF16 && !GATED && mb <= kFixedOffsetMax;
     Acc<TL> acc;
     if (fixed_offset)
         acc.init_fixed(mb);
@@ -1092,22 +1092,32 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     const float lse2 = (l_tot > 0.f) ? acc.m + __builtin_amdgcn_logf(l_tot) : -INFINITY;
 
     if (GROUP) {
-        // normalised partial O (fp32) and natural-log LSE at the query's entry
+        // normalised partial O (in the I/O dtype: bf16 for bf16 inputs, as
+        // the merged output is) and natural-log LSE at the query's entry
         if (!qvalid)
             return;
         const int64_t e = e_start + qr;
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        float *po = p.part_o + ((int64_t)hq * p.E + e) * D;
+        T *po = static_cast<T *>(p.part_o) + ((int64_t)hq * p.E + e) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                float4 v;
-                v.x = acc.o[db][a * 4 + 0] * inv;
-                v.y = acc.o[db][a * 4 + 1] * inv;
-                v.z = acc.o[db][a * 4 + 2] * inv;
-                v.w = acc.o[db][a * 4 + 3] * inv;
-                *reinterpret_cast<float4 *>(po + db * 32 + a * 8 + h * 4) = v;
+                T *dst = po + db * 32 + a * 8 + h * 4;
+                if constexpr (BF16) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        v[x] = (__bf16)(acc.o[db][a * 4 + x] * inv);
+                    *reinterpret_cast<bf16x4 *>(dst) = v;
+                } else {
+                    float4 v;
+                    v.x = acc.o[db][a * 4 + 0] * inv;
+                    v.y = acc.o[db][a * 4 + 1] * inv;
+                    v.z = acc.o[db][a * 4 + 2] * inv;
+                    v.w = acc.o[db][a * 4 + 3] * inv;
+                    *reinterpret_cast<float4 *>(dst) = v;
+                }
             }
         if (h == 0)
             p.part_lse[(int64_t)hq * p.E + e] = lse2 * kLn2;
@@ -1140,16 +1150,24 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         if (a_s == 0.f)
             continue;
         wsum += a_s;
-        const float *po = p.part_o + ((int64_t)hq * p.E + ent) * D;
+        const T *po = static_cast<const T *>(p.part_o) + ((int64_t)hq * p.E + ent) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const float4 v = *reinterpret_cast<const float4 *>(po + db * 32 + a * 8 + h * 4);
-                res[db][a * 4 + 0] += a_s * v.x;
-                res[db][a * 4 + 1] += a_s * v.y;
-                res[db][a * 4 + 2] += a_s * v.z;
-                res[db][a * 4 + 3] += a_s * v.w;
+                const T *src = po + db * 32 + a * 8 + h * 4;
+                if constexpr (BF16) {
+                    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(src);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        res[db][a * 4 + x] += a_s * (float)v[x];
+                } else {
+                    const float4 v = *reinterpret_cast<const float4 *>(src);
+                    res[db][a * 4 + 0] += a_s * v.x;
+                    res[db][a * 4 + 1] += a_s * v.y;
+                    res[db][a * 4 + 2] += a_s * v.z;
+                    res[db][a * 4 + 3] += a_s * v.w;
+                }
             }
     }
     const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
@@ -1160,7 +1178,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         for (int a = 0; a < 4; ++a) {
             T *dst = orow + db * 32 + a * 8 + h * 4;
             if (BF16) {
-                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
                 bf16x4 v;
                 v[0] = (__bf16)(res[db][a * 4 + 0] * inv);
                 v[1] = (__bf16)(res[db][a * 4 + 1] * inv);
@@ -1398,7 +1415,7 @@ Layout make_layout(const AttnShape &sh)
     L.vt = take(sh.dt == FOCUS_BF16 ? (size_t)sh.hkv * sh.d * L.n_pad * 2 : 0);
     L.etok = take((size_t)sh.hkv * L.e_pad * 4);
     L.egm = take((size_t)sh.hkv * L.e_pad * 4);
-    L.po = take((size_t)sh.hq * L.E * sh.d * 4);
+    L.po = take((size_t)sh.hq * L.E * sh.d * es);  // partial O in the I/O dtype
     L.pl = take((size_t)sh.hq * L.E * 4);
     L.tiles = take((size_t)sh.hkv * L.max_tiles * sizeof(int4));
     L.ntiles = take((size_t)sh.hkv * sizeof(int32_t));
@@ -1573,7 +1590,7 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
     p.etok = reinterpret_cast<const int32_t *>(w + L.etok);
     p.egm = reinterpret_cast<const uint32_t *>(w + L.egm);
     p.estride = L.e_pad;
-    p.part_o = reinterpret_cast<float *>(w + L.po);
+    p.part_o = w + L.po;
     p.part_lse = reinterpret_cast<float *>(w + L.pl);
     p.slot_entry = slot_entry;
     p.out = out;

@@ -39,7 +39,7 @@ struct Params {
     const int32_t *ntiles;
     int max_tiles;
     int64_t E;
-    float *part_o;
+    void *part_o;  // normalised partial O per (query head, entry), I/O dtype
     float *part_lse;
     // window pass
     const int32_t *slot_entry;

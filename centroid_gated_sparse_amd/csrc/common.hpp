@@ -18,6 +18,7 @@ constexpr int kMaxGroups = 32;
 // v_mfma_f32_32x32x16_bf16.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 // Sub-buckets per head: (group, partner) with partner in [0, K].
 inline __host__ __device__ int num_subbuckets(int K) { return K * (K + 1); }

@@ -46,11 +46,14 @@ def test_workspace_sizes(L):
     # bucket: one int per (head, sub-bucket, 512-token chunk)
     assert F.focus_bucket_workspace_bytes(8, 1 << 20, 8, 2) == 8 * 72 * 2048 * 4
     assert F.focus_bucket_workspace_bytes(1, 10, 0, 1) == 0
-    # attention: at least the fp32 partials of every (query head, entry)
+    # attention: at least the partials of every (query head, entry), O in
+    # the I/O dtype and the LSE in fp32, plus the bucket-order K and V^T
     n, hq, hkv, d, K, k = 131072, 32, 8, 128, 4, 2
     ws = F.focus_attn_workspace_bytes(F.FOCUS_BF16, hq, hkv, n, d, K, k)
-    assert ws >= hq * n * k * (d + 1) * 4
-    assert ws < 2 * hq * n * k * (d + 1) * 4 + 4 * hkv * n * k * d * 2
+    assert ws >= hq * n * k * (d * 2 + 4) + 2 * hkv * n * k * d * 2
+    assert ws < 2 * hq * n * k * (d * 2 + 4) + 4 * hkv * (n * k + n) * d * 2
+    ws32 = F.focus_attn_workspace_bytes(F.FOCUS_F32, hq, hkv, n, d, K, k)
+    assert ws32 >= hq * n * k * (d + 1) * 4
     assert F.focus_attn_workspace_bytes(F.FOCUS_BF16, hq, hkv, n, 96, K, k) == 0
     assert F.focus_attn_workspace_bytes(F.FOCUS_BF16, 6, 4, n, d, K, k) == 0
     assert F.focus_dense_workspace_bytes(F.FOCUS_F32, 2, 512, 64) > 0
