@@ -147,7 +147,7 @@ def make_step(F, wl, q, k, v, rt, ct):
     b = {
         "groups": torch.empty((H, n, topk), **i32),
         "gmask": torch.empty((H, n), **i32),
-        "offsets": torch.empty((H, K * (K + 1) + 1), **i32),
+        "offsets": torch.empty((H, F.focus_num_subbuckets(K, topk) + 1), **i32),
         "tokens": torch.empty((H, n * topk), **i32),
         "slot_entry": torch.empty((H, n, topk), **i32),
         "bws": torch.empty(max(F.focus_bucket_workspace_bytes(H, n, K, topk), 16),

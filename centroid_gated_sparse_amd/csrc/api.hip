@@ -99,7 +99,7 @@ focus_status check_buckets(const uint32_t *gmask, const int32_t *offsets, const 
         return FOCUS_OK;
     return invalid("buckets inconsistent with the routing:%s%s%s%s",
                    (found & 1u) ? " offsets" : "", (found & 2u) ? " tokens" : "",
-                   (found & 4u) ? " groups/partners/gmask" : "",
+                   (found & 4u) ? " groups/lower-set codes/gmask" : "",
                    (found & 8u) ? " slot_entry" : "");
 }
 
@@ -193,6 +193,13 @@ focus_status focus_route_project(const void *x, focus_dtype xdt, int64_t n, int3
                                         topk, groups, gmask, r,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FOCUS_OK : hip_failure(e, "focus_route_project launch");
+}
+
+int32_t focus_num_subbuckets(int32_t K, int32_t topk)
+{
+    if (K < 1 || K > kMaxGroups || topk < 1 || topk > K)
+        return 0;
+    return num_subbuckets(K, topk);
 }
 
 size_t focus_bucket_workspace_bytes(int32_t H, int64_t n, int32_t K, int32_t topk)

@@ -540,9 +540,12 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         else
             return Stage{k_lds3, v_lds3, key_lds3, a_lds3};
     };
-    __shared__ int sub_start[kMaxGroups + 1];
-    __shared__ int sub_count[kMaxGroups + 1];
-    __shared__ int sub_owner[kMaxGroups + 1];
+    // the key sub-buckets a group-pass query tile visits (at most the codes
+    // of one group), and the number of key tiles they hold
+    __shared__ int sub_start[GROUP ? kMaxCodes : 1];
+    __shared__ int sub_count[GROUP ? kMaxCodes : 1];
+    __shared__ int sub_owner[GROUP ? kMaxCodes : 1];
+    __shared__ int sub_tiles;
 
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -574,15 +577,15 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     const int hq = kvh * p.ratio + hg * p.hpb + hsub;
 
     // ---- rows of this block
-    int g = 0, mq = 0, e_start = 0;
+    int g = 0, sbq = 0, e_start = 0;
     int64_t p_start = 0;
     int tile_rows;
     if (GROUP) {
         const int4 t = p.tiles[(int64_t)kvh * p.max_tiles + slot];
-        g = t.x / (p.K + 1);
-        mq = t.x % (p.K + 1);
+        sbq = t.x;
         e_start = t.y;
         tile_rows = t.z;
+        g = t.w;
     } else {
         p_start = (int64_t)slot * rows_per_head;
         tile_rows = (int)min<int64_t>(rows_per_head, p.n - p_start);
@@ -646,35 +649,67 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     int n_tiles_total = 0;
     if (GROUP) {
         qlow = gmh[qpos] & ((1u << g) - 1u);
-        // wave 0 lanes find, per key sub-bucket, how many keys lie at or
-        // before (last query position - w)
-        if (wave == 0 && lane <= p.K) {
-            const int mk = lane;
-            const int sbk = g * (p.K + 1) + mk;
-            const int32_t *offh = p.offsets + (int64_t)kvh * (num_subbuckets(p.K) + 1);
-            const int lo0 = offh[sbk], hi0 = offh[sbk + 1];
-            const bool skip = (p.topk >= 2) && (mk == mq) && (mq < g);
-            int cnt = 0;
-            if (!skip && hi0 > lo0) {
-                const int64_t lim = (int64_t)bq_max - w;
-                int lo = lo0, hi = hi0;  // first entry with position > lim
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if ((int64_t)tok[mid] <= lim)
-                        lo = mid + 1;
-                    else
-                        hi = mid;
+        // Key sub-buckets of group g: a pair belongs to a lower group exactly
+        // when the two tokens' lower sets meet, so a key sub-bucket whose
+        // two lowest lower groups meet the query tile's is skipped whole.
+        // At top-k >= 4 a lower set can hold more than the two kept, and a
+        // per-key test on the group bits remains where either side keeps two.
+        // Wave 0 walks the group's codes, 64 at a time; each lane counts the
+        // keys at or before (last query position - w) of one kept code, and
+        // the kept codes with keys are packed in order into LDS.
+        if (wave == 0) {
+            int qa, qb;
+            decode_lower(g, sbq - group_base(g, p.topk), qa, qb);
+            const int ncode = codes_of_group(g, p.topk);
+            const int base = group_base(g, p.topk);
+            const int32_t *offh =
+                p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
+            const int64_t lim = (int64_t)bq_max - w;
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+            int kept = 0, tiles = 0;
+            if (lane == 0)
+                sub_count[0] = 0;  // read by the iterator even when nothing is kept
+            for (int c0 = 0; c0 < ncode; c0 += kWave) {
+                const int c = c0 + lane;
+                int cnt = 0, lo0 = 0, owner = 0;
+                if (c < ncode) {
+                    int ka, kb;
+                    decode_lower(g, c, ka, kb);
+                    const bool meets = (ka >= 0 && (ka == qa || ka == qb)) ||
+                                       (kb >= 0 && (kb == qa || kb == qb));
+                    lo0 = offh[base + c];
+                    const int hi0 = offh[base + c + 1];
+                    if (!meets && hi0 > lo0) {
+                        int lo = lo0, hi = hi0;  // first entry with position > lim
+                        while (lo < hi) {
+                            const int mid = (lo + hi) >> 1;
+                            if ((int64_t)tok[mid] <= lim)
+                                lo = mid + 1;
+                            else
+                                hi = mid;
+                        }
+                        cnt = lo - lo0;
+                    }
+                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
                 }
-                cnt = lo - lo0;
+                const uint64_t keep = __ballot(cnt > 0);
+                if (cnt > 0) {
+                    const int at = kept + __popcll(keep & below);
+                    sub_start[at] = lo0;
+                    sub_count[at] = cnt;
+                    sub_owner[at] = owner;
+                }
+                kept += __popcll(keep);
+                tiles += (cnt + kKeyTile - 1) / kKeyTile;
             }
-            sub_start[mk] = lo0;
-            sub_count[mk] = cnt;
-            sub_owner[mk] = (p.topk >= 3) && (mq < g) && (mk < g) && (mk != mq);
+#pragma unroll
+            for (int o = kWave / 2; o >= 1; o >>= 1)
+                tiles += __shfl_xor(tiles, o);
+            if (lane == 0)
+                sub_tiles = tiles;
         }
         __syncthreads();
-        for (int i = 0; i <= p.K; ++i)
-            n_tiles_total += (sub_count[i] + kKeyTile - 1) / kKeyTile;
-        n_tiles_total = __builtin_amdgcn_readfirstlane(n_tiles_total);
+        n_tiles_total = __builtin_amdgcn_readfirstlane(sub_tiles);
     } else {
         const int64_t lo = max<int64_t>(0, p_start - w + 1);
         j_first = (lo / kKeyTile) * kKeyTile;
@@ -1343,13 +1378,14 @@ __global__ __launch_bounds__(256) void gather_entries_kernel(const uint32_t *__r
 
 // Tile list of the group pass: for routing head h, every sub-bucket cut into
 // query tiles of `rows` entries, last tile (latest positions, most keys)
-// first.  tiles[h][i] = {sub-bucket, first entry, entry count, 0}.
-__global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ offsets, int nsb,
-                                                   int rows, int max_tiles,
+// first.  tiles[h][i] = {sub-bucket, first entry, entry count, group}.
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ offsets, int K,
+                                                   int topk, int rows, int max_tiles,
                                                    int4 *__restrict__ tiles,
                                                    int32_t *__restrict__ ntiles)
 {
-    __shared__ int start[kMaxGroups * (kMaxGroups + 1) + 1];
+    __shared__ int start[kMaxSubbuckets + 1];
+    const int nsb = num_subbuckets(K, topk);
     const int h = blockIdx.x;
     const int32_t *off = offsets + (int64_t)h * (nsb + 1);
     if (threadIdx.x == 0) {
@@ -1363,12 +1399,15 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
     }
     __syncthreads();
     int4 *th = tiles + (int64_t)h * max_tiles;
+    int g = 0;
     for (int sb = 0; sb < nsb; ++sb) {
+        while (g + 1 < K && group_base(g + 1, topk) <= sb)
+            ++g;
         const int nt = start[sb + 1] - start[sb];
         const int cnt = off[sb + 1] - off[sb];
         for (int j = threadIdx.x; j < nt; j += blockDim.x) {
             const int jj = nt - 1 - j;
-            th[start[sb] + j] = make_int4(sb, off[sb] + jj * rows, min(rows, cnt - jj * rows), 0);
+            th[start[sb] + j] = make_int4(sb, off[sb] + jj * rows, min(rows, cnt - jj * rows), g);
         }
     }
 }
@@ -1402,7 +1441,7 @@ Layout make_layout(const AttnShape &sh)
     L.E = sh.n * sh.topk;
     L.e_pad = (L.E + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
     L.n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
-    L.max_tiles = (int)((L.E + L.rows_group - 1) / L.rows_group) + num_subbuckets(sh.K);
+    L.max_tiles = (int)((L.E + L.rows_group - 1) / L.rows_group) + num_subbuckets(sh.K, sh.topk);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -1572,8 +1611,8 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
             if (e != hipSuccess)
                 return e;
         }
-        hipLaunchKernelGGL(plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets,
-                           num_subbuckets(sh.K), L.rows_group, L.max_tiles, tiles, ntiles);
+        hipLaunchKernelGGL(plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets, sh.K, sh.topk,
+                           L.rows_group, L.max_tiles, tiles, ntiles);
         e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_key_norms(sh.d, bf16, k, sh.n, sh.hkv,

@@ -72,8 +72,8 @@ struct BwdParams {
     // group pass
     const uint32_t *egm;     // group bits per entry [hkv][E]
     const int32_t *tokens;   // [hkv][E]
-    const int32_t *offsets;  // [hkv][K(K+1)+1]
-    const int4 *tiles;       // [hkv][max_tiles]: (sub-bucket, first entry, rows)
+    const int32_t *offsets;  // [hkv][num_subbuckets(K, topk) + 1]
+    const int4 *tiles;       // [hkv][max_tiles]: (sub-bucket, first entry, rows, group)
     const int32_t *ntiles;
     int max_tiles;
     int row_tiles;  // window: 128-row tiles per head
@@ -213,7 +213,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
         uint32_t gm[kWave];   // key group bits (group pass)
     };
     __shared__ __attribute__((aligned(16))) Stage stg[kDqStages];
-    __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
+    __shared__ int sub_start[GROUP ? kMaxCodes : 1], sub_count[GROUP ? kMaxCodes : 1],
+        sub_owner[GROUP ? kMaxCodes : 1], sub_tiles;
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -238,14 +239,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
     const int hq = kvh * p.ratio + hr;
     if (GROUP && slot >= p.ntiles[kvh])
         return;
-    int g = 0, mq = 0, tile_rows;
+    int g = 0, sbq = 0, tile_rows;
     int64_t row0;  // first query row (entry or position)
     if (GROUP) {
         const int4 t = p.tiles[(int64_t)kvh * p.max_tiles + slot];
-        g = t.x / (p.K + 1);
-        mq = t.x % (p.K + 1);
+        sbq = t.x;
         row0 = t.y;
         tile_rows = t.z;
+        g = t.w;
     } else {
         row0 = (int64_t)slot * kBwdRows;
         tile_rows = (int)std::min<int64_t>(kBwdRows, p.n - row0);
@@ -280,32 +281,59 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
     int64_t j_first = 0;
     if (GROUP) {
         const int bq_max = tok[row0 + tile_rows - 1];
-        if (threadIdx.x <= p.K) {
-            const int mk = threadIdx.x;
-            const int sbk = g * (p.K + 1) + mk;
-            const int32_t *offh = p.offsets + (int64_t)kvh * (num_subbuckets(p.K) + 1);
-            const int lo0 = offh[sbk], hi0 = offh[sbk + 1];
-            const bool skip = (p.topk >= 2) && (mk == mq) && (mq < g);
-            int cnt = 0;
-            if (!skip && hi0 > lo0) {
-                const int64_t lim = (int64_t)bq_max - w;  // keys at or before lim
-                int lo = lo0, hi = hi0;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if ((int64_t)tok[mid] <= lim)
-                        lo = mid + 1;
-                    else
-                        hi = mid;
+        // the key sub-buckets of group g whose lower sets miss the query
+        // tile's (as in the forward's group pass), packed by wave 0
+        if (wave == 0) {
+            int qa, qb;
+            decode_lower(g, sbq - group_base(g, p.topk), qa, qb);
+            const int ncode = codes_of_group(g, p.topk);
+            const int gb = group_base(g, p.topk);
+            const int32_t *offh =
+                p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
+            const int64_t lim = (int64_t)bq_max - w;  // keys at or before lim
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            int kept = 0, tiles = 0;
+            for (int c0 = 0; c0 < ncode; c0 += 64) {
+                const int c = c0 + lane;
+                int cnt = 0, lo0 = 0, owner = 0;
+                if (c < ncode) {
+                    int ka, kb;
+                    decode_lower(g, c, ka, kb);
+                    const bool meets = (ka >= 0 && (ka == qa || ka == qb)) ||
+                                       (kb >= 0 && (kb == qa || kb == qb));
+                    lo0 = offh[gb + c];
+                    const int hi0 = offh[gb + c + 1];
+                    if (!meets && hi0 > lo0) {
+                        int lo = lo0, hi = hi0;
+                        while (lo < hi) {
+                            const int mid = (lo + hi) >> 1;
+                            if ((int64_t)tok[mid] <= lim)
+                                lo = mid + 1;
+                            else
+                                hi = mid;
+                        }
+                        cnt = lo - lo0;
+                    }
+                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
                 }
-                cnt = lo - lo0;
+                const uint64_t keep = __ballot(cnt > 0);
+                if (cnt > 0) {
+                    const int at = kept + __popcll(keep & below);
+                    sub_start[at] = lo0;
+                    sub_count[at] = cnt;
+                    sub_owner[at] = owner;
+                }
+                kept += __popcll(keep);
+                tiles += (cnt + kQKeys - 1) / kQKeys;
             }
-            sub_start[mk] = lo0;
-            sub_count[mk] = cnt;
-            sub_owner[mk] = (p.topk >= 3) && (mq < g) && (mk < g) && (mk != mq);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+                tiles += __shfl_xor(tiles, o);
+            if (lane == 0)
+                sub_tiles = tiles;
         }
         __syncthreads();
-        for (int i = 0; i <= p.K; ++i)
-            n_tiles += (sub_count[i] + kQKeys - 1) / kQKeys;
+        n_tiles = sub_tiles;
     } else if (w > 0) {
         const int64_t lo = std::max<int64_t>(0, row0 - w + 1);
         j_first = (lo / kQKeys) * kQKeys;
@@ -587,7 +615,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         uint32_t gm[kWave];    // query group bits (group pass)
     };
     __shared__ __attribute__((aligned(16))) Stage stg[kDkvStages];
-    __shared__ int sub_start[kMaxGroups + 1], sub_count[kMaxGroups + 1], sub_owner[kMaxGroups + 1];
+    __shared__ int sub_start[GROUP ? kMaxCodes : 1], sub_count[GROUP ? kMaxCodes : 1],
+        sub_owner[GROUP ? kMaxCodes : 1], sub_tiles;
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -605,14 +634,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     const int kvh = b / tiles_per_kvh;
     if (GROUP && slot >= p.ntiles[kvh])
         return;
-    int g = 0, mk = 0, tile_keys;
+    int g = 0, sbk = 0, tile_keys;
     int64_t row0;
     if (GROUP) {
         const int4 t = p.tiles[(int64_t)kvh * p.max_tiles + slot];
-        g = t.x / (p.K + 1);
-        mk = t.x % (p.K + 1);
+        sbk = t.x;
         row0 = t.y;
         tile_keys = t.z;
+        g = t.w;
     } else {
         row0 = (int64_t)slot * kBwdRows;
         tile_keys = (int)std::min<int64_t>(kBwdRows, p.n - row0);
@@ -645,32 +674,61 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     int64_t i_first = 0;
     if (GROUP) {
         const int bk_min = tok[row0];  // keys ascend inside the sub-bucket
-        if (threadIdx.x <= p.K) {
-            const int mq = threadIdx.x;
-            const int sbq = g * (p.K + 1) + mq;
-            const int32_t *offh = p.offsets + (int64_t)kvh * (num_subbuckets(p.K) + 1);
-            const int lo0 = offh[sbq], hi0 = offh[sbq + 1];
-            const bool skip = (p.topk >= 2) && (mq == mk) && (mk < g);
-            int first = hi0;
-            if (!skip && hi0 > lo0) {
-                const int64_t lim = (int64_t)bk_min + w;  // queries at or after lim
-                int lo = lo0, hi = hi0;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if ((int64_t)tok[mid] < lim)
-                        lo = mid + 1;
-                    else
-                        hi = mid;
+        // the query sub-buckets of group g whose lower sets miss the key
+        // tile's, with the queries at or after (first key position + w),
+        // packed by wave 0
+        if (wave == 0) {
+            int ka, kb;
+            decode_lower(g, sbk - group_base(g, p.topk), ka, kb);
+            const int ncode = codes_of_group(g, p.topk);
+            const int gb = group_base(g, p.topk);
+            const int32_t *offh =
+                p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
+            const int64_t lim = (int64_t)bk_min + w;  // queries at or after lim
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            int kept = 0, tiles = 0;
+            for (int c0 = 0; c0 < ncode; c0 += 64) {
+                const int c = c0 + lane;
+                int cnt = 0, first = 0, owner = 0;
+                if (c < ncode) {
+                    int qa, qb;
+                    decode_lower(g, c, qa, qb);
+                    const bool meets = (qa >= 0 && (qa == ka || qa == kb)) ||
+                                       (qb >= 0 && (qb == ka || qb == kb));
+                    const int lo0 = offh[gb + c], hi0 = offh[gb + c + 1];
+                    first = hi0;
+                    if (!meets && hi0 > lo0) {
+                        int lo = lo0, hi = hi0;
+                        while (lo < hi) {
+                            const int mid = (lo + hi) >> 1;
+                            if ((int64_t)tok[mid] < lim)
+                                lo = mid + 1;
+                            else
+                                hi = mid;
+                        }
+                        first = lo;
+                    }
+                    cnt = hi0 - first;
+                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
                 }
-                first = lo;
+                const uint64_t keep = __ballot(cnt > 0);
+                if (cnt > 0) {
+                    const int at = kept + __popcll(keep & below);
+                    sub_start[at] = first;
+                    sub_count[at] = cnt;
+                    sub_owner[at] = owner;
+                }
+                kept += __popcll(keep);
+                tiles += (cnt + kKQueries - 1) / kKQueries;
             }
-            sub_start[mq] = first;
-            sub_count[mq] = hi0 - first;
-            sub_owner[mq] = (p.topk >= 3) && (mq < g) && (mk < g) && (mk != mq);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+                tiles += __shfl_xor(tiles, o);
+            if (lane == 0)
+                sub_tiles = tiles;
         }
         __syncthreads();
-        for (int i = 0; i <= p.K; ++i)
-            tiles_per_head += (sub_count[i] + kKQueries - 1) / kKQueries;
+        tiles_per_head = sub_tiles;
     } else if (w > 0) {
         i_first = row0;
         const int64_t i_last = std::min<int64_t>(p.n - 1, row0 + tile_keys - 1 + w - 1);
@@ -988,11 +1046,12 @@ __global__ __launch_bounds__(256) void bwd_drow_kernel(const __bf16 *__restrict_
 
 // Tiles of up to 128 entries inside each sub-bucket, one block per head.
 __global__ __launch_bounds__(256) void bwd_plan_kernel(const int32_t *__restrict__ offsets,
-                                                       int nsb, int max_tiles,
+                                                       int K, int topk, int max_tiles,
                                                        int4 *__restrict__ tiles,
                                                        int32_t *__restrict__ ntiles)
 {
-    __shared__ int base[1057];
+    __shared__ int base[kMaxSubbuckets + 1];
+    const int nsb = num_subbuckets(K, topk);
     const int h = blockIdx.x;
     const int32_t *off = offsets + (int64_t)h * (nsb + 1);
     if (threadIdx.x == 0) {
@@ -1007,11 +1066,14 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const int32_t *__restrict
     __syncthreads();
     for (int sb = threadIdx.x; sb < nsb; sb += blockDim.x) {
         const int lo = off[sb], cnt = off[sb + 1] - lo;
+        int g = 0;
+        while (g + 1 < K && group_base(g + 1, topk) <= sb)
+            ++g;
         for (int t = 0; t * kBwdRows < cnt; ++t) {
             const int slot = base[sb] + t;
             if (slot < max_tiles)
                 tiles[(int64_t)h * max_tiles + slot] =
-                    make_int4(sb, lo + t * kBwdRows, std::min(kBwdRows, cnt - t * kBwdRows), 0);
+                    make_int4(sb, lo + t * kBwdRows, std::min(kBwdRows, cnt - t * kBwdRows), g);
         }
     }
 }
@@ -1100,7 +1162,7 @@ BwdLayout bwd_layout(const AttnShape &sh)
 {
     BwdLayout L{};
     const int64_t n = sh.n, E = n * sh.topk;
-    const int nsb = num_subbuckets(sh.K);
+    const int nsb = num_subbuckets(sh.K, sh.topk);
     L.max_tiles = (int)((E + kBwdRows - 1) / kBwdRows + nsb);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -1176,8 +1238,8 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
                        static_cast<const __bf16 *>(out), p.dout, lse, qrows,
                        reinterpret_cast<float *>(base + L.drow),
                        reinterpret_cast<float *>(base + L.l2));
-    hipLaunchKernelGGL(bwd_plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets,
-                       num_subbuckets(sh.K), L.max_tiles,
+    hipLaunchKernelGGL(bwd_plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets, sh.K, sh.topk,
+                       L.max_tiles,
                        reinterpret_cast<int4 *>(base + L.tiles),
                        reinterpret_cast<int32_t *>(base + L.ntiles));
 

@@ -3,11 +3,13 @@
 // The pages split the sparse pattern into a local-window call and a
 // within-group causal call (Technical Summary, Key Contributions 5) without
 // saying how tokens are gathered.  Here the n*topk (token, group) entries of
-// each routing head are counting-sorted, stably, by the key
-// sb = group * (K + 1) + partner, where the partner is the token's lowest
-// group other than this one (K at top-1).  Inside a sub-bucket positions
-// ascend, so "causal" in bucket order is causal in positions, and a tile of
-// one sub-bucket meets a tile of another with a single owner decision.
+// each routing head are counting-sorted, stably, by the sub-bucket
+// group_base(g) + lower_code(g, a, b), where a < b are the token's two lowest
+// groups below g (see common.hpp).  Inside a sub-bucket positions ascend, so
+// "causal" in bucket order is causal in positions, and a tile of one
+// sub-bucket meets a tile of another with a single owner decision: their
+// pairs belong to a lower group exactly when the two lower sets meet (at
+// top-k <= 3; above, the lower sets may hold more than the two kept).
 //
 // Three kernels, all bound by HBM and integer only:
 //   count   one wavefront per chunk of tokens; LDS histogram per wave
@@ -26,7 +28,8 @@ namespace {
 constexpr int kChunkMax = 512;           // tokens per wavefront chunk, long sequences
 constexpr int kChunkMin = 64;            // ... and the shortest chunk
 constexpr int64_t kChunkWaves = 8192;    // wavefronts wanted before chunks shrink
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 4;       // ... while their histograms fit in 64 KB of LDS
+constexpr size_t kHistLdsBytes = 64 * 1024;
 constexpr int kCachedTopk = 4;           // scatter keeps keys in registers up to here
 constexpr int kScanThreads = 1024;
 
@@ -43,10 +46,13 @@ __device__ __forceinline__ int2 two_lowest(const int32_t *gt, int topk, int K)
     return make_int2(lo1, lo2);
 }
 
-__device__ __forceinline__ int subbucket(int g, int lo1, int lo2, int K)
+// Sub-bucket of the token's entry in its group g, from its two lowest groups
+// lo1 < lo2: below the lowest it has no lower group, below the second only
+// lo1, and below any higher one lo1 and lo2 are the two lowest.
+__device__ __forceinline__ int subbucket(int g, int lo1, int lo2, int topk)
 {
-    const int partner = (g == lo1) ? lo2 : lo1;
-    return g * (K + 1) + partner;
+    const int code = g == lo1 ? 0 : g == lo2 ? 1 + lo1 : 1 + g + lo2 * (lo2 - 1) / 2 + lo1;
+    return group_base(g, topk) + code;
 }
 
 // Sub-bucket keys of a token's entries, in registers (topk <= TK).  An
@@ -66,22 +72,22 @@ __device__ __forceinline__ void entry_keys(const int32_t *gt, int topk, int K, b
     }
 #pragma unroll
     for (int s = 0; s < TK; ++s)
-        key[s] = subbucket(g[s], lo1, lo2, K);
+        key[s] = subbucket(g[s], lo1, lo2, topk);
 }
 
-// counts[h][sb][chunk]
-template <int TK>
+// counts[h][sb][chunk]; WPB wavefronts (chunks) per block
+template <int TK, int WPB>
 __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t *__restrict__ groups,
                                                            int64_t n, int K, int topk,
                                                            int chunk_len, int nchunks,
                                                            int32_t *__restrict__ counts)
 {
-    extern __shared__ int32_t hist[];  // [kWavesPerBlock][nsb]
-    const int nsb = num_subbuckets(K);
+    extern __shared__ int32_t hist[];  // [WPB][nsb]
+    const int nsb = num_subbuckets(K, topk);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int h = blockIdx.y;
-    const int chunk = blockIdx.x * kWavesPerBlock + wave;
+    const int chunk = blockIdx.x * WPB + wave;
     int32_t *my = hist + wave * nsb;
     for (int i = lane; i < nsb; i += kWave)
         my[i] = 0;
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t *__rest
             } else {
                 const int2 lo = two_lowest(gt, topk, K);
                 for (int s = 0; s < topk; ++s)
-                    atomicAdd(&my[subbucket(gt[s], lo.x, lo.y, K)], 1);
+                    atomicAdd(&my[subbucket(gt[s], lo.x, lo.y, topk)], 1);
             }
         }
     }
@@ -167,18 +173,18 @@ __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(int32_t *__re
 // registers, so a pass touches memory only for the LDS cursor and the stores.
 // TK == 0 serves any topk and re-reads the group ids each pass.  The count
 // kernel takes the same two forms.
-template <int TK>
+template <int TK, int WPB>
 __global__ __launch_bounds__(256) void bucket_scatter_kernel(
     const int32_t *__restrict__ groups, int64_t n, int K, int topk, int chunk_len, int nchunks,
     const int32_t *__restrict__ bases, int32_t *__restrict__ tokens,
     int32_t *__restrict__ slot_entry)
 {
-    extern __shared__ int32_t run[];  // [kWavesPerBlock][nsb] running cursor
-    const int nsb = num_subbuckets(K);
+    extern __shared__ int32_t run[];  // [WPB][nsb] running cursor
+    const int nsb = num_subbuckets(K, topk);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int h = blockIdx.y;
-    const int chunk = blockIdx.x * kWavesPerBlock + wave;
+    const int chunk = blockIdx.x * WPB + wave;
     if (chunk >= nchunks)
         return;  // whole wavefront leaves together; no block barrier below
     int32_t *my = run + wave * nsb;
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
                     if ((pending >> s) & 1u)
                         my_key = key[s];
             } else if (pending != 0) {
-                my_key = subbucket(gt[__ffs(pending) - 1], lo.x, lo.y, K);
+                my_key = subbucket(gt[__ffs(pending) - 1], lo.x, lo.y, topk);
             }
             const int X = __builtin_amdgcn_readlane(my_key, leader);
             int sx = -1;
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
             } else {
                 for (uint32_t p = pending; p != 0; p &= p - 1) {
                     const int s = __ffs(p) - 1;
-                    if (subbucket(gt[s], lo.x, lo.y, K) == X)
+                    if (subbucket(gt[s], lo.x, lo.y, topk) == X)
                         sx = s;
                 }
             }
@@ -300,28 +306,29 @@ int bucket_chunk(int H, int64_t n)
 
 size_t bucket_workspace_bytes(int H, int64_t n, int K, int topk)
 {
-    (void)topk;
     const int chunk = bucket_chunk(H, n);
     const int64_t nchunks = (n + chunk - 1) / chunk;
-    return align_up((size_t)H * num_subbuckets(K) * nchunks * sizeof(int32_t), 256);
+    return align_up((size_t)H * num_subbuckets(K, topk) * nchunks * sizeof(int32_t), 256);
 }
 
-hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int topk,
-                         int32_t *offsets, int32_t *tokens, int32_t *slot_entry, void *ws,
-                         hipStream_t s)
+namespace {
+template <int WPB>
+hipError_t launch_bucket_wpb(const int32_t *groups, int H, int64_t n, int K, int topk,
+                             int32_t *offsets, int32_t *tokens, int32_t *slot_entry, void *ws,
+                             hipStream_t s)
 {
-    const int nsb = num_subbuckets(K);
+    const int nsb = num_subbuckets(K, topk);
     const int chunk = bucket_chunk(H, n);
     const int nchunks = (int)((n + chunk - 1) / chunk);
     int32_t *counts = static_cast<int32_t *>(ws);
-    const dim3 grid((nchunks + kWavesPerBlock - 1) / kWavesPerBlock, H);
-    const size_t lds = sizeof(int32_t) * nsb * kWavesPerBlock;
+    const dim3 grid((nchunks + WPB - 1) / WPB, H);
+    const size_t lds = sizeof(int32_t) * nsb * WPB;
     if (topk <= kCachedTopk)
-        hipLaunchKernelGGL(bucket_count_kernel<kCachedTopk>, grid, dim3(kWave * kWavesPerBlock),
-                           lds, s, groups, n, K, topk, chunk, nchunks, counts);
-    else
-        hipLaunchKernelGGL(bucket_count_kernel<0>, grid, dim3(kWave * kWavesPerBlock), lds, s,
+        hipLaunchKernelGGL((bucket_count_kernel<kCachedTopk, WPB>), grid, dim3(kWave * WPB), lds, s,
                            groups, n, K, topk, chunk, nchunks, counts);
+    else
+        hipLaunchKernelGGL((bucket_count_kernel<0, WPB>), grid, dim3(kWave * WPB), lds, s, groups,
+                           n, K, topk, chunk, nchunks, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -331,13 +338,25 @@ hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int top
     if (e != hipSuccess)
         return e;
     if (topk <= kCachedTopk)
-        hipLaunchKernelGGL(bucket_scatter_kernel<kCachedTopk>, grid,
-                           dim3(kWave * kWavesPerBlock), lds, s, groups, n, K, topk, chunk,
-                           nchunks, counts, tokens, slot_entry);
-    else
-        hipLaunchKernelGGL(bucket_scatter_kernel<0>, grid, dim3(kWave * kWavesPerBlock), lds,
+        hipLaunchKernelGGL((bucket_scatter_kernel<kCachedTopk, WPB>), grid, dim3(kWave * WPB), lds,
                            s, groups, n, K, topk, chunk, nchunks, counts, tokens, slot_entry);
+    else
+        hipLaunchKernelGGL((bucket_scatter_kernel<0, WPB>), grid, dim3(kWave * WPB), lds, s,
+                           groups, n, K, topk, chunk, nchunks, counts, tokens, slot_entry);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_bucket(const int32_t *groups, int H, int64_t n, int K, int topk,
+                         int32_t *offsets, int32_t *tokens, int32_t *slot_entry, void *ws,
+                         hipStream_t s)
+{
+    // four chunks per block while their LDS histograms fit in 64 KB (up to
+    // 4,096 sub-buckets), one otherwise (K above 28 at top-3 or more)
+    if (sizeof(int32_t) * num_subbuckets(K, topk) * kWavesPerBlock <= kHistLdsBytes)
+        return launch_bucket_wpb<kWavesPerBlock>(groups, H, n, K, topk, offsets, tokens,
+                                                 slot_entry, ws, s);
+    return launch_bucket_wpb<1>(groups, H, n, K, topk, offsets, tokens, slot_entry, ws, s);
 }
 
 }  // namespace focus

@@ -8,13 +8,13 @@
 // value is range-tested before it serves as an index), so inconsistent input
 // turns into an error bit, never into a stray access.  What it establishes,
 // per head (the bucketing of focus_bucket: a stable sort of the n*topk
-// (token, group) entries by sub-bucket group * (K + 1) + partner, the
-// partner being the token's lowest other group, K at top-1):
+// (token, group) entries by sub-bucket group_base(g) + lower-set code):
 //   offsets  start at 0, never decrease, end at n*topk              (bit 1)
 //   tokens   in [0, n), strictly ascending inside each sub-bucket   (bit 2)
 //   groups   the entry's group is one of its token's gmask bits and the
-//            sub-bucket's partner is the token's lowest other group;
-//            every gmask holds exactly topk bits                     (bit 4)
+//            sub-bucket's lower-set code is the token's (its two lowest
+//            groups below the entry's group); every gmask holds exactly topk
+//            bits                                                  (bit 4)
 //   slots    slot_entry[t][s] is an entry of token t, and the groups of a
 //            token's topk entries are exactly its gmask bits          (bit 8)
 // Together these make slot_entry a bijection onto the entries.
@@ -44,6 +44,15 @@ __device__ __forceinline__ int find_subbucket(const int32_t *off, int nsb, int64
     return lo;
 }
 
+// Group of sub-bucket sb (0 <= sb < num_subbuckets(K, topk)).
+__device__ __forceinline__ int group_of(int sb, int K, int topk)
+{
+    int g = 0;
+    while (g + 1 < K && group_base(g + 1, topk) <= sb)
+        ++g;
+    return g;
+}
+
 // one block per head
 __global__ __launch_bounds__(256) void check_offsets_kernel(const int32_t *__restrict__ offsets,
                                                             int nsb, int64_t E,
@@ -64,10 +73,10 @@ __global__ __launch_bounds__(256) void check_offsets_kernel(const int32_t *__res
 // one thread per (head, entry)
 __global__ __launch_bounds__(256) void check_entries_kernel(
     const uint32_t *__restrict__ gmask, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ tokens, int H, int64_t n, int K, int64_t E,
+    const int32_t *__restrict__ tokens, int H, int64_t n, int K, int topk, int64_t E,
     uint32_t *__restrict__ flag)
 {
-    const int nsb = num_subbuckets(K);
+    const int nsb = num_subbuckets(K, topk);
     const int64_t total = (int64_t)H * E;
     uint32_t bits = 0u;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -84,11 +93,14 @@ __global__ __launch_bounds__(256) void check_entries_kernel(
         const int64_t end = off[sb + 1];
         if (e + 1 < E && e + 1 < end && !(t < tokens[i + 1]))
             bits |= kBadTokens;
-        const int g = sb / (K + 1), partner = sb % (K + 1);
+        const int g = group_of(sb, K, topk);
+        const int code = sb - group_base(g, topk);
         const uint32_t m = gmask[h * n + t];
-        const uint32_t rest = m & ~(1u << g);
-        const int want = rest ? __builtin_ctz(rest) : K;
-        if (!((m >> g) & 1u) || partner != want)
+        const uint32_t lower = m & ((1u << g) - 1u);     // the token's groups below g
+        const uint32_t rest = lower & (lower - 1u);       // ... without the lowest
+        const int want = lower_code(g, lower ? __builtin_ctz(lower) : -1,
+                                    rest ? __builtin_ctz(rest) : -1);
+        if (!((m >> g) & 1u) || code != want)
             bits |= kBadGroups;
     }
     if (bits)
@@ -101,7 +113,7 @@ __global__ __launch_bounds__(256) void check_slots_kernel(
     const int32_t *__restrict__ tokens, const int32_t *__restrict__ slot_entry, int H,
     int64_t n, int K, int topk, uint32_t *__restrict__ flag)
 {
-    const int nsb = num_subbuckets(K);
+    const int nsb = num_subbuckets(K, topk);
     const int64_t E = n * topk;
     const int64_t total = (int64_t)H * n;
     uint32_t bits = 0u;
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(256) void check_slots_kernel(
             }
             if ((int64_t)tokens[h * E + e] != t)
                 bits |= kBadSlots;
-            seen |= 1u << (find_subbucket(off, nsb, e) / (K + 1));
+            seen |= 1u << group_of(find_subbucket(off, nsb, e), K, topk);
         }
         if (seen != m)
             bits |= kBadSlots;
@@ -146,9 +158,9 @@ hipError_t launch_check_buckets(const uint32_t *gmask, const int32_t *offsets,
     const int64_t E = n * topk;
     hipLaunchKernelGGL(check_clear_kernel, dim3(1), dim3(1), 0, s, flag);
     hipLaunchKernelGGL(check_offsets_kernel, dim3(H), dim3(256), 0, s, offsets,
-                       num_subbuckets(K), E, flag);
+                       num_subbuckets(K, topk), E, flag);
     hipLaunchKernelGGL(check_entries_kernel, dim3(grid_for((int64_t)H * E)), dim3(256), 0, s,
-                       gmask, offsets, tokens, H, n, K, E, flag);
+                       gmask, offsets, tokens, H, n, K, topk, E, flag);
     hipLaunchKernelGGL(check_slots_kernel, dim3(grid_for((int64_t)H * n)), dim3(256), 0, s,
                        gmask, offsets, tokens, slot_entry, H, n, K, topk, flag);
     hipError_t e = hipGetLastError();

@@ -20,8 +20,61 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
-// Sub-buckets per head: (group, partner) with partner in [0, K].
-inline __host__ __device__ int num_subbuckets(int K) { return K * (K + 1); }
+// Sub-buckets: every group g is split by the token's lower set inside it,
+// its groups below g.  The sub-bucket's key keeps the two lowest of them
+// (the whole lower set at top-k <= 3) as a code:
+//     no group below g  -> 0
+//     only a            -> 1 + a
+//     a < b (and more)  -> 1 + g + b (b - 1) / 2 + a
+// Two tokens of g share a group below g exactly when their lower sets meet;
+// when the two-lowest keys already meet, the pair belongs to a lower group.
+// Codes a token of group g can take at this top-k.
+inline __host__ __device__ int codes_of_group(int g, int topk)
+{
+    return topk == 1 ? 1 : topk == 2 ? 1 + g : 1 + g + g * (g - 1) / 2;
+}
+// First sub-bucket of group g: the codes of all groups below it.
+inline __host__ __device__ int group_base(int g, int topk)
+{
+    const int pairs = g * (g - 1) / 2;  // sum of g' over g' < g
+    if (topk == 1)
+        return g;
+    if (topk == 2)
+        return g + pairs;
+    return g + pairs + g * (g - 1) * (g - 2) / 6;
+}
+// Sub-buckets per head.
+inline __host__ __device__ int num_subbuckets(int K, int topk) { return group_base(K, topk); }
+// Most codes of one group (the last one).
+inline __host__ __device__ int max_codes(int K, int topk) { return codes_of_group(K - 1, topk); }
+// Code of a lower set given by its lowest member a and second-lowest b
+// (-1 when absent).
+inline __host__ __device__ int lower_code(int g, int a, int b)
+{
+    return a < 0 ? 0 : b < 0 ? 1 + a : 1 + g + b * (b - 1) / 2 + a;
+}
+// The two lowest members (a, b; -1 when absent) of the lower set with code c.
+inline __host__ __device__ void decode_lower(int g, int c, int &a, int &b)
+{
+    a = -1;
+    b = -1;
+    if (c == 0)
+        return;
+    if (c <= g) {
+        a = c - 1;
+        return;
+    }
+    int p = c - 1 - g;  // index of the pair (a, b), a < b, ordered by b then a
+    int bb = 1;
+    while ((bb + 1) * bb / 2 <= p)
+        ++bb;
+    b = bb;
+    a = p - bb * (bb - 1) / 2;
+}
+// Largest number of codes of one group, and of sub-buckets of a head, over
+// every K <= 32 and top-k.
+constexpr int kMaxCodes = 1 + 31 + 31 * 30 / 2;
+constexpr int kMaxSubbuckets = 32 + 32 * 31 / 2 + 32 * 31 * 30 / 6;
 
 // Host-side record of the last error on this thread (read by
 // focus_last_error).

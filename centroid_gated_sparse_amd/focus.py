@@ -26,7 +26,8 @@ CHECK_WORKSPACE_BYTES = 256  # FOCUS_CHECK_WORKSPACE_BYTES
 # exported symbols (all declared in include/focus.h)
 SYMBOLS = (
     "focus_status_string", "focus_last_error", "focus_abi_version",
-    "focus_route", "focus_route_project", "focus_bucket_workspace_bytes", "focus_bucket",
+    "focus_route", "focus_route_project", "focus_num_subbuckets", "focus_bucket_workspace_bytes",
+    "focus_bucket",
     "focus_bucket_noalloc",
     "focus_attn_fwd_workspace_bytes", "focus_attn_workspace_bytes", "focus_check_buckets",
     "focus_attn_fwd", "focus_attn_fwd_part",
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.focus_route.argtypes = [P, P, i32, i64, i32, i32, i32, P, P, P]
     L.focus_route_project.argtypes = [P, ctypes.c_int, i64, i32, P, P, i32, i32, i32, i32,
                                       P, P, P, P]
+    L.focus_num_subbuckets.argtypes = [i32, i32]
+    L.focus_num_subbuckets.restype = i32
     L.focus_bucket_workspace_bytes.argtypes = [i32, i64, i32, i32]
     L.focus_bucket_workspace_bytes.restype = sz
     L.focus_bucket.argtypes = [P, i32, i64, i32, i32, P, P, P, P, sz, P]
@@ -180,19 +183,24 @@ def focus_route_project(x, Wt, centroids, topk: int, groups=None, gmask=None, r=
     return groups, gmask, r
 
 
+def focus_num_subbuckets(K: int, topk: int) -> int:
+    """Sub-buckets per routing head: every (group, lower-set code)."""
+    return int(lib().focus_num_subbuckets(K, topk))
+
+
 def focus_bucket_workspace_bytes(H: int, n: int, K: int, topk: int) -> int:
     return int(lib().focus_bucket_workspace_bytes(H, n, K, topk))
 
 
 def focus_bucket(groups, K: int, offsets=None, tokens=None, slot_entry=None, workspace=None,
                  stream=None):
-    """groups int32 [H, n, topk] -> (offsets [H, K*(K+1)+1], tokens [H, n*topk],
-    slot_entry [H, n, topk]), all int32."""
+    """groups int32 [H, n, topk] -> (offsets [H, focus_num_subbuckets(K, topk) + 1],
+    tokens [H, n*topk], slot_entry [H, n, topk]), all int32."""
     import torch
 
     H, n, topk = groups.shape
     dev = groups.device
-    nsb = K * (K + 1)
+    nsb = focus_num_subbuckets(K, topk)
     if offsets is None:
         offsets = torch.empty((H, nsb + 1), dtype=torch.int32, device=dev)
     if tokens is None:
@@ -221,7 +229,8 @@ def focus_bucket_noalloc(groups, K: int, offsets=None, tokens=None, slot_entry=N
     H, n, topk = groups.shape
     dev = groups.device
     if offsets is None:
-        offsets = torch.empty((H, K * (K + 1) + 1), dtype=torch.int32, device=dev)
+        offsets = torch.empty((H, focus_num_subbuckets(K, topk) + 1), dtype=torch.int32,
+                              device=dev)
     if tokens is None:
         tokens = torch.empty((H, n * topk), dtype=torch.int32, device=dev)
     if slot_entry is None:

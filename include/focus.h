@@ -130,20 +130,26 @@ focus_status focus_route_project(const void *x, focus_dtype xdt, int64_t n, int3
  * the sparse pattern splits into a local-window call and a within-group
  * causal call; the pages leave the gathering itself open).
  *
- * A stable counting sort of the entries of each head by the key
- * (group g, partner p), where the partner of token t in group g is its
- * lowest group other than g (K when topk == 1).  Inside a (g, p)
- * sub-bucket positions ascend.  Sub-bucket sb = g * (K + 1) + p.
+ * A stable counting sort of the entries of each head by sub-bucket: group g,
+ * then the token's lower set inside g (its groups below g), keyed by the two
+ * lowest of them as a code c:
+ *     no group below g            c = 0
+ *     only a below g              c = 1 + a
+ *     a < b lowest below g        c = 1 + g + b (b - 1) / 2 + a
+ * Group g holds codes_g = 1 (topk 1), 1 + g (topk 2) or 1 + g + g (g - 1) / 2
+ * (topk >= 3) sub-buckets, and sub-bucket sb = (codes of the groups below g)
+ * + c.  Inside a sub-bucket positions ascend.  Two tokens of g share a group
+ * below g exactly when their lower sets meet, which the codes decide whole at
+ * topk <= 3; focus_num_subbuckets(K, topk) gives the count per head.
  *
  *   groups      int32 [H, n, topk]      from focus_route
- *   offsets     int32 [H, K*(K+1)+1]    out: first entry of each sub-bucket;
- *                                        offsets[h][K*(K+1)] = n * topk.
- *                                        Group g's entries are the run from
- *                                        offsets[h][g*(K+1)] to
- *                                        offsets[h][(g+1)*(K+1)] (a stride of
- *                                        K + 1): every token holding g, each
- *                                        once, ascending by position inside
- *                                        each partner sub-bucket (not across
+ *   offsets     int32 [H, S + 1]        out, S = focus_num_subbuckets(K, topk):
+ *                                        first entry of each sub-bucket;
+ *                                        offsets[h][S] = n * topk.  Group g's
+ *                                        entries are one run of whole
+ *                                        sub-buckets: every token holding g,
+ *                                        each once, ascending by position
+ *                                        inside each sub-bucket (not across
  *                                        the whole group)
  *   tokens      int32 [H, n*topk]       out: position of each entry
  *   slot_entry  int32 [H, n, topk]      out: entry index of (t, groups[t][s])
@@ -152,6 +158,7 @@ focus_status focus_route_project(const void *x, focus_dtype xdt, int64_t n, int3
  * for K > 32; WORKSPACE if the workspace is missing or short.  Group ids
  * outside [0, K) or repeated ids in a token's list are undefined input.
  */
+int32_t focus_num_subbuckets(int32_t K, int32_t topk); /* 0 for K or topk out of range */
 size_t focus_bucket_workspace_bytes(int32_t H, int64_t n, int32_t K, int32_t topk);
 focus_status focus_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
                           int32_t topk, int32_t *offsets, int32_t *tokens,
@@ -185,8 +192,8 @@ focus_status focus_bucket_noalloc(const int32_t *groups, int32_t H, int64_t n, i
  *   offsets     start at 0, never decrease, end at n * topk;
  *   tokens      in [0, n), strictly ascending inside each sub-bucket;
  *   groups      each entry's group is a bit of its token's gmask, its
- *               sub-bucket's partner is the token's lowest other group (K at
- *               top-1), and every gmask holds exactly topk bits below K;
+ *               sub-bucket's lower-set code is the token's inside that group,
+ *               and every gmask holds exactly topk bits below K;
  *   slot_entry  slot_entry[t][s] is an entry of token t, and the groups of a
  *               token's topk entries are exactly its gmask bits.
  *   gmask, offsets, tokens, slot_entry   as passed to focus_attn_fwd

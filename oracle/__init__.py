@@ -58,6 +58,8 @@ def _load():
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.oracle_route.argtypes = [P, P, i32, i64, i32, i32, i32, P, P]
     lib.oracle_bucket.argtypes = [P, i32, i64, i32, i32, P, P, P]
+    lib.oracle_num_subbuckets.argtypes = [i32, i32]
+    lib.oracle_num_subbuckets.restype = i32
     lib.oracle_attn_rows.argtypes = [P, i32, P, P, i32, i32, i32, i64, i32, P, i32, i32,
                                      i64, f64, P, P, i64, P, P, P, i32]
     lib.oracle_pair_counts.argtypes = [P, i32, i64, i32, i32, i64, P]
@@ -133,15 +135,21 @@ def route_project(x: np.ndarray, W: np.ndarray, centroids: np.ndarray, topk: int
     return r, groups, gmask
 
 
+def num_subbuckets(K: int, topk: int) -> int:
+    """Sub-buckets per routing head: every (group, lower-set code)."""
+    return int(_load().oracle_num_subbuckets(int(K), int(topk)))
+
+
 def bucket(groups: np.ndarray, K: int):
     """Per-head stable bucketing of (token, group) entries.
 
-    Returns (offsets int32 [H, K*(K+1)+1], tokens int32 [H, n*topk],
-    slot_entry int32 [H, n, topk]).
+    Sub-buckets are (group, lower-set code) pairs, num_subbuckets(K, topk)
+    per head.  Returns (offsets int32 [H, num_subbuckets + 1],
+    tokens int32 [H, n*topk], slot_entry int32 [H, n, topk]).
     """
     groups = np.ascontiguousarray(groups, dtype=np.int32)
     H, n, topk = groups.shape
-    nsb = K * (K + 1)
+    nsb = num_subbuckets(K, topk)
     offsets = np.empty((H, nsb + 1), np.int32)
     tokens = np.empty((H, n * topk), np.int32)
     slot_entry = np.empty((H, n, topk), np.int32)

@@ -19,8 +19,9 @@
  *           token keeps its top-k groups G(t).
  *   attend: A(i) = { j <= i : i - j < w  or  G(i) and G(j) share a group }
  *           and the output is the exact softmax over A(i).
- *   bucket: the (token, group) entries sorted by group, then by the token's
- *           lowest other group ("partner"), then by position.
+ *   bucket: the (token, group) entries sorted by group g, then by the
+ *           token's lower set inside g (its groups below g: the two lowest
+ *           of them, as a code), then by position.
  *   project: r_t = W x_t, the hidden state projected into the routing space
  *           by one 16 x d_model matrix per layer (Technical Summary, Core
  *           Architecture and Token Grouping; the thelatestinai.com Tables 2
@@ -150,23 +151,61 @@ int oracle_project(const void *x, int32_t is_bf16, int64_t n, int32_t dm,
     return ORACLE_OK;
 }
 
-/* Partner of token t inside group g: its lowest group other than g, or K when
- * it belongs to g alone (top-1). */
-static int partner_of(const int32_t *gt, int topk, int g, int K)
+/* Lower-set code of token t inside group g.  The token's groups below g,
+ * ascending, are a < b < ...; the code keeps the two lowest:
+ *     no lower group      -> 0
+ *     only a               -> 1 + a
+ *     a, b (and any more)  -> 1 + g + b (b - 1) / 2 + a
+ * Two tokens of group g share a group below g exactly when their full lower
+ * sets meet; at top-k <= 3 a lower set has at most two groups, so the code is
+ * the whole lower set. */
+static int lower_code(const int32_t *gt, int topk, int g)
 {
-    int p = K;
-    for (int s = 0; s < topk; ++s)
-        if (gt[s] != g && gt[s] < p)
-            p = gt[s];
-    return p;
+    int a = -1, b = -1; /* the lowest and second-lowest groups below g */
+    for (int s = 0; s < topk; ++s) {
+        const int x = gt[s];
+        if (x >= g)
+            continue;
+        if (a < 0 || x < a) {
+            b = a;
+            a = x;
+        } else if (b < 0 || x < b) {
+            b = x;
+        }
+    }
+    if (a < 0)
+        return 0;
+    if (b < 0)
+        return 1 + a;
+    return 1 + g + b * (b - 1) / 2 + a;
+}
+
+/* Number of lower-set codes a token of group g can take at this top-k. */
+static int codes_of_group(int g, int topk)
+{
+    if (topk == 1)
+        return 1;
+    if (topk == 2)
+        return 1 + g;
+    return 1 + g + g * (g - 1) / 2;
+}
+
+/* Sub-buckets per routing head: every (group, lower-set code). */
+int oracle_num_subbuckets(int32_t K, int32_t topk)
+{
+    int total = 0;
+    for (int g = 0; g < K; ++g)
+        total += codes_of_group(g, topk);
+    return total;
 }
 
 /* Bucketing: the per-group token lists that within-group causal attention
  * runs over (Technical Summary, Key Contributions 5: the pattern splits into
  * a local-window call and a within-group causal call).  Entries are listed
- * group by group; inside a group, sub-bucket by partner 0..K, and inside a
- * sub-bucket by ascending position.  offsets has K*(K+1)+1 entries per head;
- * slot_entry[t][s] is the entry that holds (t, groups[t][s]). */
+ * group by group; inside a group, sub-bucket by lower-set code 0, 1, ...,
+ * and inside a sub-bucket by ascending position.  offsets has one entry per
+ * sub-bucket plus the total; slot_entry[t][s] is the entry that holds
+ * (t, groups[t][s]). */
 int oracle_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
                   int32_t topk, int32_t *offsets, int32_t *tokens,
                   int32_t *slot_entry)
@@ -174,12 +213,14 @@ int oracle_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
     if (!groups || !offsets || !tokens || !slot_entry || H < 1 || n < 1 ||
         K < 1 || K > 32 || topk < 1 || topk > K || n * topk > INT32_MAX)
         return ORACLE_BAD_ARG;
-    const int nsb = K * (K + 1);
-    int32_t *part = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    const int nsb = oracle_num_subbuckets(K, topk);
+    int32_t *code = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
     int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
-    if (!part || !slot) {
-        free(part);
+    char *present = (char *)malloc((size_t)codes_of_group(K - 1, topk));
+    if (!code || !slot || !present) {
+        free(code);
         free(slot);
+        free(present);
         return ORACLE_NO_MEMORY;
     }
     for (int h = 0; h < H; ++h) {
@@ -188,30 +229,40 @@ int oracle_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
         int32_t *tok = tokens + (int64_t)h * n * topk;
         int32_t *se = slot_entry + (int64_t)h * n * topk;
         int32_t cursor = 0;
+        int base = 0; /* first sub-bucket of group g */
         for (int g = 0; g < K; ++g) {
-            /* membership slot and partner of every token for this group */
+            const int ncode = codes_of_group(g, topk);
+            memset(present, 0, (size_t)ncode);
+            /* membership slot and lower-set code of every token for g */
             for (int64_t t = 0; t < n; ++t) {
                 slot[t] = -1;
                 for (int s = 0; s < topk; ++s)
                     if (gh[t * topk + s] == g)
                         slot[t] = s;
-                part[t] = slot[t] >= 0 ? partner_of(gh + t * topk, topk, g, K) : -1;
+                code[t] = slot[t] >= 0 ? lower_code(gh + t * topk, topk, g) : -1;
+                if (code[t] >= 0)
+                    present[code[t]] = 1;
             }
-            for (int m = 0; m <= K; ++m) {
-                off[g * (K + 1) + m] = cursor;
+            /* each code's tokens in position order (empty codes are skipped) */
+            for (int c = 0; c < ncode; ++c) {
+                off[base + c] = cursor;
+                if (!present[c])
+                    continue;
                 for (int64_t t = 0; t < n; ++t) {
-                    if (slot[t] < 0 || part[t] != m)
+                    if (code[t] != c)
                         continue;
                     tok[cursor] = (int32_t)t;
                     se[t * topk + slot[t]] = cursor;
                     ++cursor;
                 }
             }
+            base += ncode;
         }
         off[nsb] = cursor;
     }
-    free(part);
+    free(code);
     free(slot);
+    free(present);
     return ORACLE_OK;
 }
 

@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(F.SYMBOLS)
@@ -43,8 +43,16 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_sizes(L):
+    # sub-buckets: group g of K holds 1, 1 + g or 1 + g + C(g, 2) lower-set
+    # codes at top-1, top-2 and top-3 or more
+    assert F.focus_num_subbuckets(8, 1) == 8
+    assert F.focus_num_subbuckets(8, 2) == 8 + 28
+    assert F.focus_num_subbuckets(8, 3) == F.focus_num_subbuckets(8, 6) == 8 + 28 + 56
+    assert F.focus_num_subbuckets(32, 4) == 32 + 496 + 4960
+    assert F.focus_num_subbuckets(0, 1) == F.focus_num_subbuckets(4, 5) == 0
+    assert F.focus_num_subbuckets(33, 2) == 0
     # bucket: one int per (head, sub-bucket, 512-token chunk)
-    assert F.focus_bucket_workspace_bytes(8, 1 << 20, 8, 2) == 8 * 72 * 2048 * 4
+    assert F.focus_bucket_workspace_bytes(8, 1 << 20, 8, 2) == 8 * 36 * 2048 * 4
     assert F.focus_bucket_workspace_bytes(1, 10, 0, 1) == 0
     # attention: at least the partials of every (query head, entry), O in
     # the I/O dtype and the LSE in fp32, plus the bucket-order K and V^T

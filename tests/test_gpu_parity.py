@@ -148,7 +148,12 @@ SMALL = [
     W("bf16_d64_mha_k2", 1500, 3, 3, 64, 4, 2, 256, "bf16"),
     W("bf16_d128_gqa4_skew", 1300, 8, 2, 128, 4, 2, 100, "bf16", z_probs=(0.4, 0.3, 0.2, 0.1)),
     W("bf16_d128_gqa4_k8", 2000, 8, 2, 128, 8, 2, 64, "bf16"),
-    W("bf16_d128_top3_owner", 900, 4, 1, 128, 8, 3, 32, "bf16"),
+    W("bf16_d128_top3", 900, 4, 1, 128, 8, 3, 32, "bf16"),
+    # top-4 and more: sub-bucket pairs whose two lowest lower-set groups are
+    # disjoint run with the per-key owner test
+    W("bf16_d128_k8_top4_owner", 900, 4, 2, 128, 8, 4, 24, "bf16"),
+    W("bf16_d128_k16_top5_owner", 1200, 4, 2, 128, 16, 5, 32, "bf16", z_probs=SKEW16),
+    W("f32_d64_k10_top4_owner", 400, 2, 1, 64, 10, 4, 16, "f32"),
     W("bf16_d64_w0", 800, 2, 2, 64, 4, 2, 0, "bf16"),
     W("bf16_d64_w_ge_n", 600, 2, 1, 64, 4, 2, 600, "bf16"),
     W("bf16_d128_K1", 700, 4, 4, 128, 1, 1, 16, "bf16"),
@@ -167,19 +172,19 @@ SMALL = [
     # 2 top-k > K: every pair shares a group, all of them in the window pass
     W("bf16_d128_k4_top3_allpairs", 700, 4, 2, 128, 4, 3, 40, "bf16"),
     W("f32_d64_k3_top2_allpairs", 350, 2, 1, 64, 3, 2, 16, "f32"),
-    # K = 16 and 32 (thelatestinai.com Table 9 ablates K up to 32): K + 1
-    # partner sub-buckets per group, up to 1056 per head; skewed group
-    # frequencies make crowded and near-empty buckets side by side, and at
-    # top-3 (2 top-k <= K) the per-key owner test runs on the tiles whose
-    # partner is below g
+    # K = 16 and 32 (thelatestinai.com Table 9 ablates K up to 32): group g
+    # splits into lower-set sub-buckets (1 + g + C(g, 2) of them at top-3, up
+    # to 5488 per head); skewed group frequencies make crowded and near-empty
+    # buckets side by side, and at top-3 every query/key sub-bucket pair whose
+    # lower sets meet is skipped whole
     W("bf16_d128_gqa4_k16_top2", 1500, 8, 2, 128, 16, 2, 48, "bf16", z_probs=SKEW16),
-    W("bf16_d128_gqa4_k16_top3_owner", 1500, 8, 2, 128, 16, 3, 40, "bf16", z_probs=SKEW16),
+    W("bf16_d128_gqa4_k16_top3", 1500, 8, 2, 128, 16, 3, 40, "bf16", z_probs=SKEW16),
     W("bf16_d128_gqa4_k32_top2", 2500, 8, 2, 128, 32, 2, 64, "bf16", z_probs=SKEW32),
-    W("bf16_d128_gqa4_k32_top3_owner", 2500, 8, 2, 128, 32, 3, 64, "bf16", z_probs=SKEW32),
-    W("bf16_d64_k32_top3_owner", 1200, 4, 4, 64, 32, 3, 16, "bf16", z_probs=SKEW32),
-    # fp32 path: pure group attention, and the owner test at top-3 of 8
+    W("bf16_d128_gqa4_k32_top3", 2500, 8, 2, 128, 32, 3, 64, "bf16", z_probs=SKEW32),
+    W("bf16_d64_k32_top3", 1200, 4, 4, 64, 32, 3, 16, "bf16", z_probs=SKEW32),
+    # fp32 path: pure group attention, and lower-set sub-buckets at top-3 of 8
     W("f32_d64_w0", 600, 2, 2, 64, 4, 2, 0, "f32"),
-    W("f32_d128_k8_top3_owner", 500, 4, 2, 128, 8, 3, 24, "f32"),
+    W("f32_d128_k8_top3", 500, 4, 2, 128, 8, 3, 24, "f32"),
 ]
 
 

@@ -25,7 +25,8 @@ MUTATIONS = {
     "lse_without_max": ("lse[r] = mx + log(l);", "lse[r] = log(l);"),
     "not_causal_self": ("for (int64_t j = 0; j <= i; ++j) {\n                int in_window",
                         "for (int64_t j = 0; j < i; ++j) {\n                int in_window"),
-    "partner_max": ("if (gt[s] != g && gt[s] < p)", "if (gt[s] != g && (p == K || gt[s] > p))"),
+    "lower_set_highest": ("if (a < 0 || x < a) {", "if (a < 0 || x > a) {"),
+    "lower_code_swapped": ("return 1 + g + b * (b - 1) / 2 + a;", "return 1 + g + a * (a - 1) / 2 + b;"),
     "count_far_edge": ("int64_t far_end = i - w;", "int64_t far_end = i - w + 1;"),
     "value_index": ("acc[e] += p * widen(v, is_bf16, vb + e);",
                     "acc[e] += p * widen(v, is_bf16, kb_unused(vb) + e);"),
