@@ -839,8 +839,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     // the matrix cores: S = Q K^T (16-byte fragments streamed two steps
     // ahead, the transpose reads of dO^T in between); the key's query mask;
     // dP = dO V^T with P = exp2(S c - L log2 e) formed two elements per step
-    // (Q^T transpose reads in between); dv^T += dO^T P with dS = P (dP - D)
-    // formed two elements per step; dk^T += Q^T dS; then the DMA of tile
+    // (no mask where the wave's keys all see the whole tile); dv^T += dO^T P
+    // with dS = P (dP - D) formed two elements per step and the Q^T
+    // transpose reads in between; dk^T += Q^T dS; then the DMA of tile
     // u + AHEAD and the end-of-tile barrier.
     auto body = [&](int S, int u) {
         int head_c, origin, valid, owner;
@@ -864,16 +865,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
                 fr[n2 % 3] = lds16(n2 < KS ? ql : dl, qoff[n2 % KS]);
             }
         };
-        auto transpose_reads = [&](int i) {  // dO^T during S, Q^T during dP
+        auto transpose_reads = [&](int i) {  // dO^T during S
 #pragma unroll
             for (int q = 0; q < 2 * DB / KS; ++q) {
-                const int f = (i % KS) * (2 * DB / KS) + q;  // f / 2 = db, f % 2 = t
+                const int f = i * (2 * DB / KS) + q;  // f / 2 = db, f % 2 = t
                 const int db = f / 2, t = f % 2;
                 const uint32_t step = (uint32_t)(8 * t * RB);
-                if (i < KS)
-                    dtf[db][t] = tr_frag(dl, tro[db][0] + step, tro[db][1] + step);
-                else
-                    qtf[db][t] = tr_frag(ql, tro[db][0] + step, tro[db][1] + step);
+                dtf[db][t] = tr_frag(dl, tro[db][0] + step, tro[db][1] + step);
             }
         };
 #pragma unroll
@@ -924,39 +922,57 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
                         ? (uint32_t)((2ull << qhi) - (1ull << qlo))
                         : 0u;
         }
-        // this lane's 16 queries are 16h .. 16h + 15
+        // this lane's 16 queries are 16h .. 16h + 15; a wave whose valid
+        // keys all see the whole tile skips the mask (the columns of keys
+        // past the tile's end are never stored)
         const uint32_t mh = qmask >> (16 * h);
+        const bool full = __builtin_amdgcn_ballot_w64(kvalid && qmask != 0xffffffffu) == 0;
         __builtin_amdgcn_sched_barrier(0);
 
         // dP chain; P of registers 2i, 2i + 1 after dP step i
+        auto dp_chain = [&](auto masked) {
 #pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            stream(KS + i);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(KS + i) % 3], vf[i], dp, 0, 0, 0);
-            transpose_reads(KS + i);
+            for (int i = 0; i < KS; ++i) {
+                stream(KS + i);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(KS + i) % 3], vf[i], dp, 0, 0,
+                                                             0);
 #pragma unroll
-            for (int e = 0; e < 16 / KS; ++e) {
-                const int r = (16 / KS) * i + e;
-                const float l = r % 4 == 0 ? l4[r / 4].x : r % 4 == 1 ? l4[r / 4].y
-                              : r % 4 == 2 ? l4[r / 4].z : l4[r / 4].w;
-                const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - l);
-                const int keep = __builtin_amdgcn_sbfe((int)mh, r, 1);  // 0 or -1
-                s[r] = __int_as_float(__float_as_int(pr) & keep);
+                for (int e = 0; e < 16 / KS; ++e) {
+                    const int r = (16 / KS) * i + e;
+                    const float l = r % 4 == 0 ? l4[r / 4].x : r % 4 == 1 ? l4[r / 4].y
+                                  : r % 4 == 2 ? l4[r / 4].z : l4[r / 4].w;
+                    const float pr = __builtin_amdgcn_exp2f(s[r] * p.c - l);
+                    if constexpr (decltype(masked)::value) {
+                        const int keep = __builtin_amdgcn_sbfe((int)mh, r, 1);  // 0 or -1
+                        s[r] = __int_as_float(__float_as_int(pr) & keep);
+                    } else {
+                        s[r] = pr;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        };
+        if (full)
+            dp_chain(std::false_type{});
+        else
+            dp_chain(std::true_type{});
         const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
         float4 d4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             d4[j] = reinterpret_cast<const float4 *>(stg[S].dd)[4 * h + j];
         __builtin_amdgcn_sched_barrier(0);
-        // dv^T += dO^T P; dS of registers 2i, 2i + 1 after MFMA i
+        // dv^T += dO^T P; dS of registers 2i, 2i + 1 after MFMA i, and the Q^T
+        // fragment of step i read into the registers dO^T fragment i leaves
 #pragma unroll
         for (int i = 0; i < 2 * DB; ++i) {
             const int db = i / 2, t = i % 2;
             dv_acc[db] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(dtf[db][t], pf[t], dv_acc[db], 0, 0, 0);
+            {
+                const uint32_t step = (uint32_t)(8 * t * RB);
+                qtf[db][t] = tr_frag(ql, tro[db][0] + step, tro[db][1] + step);
+            }
 #pragma unroll
             for (int e = 0; e < 16 / (2 * DB); ++e) {
                 const int r = (16 / (2 * DB)) * i + e;
