@@ -54,6 +54,7 @@ using namespace attn;
 constexpr int kBwdThreads = 256;  // dk/dv pass: 4 wavefronts
 constexpr int kDqThreads = 512;   // dq pass: 8 wavefronts, 2 per SIMD
 constexpr int kBwdRows = 128;     // query rows (dq pass) or keys (dk/dv pass) per block
+constexpr int kWideKeys = 256;    // keys per block of the wide dk/dv group pass
 constexpr int kQKeys = 64;        // dq pass: keys per staged tile
 constexpr int kKQueries = 32;     // dk/dv pass: queries per staged tile
 constexpr int kDqStages = 4;      // LDS ring depth (dq pass)
@@ -76,6 +77,9 @@ struct BwdParams {
     const int4 *tiles;       // [hkv][max_tiles]: (sub-bucket, first entry, rows, group)
     const int32_t *ntiles;
     int max_tiles;
+    const int4 *tiles_w;     // the same for the wide dk/dv pass's tiles of 256 keys
+    const int32_t *ntiles_w;
+    int max_tiles_w;
     int row_tiles;  // window: 128-row tiles per head
     // outputs (fp32 partials): rows are positions (window) or entries (group)
     float *dq;      // [hq][rows][D]
@@ -1033,6 +1037,524 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
+// dk/dv group pass, wide form: 64 keys per wavefront
+//
+// Each wavefront holds two 32-key column blocks, so every Q / dO fragment
+// and every Q^T / dO^T transpose fragment read from LDS feeds two products
+// instead of one: fewer LDS reads, waits and per-tile bookkeeping per FLOP
+// than the 32-key form.  The dK and dV sums of 64 keys take 256 registers
+// per lane; they live in the AGPR file (one wavefront per SIMD has all 512
+// registers), written by the products below.  V stays in VGPRs; K sits in
+// LDS (64 KB per block), each lane reading back exactly the chunks it wrote,
+// so S takes one more 16-byte read per product.
+
+// One v_mfma_f32_32x32x16_bf16 accumulating into AGPRs.  The compiler does
+// not see inside the statement, so it carries the wait states itself: two
+// before the product, for an A/B operand a VALU instruction has just written
+// (LDS loads are covered by the compiler's own lgkmcnt waits).  Dependent
+// products into the same accumulator issue back to back; a read of the
+// accumulator needs the product to have landed (agpr_settle).
+__device__ __forceinline__ void mfma_agpr(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_agpr_zero(f32x16 &acc, const bf16x8 &z)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+}
+// 32 wait states: more than a 32x32x16 product needs before its result is
+// read by any other instruction
+__device__ __forceinline__ void agpr_settle()
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// NE consecutive floats of an LDS array (NE = 2 or 4)
+template <int NE>
+__device__ __forceinline__ void lds_floats(const float *p, float (&out)[NE])
+{
+    if constexpr (NE == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        out[0] = v.x;
+        out[1] = v.y;
+    } else {
+        static_assert(NE == 4, "two or four values per step");
+        const float4 v = *reinterpret_cast<const float4 *>(p);
+        out[0] = v.x;
+        out[1] = v.y;
+        out[2] = v.z;
+        out[3] = v.w;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_wide_kernel(BwdParams p)
+{
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int RB = D * 2;
+    constexpr int KB = 2;                  // 32-key column blocks per wavefront
+    constexpr int NP = 16 / KS;            // P elements per block per dP step
+    constexpr int NS = 16 / (2 * DB);      // dS elements per block per dV step
+    constexpr int NTR = 4 * DB;            // transpose fragments per tile (dO^T, then Q^T)
+    using Dma = TileDma<D, kKQueries>;
+    struct Stage {
+        char q[kKQueries * RB];
+        char d[kKQueries * RB];
+        int pos[kWave];        // query positions
+        float l2[kWave];       // query log-sum-exp times log2(e)
+        float dd[kWave];       // query D_i
+        uint32_t gm[kWave];    // query group bits
+    };
+    __shared__ __attribute__((aligned(16))) Stage stg[kDkvStages];
+    __shared__ __attribute__((aligned(16))) char k_lds[kBwdThreads / kWave][32 * KB * RB];
+    __shared__ int sub_start[kMaxCodes], sub_count[kMaxCodes], sub_owner[kMaxCodes], sub_tiles;
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int m = lane % 32;
+    const int h = lane / 32;
+
+    // ---- work item: (key/value head, tile of up to 256 keys of one
+    // sub-bucket); each XCD takes one contiguous range
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    if (b >= p.hkv * p.max_tiles_w)
+        return;
+    const int slot = b % p.max_tiles_w;
+    const int kvh = b / p.max_tiles_w;
+    if (slot >= p.ntiles_w[kvh])
+        return;
+    const int4 wt = p.tiles_w[(int64_t)kvh * p.max_tiles_w + slot];
+    const int sbk = wt.x;
+    const int64_t row0 = wt.y;
+    const int tile_keys = wt.z;
+    const int g = wt.w;
+    const int64_t rows = p.E;
+    const int32_t *tok = p.tokens + (int64_t)kvh * p.E;
+    const uint32_t *egm = p.egm + (int64_t)kvh * p.E;
+    const int w = p.window;
+
+    // ---- this lane's keys: column m of key blocks c (keys 64 wave + 32 c + m)
+    // per-lane LDS byte offsets: Q and dO rows (row sigma(m), chunk 2ks+h)
+    // and Q^T / dO^T by transpose reads (d = 32 db + m, queries
+    // 16h + 8t + 4s + 0..3; t adds 8 rows).  The swizzle only flips chunk
+    // bits, so k-step ks is the ks = 0 offset XOR 32 ks, and d-block db the
+    // db = 0 offset XOR 64 db.
+    const uint32_t qoff0 = rbyte<D>(sigma(m), h);
+    auto qoff = [&](int ks) { return qoff0 ^ (uint32_t)(32 * ks); };
+    uint32_t tro0[2];
+    {
+        const int jj = lane & 15, gp = (lane >> 4) & 1;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int row = 16 * h + 4 * s + (jj >> 2);
+            const int col = 16 * gp + 4 * (jj & 3);
+            tro0[s] = rbyte<D>(row, col >> 3) + (uint32_t)(col & 7) * 2u;
+        }
+    }
+    auto tro = [&](int db, int s) { return tro0[s] ^ (uint32_t)(64 * db); };
+    // key (c, m) of this wave sits at row 32 c + sigma(m) of its LDS K block,
+    // so the fragment reads use the Q offsets
+    char *const kl = k_lds[wave];
+
+    bool kvalid[KB];
+    int kpos[KB];
+    uint32_t kgm[KB];
+    bf16x8 vf[KB][KS];
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+        const int kr = wave * 32 * KB + 32 * c + m;
+        kvalid[c] = kr < tile_keys;
+        const int krc = kvalid[c] ? kr : 0;
+        kpos[c] = tok[row0 + krc];
+        kgm[c] = egm[row0 + krc];
+        const int64_t row = (int64_t)kvh * rows + row0 + krc;
+        const bf16x8 *ks_ = reinterpret_cast<const bf16x8 *>(p.k + row * D);
+        const bf16x8 *vs_ = reinterpret_cast<const bf16x8 *>(p.v + row * D);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            *reinterpret_cast<bf16x8 *>(kl + 32 * c * RB + qoff(ks)) = ks_[ks * 2 + h];
+            vf[c][ks] = vs_[ks * 2 + h];
+        }
+    }
+
+    // ---- the query sub-buckets of group g whose lower sets miss the key
+    // tile's, with the queries at or after (first key position + w), packed
+    // by wave 0
+    {
+        const int bk_min = tok[row0];  // keys ascend inside the sub-bucket
+        if (wave == 0) {
+            int ka, kb;
+            decode_lower(g, sbk - group_base(g, p.topk), ka, kb);
+            const int ncode = codes_of_group(g, p.topk);
+            const int gb = group_base(g, p.topk);
+            const int32_t *offh =
+                p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
+            const int64_t lim = (int64_t)bk_min + w;  // queries at or after lim
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            int kept = 0, tiles = 0;
+            for (int c0 = 0; c0 < ncode; c0 += 64) {
+                const int c = c0 + lane;
+                int cnt = 0, first = 0, owner = 0;
+                if (c < ncode) {
+                    int qa, qb;
+                    decode_lower(g, c, qa, qb);
+                    const bool meets = (qa >= 0 && (qa == ka || qa == kb)) ||
+                                       (qb >= 0 && (qb == ka || qb == kb));
+                    const int lo0 = offh[gb + c], hi0 = offh[gb + c + 1];
+                    first = hi0;
+                    if (!meets && hi0 > lo0) {
+                        int lo = lo0, hi = hi0;
+                        while (lo < hi) {
+                            const int mid = (lo + hi) >> 1;
+                            if ((int64_t)tok[mid] < lim)
+                                lo = mid + 1;
+                            else
+                                hi = mid;
+                        }
+                        first = lo;
+                    }
+                    cnt = hi0 - first;
+                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
+                }
+                const uint64_t keep = __ballot(cnt > 0);
+                if (cnt > 0) {
+                    const int at = kept + __popcll(keep & below);
+                    sub_start[at] = first;
+                    sub_count[at] = cnt;
+                    sub_owner[at] = owner;
+                }
+                kept += __popcll(keep);
+                tiles += (cnt + kKQueries - 1) / kKQueries;
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+                tiles += __shfl_xor(tiles, o);
+            if (lane == 0)
+                sub_tiles = tiles;
+        }
+        __syncthreads();
+    }
+    const int tiles_per_head = __builtin_amdgcn_readfirstlane(sub_tiles);
+    const int T = tiles_per_head * p.ratio;
+    // a tile whose first query is at or after this wave's largest kpos + w
+    // is seen by every key of the wave
+    int wave_lim = -0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+        if (kvalid[c])
+            wave_lim = std::max(wave_lim, kpos[c] + w);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        wave_lim = std::max(wave_lim, __shfl_xor(wave_lim, off));
+    wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
+
+    // ---- tiles in order, per query head (wave-uniform iterator; the issue
+    // side runs AHEAD tiles ahead of the compute side)
+    struct It {
+        int head, sub, tile, count, cnt, start, owner;
+    };
+    auto it_next = [&](It &t, int &head, int &origin, int &valid, int &owner) {
+        if (t.count == tiles_per_head) {  // next query head
+            ++t.head;
+            t.sub = -1;
+            t.tile = 0;
+            t.cnt = 0;
+            t.count = 0;
+        }
+        ++t.count;
+        head = kvh * p.ratio + t.head;
+        while (t.tile * kKQueries >= t.cnt) {
+            ++t.sub;
+            t.tile = 0;
+            t.cnt = __builtin_amdgcn_readfirstlane(sub_count[t.sub]);
+            t.start = __builtin_amdgcn_readfirstlane(sub_start[t.sub]);
+            t.owner = __builtin_amdgcn_readfirstlane(sub_owner[t.sub]);
+        }
+        valid = std::min(kKQueries, t.cnt - t.tile * kKQueries);
+        origin = t.start + t.tile * kKQueries;
+        owner = t.owner;
+        ++t.tile;
+    };
+    It it_issue{0, -1, 0, 0, 0, 0, 0}, it_comp{0, -1, 0, 0, 0, 0, 0};
+
+    // ---- staging: Q and dO tiles by LDS-DMA (all waves); per query the
+    // position (wave 0), log2-domain log-sum-exp (wave 1), D (wave 2) and
+    // group bits (wave 3) by 4-byte DMA
+    Dma dma;
+    dma.init(wave, lane);
+    constexpr int per_tile = 2 * Dma::LOADS + 1;  // each wave's loads per tile
+    constexpr int AHEAD = kDkvStages - 1;
+    auto issue = [&](int S) {
+        int head, origin, valid, owner;
+        it_next(it_issue, head, origin, valid, owner);
+        const int64_t r0 = (int64_t)head * rows + origin;
+        dma.issue(p.q + r0 * D, valid, lds_address(stg[S].q), wave);
+        dma.issue(p.dout + r0 * D, valid, lds_address(stg[S].d), wave);
+        const uint32_t lo = (uint32_t)std::min(lane, valid - 1) * 4u;
+        if (wave == 0)
+            dma4(tok + origin, lo, lds_address(stg[S].pos));
+        else if (wave == 1)
+            dma4(p.l2 + r0, lo, lds_address(stg[S].l2));
+        else if (wave == 2)
+            dma4(p.drow + r0, lo, lds_address(stg[S].dd));
+        else
+            dma4(egm + origin, lo, lds_address(stg[S].gm));
+    };
+
+    // dK^T and dV^T of both key blocks, in AGPRs, cleared by zero products
+    f32x16 dk_acc[KB][DB], dv_acc[KB][DB];
+    {
+        bf16x8 z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            z[e] = (__bf16)0.f;
+#pragma unroll
+        for (int c = 0; c < KB; ++c)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                mfma_agpr_zero(dk_acc[c][db], z);
+                mfma_agpr_zero(dv_acc[c][db], z);
+            }
+    }
+
+    const uint32_t low = (1u << g) - 1u;
+
+    // One query tile in stage S: S = Q K^T for both key blocks (each Q
+    // fragment read once, streamed two steps ahead); the query masks; dP =
+    // dO V^T with P formed between the products; dv^T += dO^T P and
+    // dk^T += Q^T dS, each transpose fragment read once (two ahead) for both
+    // blocks, dS formed between the dV products; then the DMA of tile
+    // u + AHEAD and the end-of-tile barrier.
+    auto body = [&](int S, int u) {
+        int head_c, origin, valid, owner;
+        it_next(it_comp, head_c, origin, valid, owner);
+        (void)head_c;
+        (void)origin;
+        const char *ql = stg[S].q;
+        const char *dl = stg[S].d;
+        const int qfirst = stg[S].pos[0];
+
+        f32x16 s[KB], dp[KB];
+#pragma unroll
+        for (int c = 0; c < KB; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[c][r] = dp[c][r] = 0.f;
+        // fragments streamed two steps ahead: Q then dO, and with each Q
+        // fragment the two key blocks' K fragments of the same k-step
+        bf16x8 fr[3], kfr[3][KB];
+        auto stream_at = [&](int n2) {
+            fr[n2 % 3] = lds16(n2 < KS ? ql : dl, qoff(n2 % KS));
+            if (n2 < KS) {
+#pragma unroll
+                for (int c = 0; c < KB; ++c)
+                    kfr[n2 % 3][c] = lds16(kl, (uint32_t)(32 * c * RB) + qoff(n2));
+            }
+        };
+        stream_at(0);
+        stream_at(1);
+        auto stream = [&](int i) {
+            if (i + 2 < 2 * KS)
+                stream_at(i + 2);
+        };
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            stream(i);
+#pragma unroll
+            for (int c = 0; c < KB; ++c)
+                s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3], kfr[i % 3][c], s[c], 0,
+                                                               0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // Queries each of this lane's keys sees, as a bit mask over the tile:
+        // the far ones (qpos >= kpos + w) are a suffix, since the queries
+        // ascend; in owner tiles also without a lower shared group.
+        const uint32_t vmask = valid == kKQueries ? 0xffffffffu : ((1u << valid) - 1u);
+        uint32_t qmask[KB];
+        bool need = false;
+#pragma unroll
+        for (int c = 0; c < KB; ++c) {
+            int qlo = 0;
+            if (__builtin_amdgcn_readfirstlane(qfirst) < wave_lim && kvalid[c]) {
+                const int lim = kpos[c] + w;
+                if (qfirst < lim) {
+                    int lo = 0, hi = valid;
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (stg[S].pos[mid] < lim)
+                            lo = mid + 1;
+                        else
+                            hi = mid;
+                    }
+                    qlo = lo;
+                }
+            }
+            qmask[c] = kvalid[c] && qlo < kKQueries ? (vmask & (0xffffffffu << qlo)) : 0u;
+            if (owner) {
+                for (int qi = 0; qi < valid; ++qi)
+                    if ((stg[S].gm[qi] & kgm[c] & low) != 0u)
+                        qmask[c] &= ~(1u << qi);
+            }
+            need |= kvalid[c] && qmask[c] != 0xffffffffu;
+        }
+        // this lane's 16 queries are 16h .. 16h + 15; a wave whose valid keys
+        // all see the whole tile skips the mask (the columns of keys past the
+        // tile's end are never stored)
+        const bool full = __builtin_amdgcn_ballot_w64(need) == 0;
+        uint32_t mh[KB];
+#pragma unroll
+        for (int c = 0; c < KB; ++c)
+            mh[c] = qmask[c] >> (16 * h);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // dP chain for both blocks; P of registers NP i .. NP i + NP - 1
+        // after step i (the log-sum-exp of those queries read alongside)
+        auto dp_chain = [&](auto masked) {
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+                stream(KS + i);
+                float l[NP];
+                lds_floats<NP>(stg[S].l2 + 16 * h + NP * i, l);
+#pragma unroll
+                for (int c = 0; c < KB; ++c)
+                    dp[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(KS + i) % 3], vf[c][i],
+                                                                    dp[c], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < KB; ++c)
+#pragma unroll
+                    for (int e = 0; e < NP; ++e) {
+                        const int r = NP * i + e;
+                        const float pr = __builtin_amdgcn_exp2f(s[c][r] * p.c - l[e]);
+                        if constexpr (decltype(masked)::value) {
+                            const int keep = __builtin_amdgcn_sbfe((int)mh[c], r, 1);  // 0 or -1
+                            s[c][r] = __int_as_float(__float_as_int(pr) & keep);
+                        } else {
+                            s[c][r] = pr;
+                        }
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (full)
+            dp_chain(std::false_type{});
+        else
+            dp_chain(std::true_type{});
+
+        // transpose fragments j = 0 .. NTR - 1: dO^T (db, t) for the dV
+        // products, then Q^T for the dK products; a ring of three, two ahead
+        bf16x8 trf[3];
+        auto tr_load = [&](int j) {
+            const int jj = j % (2 * DB);
+            const int db = jj / 2, t = jj % 2;
+            const uint32_t step = (uint32_t)(8 * t * RB);
+            trf[j % 3] = tr_frag(j < 2 * DB ? dl : ql, tro(db, 0) + step, tro(db, 1) + step);
+        };
+        tr_load(0);
+        tr_load(1);
+        bf16x8 pf[KB][2];
+#pragma unroll
+        for (int c = 0; c < KB; ++c) {
+            pf[c][0] = pack8(s[c], 0);
+            pf[c][1] = pack8(s[c], 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dv^T += dO^T P; dS of registers NS i .. NS i + NS - 1 after step i
+#pragma unroll
+        for (int i = 0; i < 2 * DB; ++i) {
+            const int db = i / 2, t = i % 2;
+            if (i + 2 < NTR)
+                tr_load(i + 2);
+            float dd[NS];
+            lds_floats<NS>(stg[S].dd + 16 * h + NS * i, dd);
+#pragma unroll
+            for (int c = 0; c < KB; ++c)
+                mfma_agpr(dv_acc[c][db], trf[i % 3], pf[c][t]);
+#pragma unroll
+            for (int c = 0; c < KB; ++c)
+#pragma unroll
+                for (int e = 0; e < NS; ++e) {
+                    const int r = NS * i + e;
+                    dp[c][r] = s[c][r] * (dp[c][r] - dd[e]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 dsf[KB][2];
+#pragma unroll
+        for (int c = 0; c < KB; ++c) {
+            dsf[c][0] = pack8(dp[c], 0);
+            dsf[c][1] = pack8(dp[c], 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dk^T += Q^T dS
+#pragma unroll
+        for (int i = 0; i < 2 * DB; ++i) {
+            const int j = 2 * DB + i;
+            const int db = i / 2, t = i % 2;
+            if (j + 2 < NTR)
+                tr_load(j + 2);
+#pragma unroll
+            for (int c = 0; c < KB; ++c)
+                mfma_agpr(dk_acc[c][db], trf[j % 3], dsf[c][t]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // tile u + AHEAD into the stage tile u - 1 left (every wave passed
+        // the barrier after it), then: tile u + 1 landed (the tiles after it
+        // may still fly) and every wave done with this stage
+        if (u + AHEAD < T)
+            issue(S == 0 ? kDkvStages - 1 : S - 1);
+        if (u + 1 < T) {
+            wait_vm_n((std::min(T - 1, u + AHEAD) - u - 1) * per_tile);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+    };
+
+    // the loads above have landed before any DMA is issued (the compiler's
+    // own wait tracking then has nothing outstanding in the loop)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    for (int i = 0; i < AHEAD && i < T; ++i)
+        issue(i);
+    wait_vm_n((std::min(T, AHEAD) - 1) * per_tile);
+    __syncthreads();
+    for (int u = 0, S = 0; u < T; ++u, S = S == kDkvStages - 1 ? 0 : S + 1)
+        body(S, u);
+
+    // the last products land before the accumulators are read
+    agpr_settle();
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            asm volatile("" : "+a"(dk_acc[c][db]), "+a"(dv_acc[c][db]));
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+        if (!kvalid[c])
+            continue;
+        const int kr = wave * 32 * KB + 32 * c + m;
+        float *dk = p.dk + ((int64_t)kvh * rows + row0 + kr) * D;
+        float *dv = p.dv + ((int64_t)kvh * rows + row0 + kr) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = db * 32 + 8 * j + 4 * h;
+                *reinterpret_cast<float4 *>(dk + d) = make_float4(
+                    dk_acc[c][db][4 * j] * p.scale, dk_acc[c][db][4 * j + 1] * p.scale,
+                    dk_acc[c][db][4 * j + 2] * p.scale, dk_acc[c][db][4 * j + 3] * p.scale);
+                *reinterpret_cast<float4 *>(dv + d) =
+                    make_float4(dv_acc[c][db][4 * j], dv_acc[c][db][4 * j + 1],
+                                dv_acc[c][db][4 * j + 2], dv_acc[c][db][4 * j + 3]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // row statistics, plan and merge
 
 // D_i = dO_i . O_i in fp32, one wavefront per row, and the row's
@@ -1060,7 +1582,8 @@ __global__ __launch_bounds__(256) void bwd_drow_kernel(const __bf16 *__restrict_
     }
 }
 
-// Tiles of up to 128 entries inside each sub-bucket, one block per head.
+// Tiles of up to ROWS entries inside each sub-bucket, one block per head.
+template <int ROWS>
 __global__ __launch_bounds__(256) void bwd_plan_kernel(const int32_t *__restrict__ offsets,
                                                        int K, int topk, int max_tiles,
                                                        int4 *__restrict__ tiles,
@@ -1074,7 +1597,7 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const int32_t *__restrict
         int acc = 0;
         for (int sb = 0; sb < nsb; ++sb) {
             base[sb] = acc;
-            acc += (off[sb + 1] - off[sb] + kBwdRows - 1) / kBwdRows;
+            acc += (off[sb + 1] - off[sb] + ROWS - 1) / ROWS;
         }
         base[nsb] = acc;
         ntiles[h] = acc;
@@ -1085,11 +1608,11 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const int32_t *__restrict
         int g = 0;
         while (g + 1 < K && group_base(g + 1, topk) <= sb)
             ++g;
-        for (int t = 0; t * kBwdRows < cnt; ++t) {
+        for (int t = 0; t * ROWS < cnt; ++t) {
             const int slot = base[sb] + t;
             if (slot < max_tiles)
                 tiles[(int64_t)h * max_tiles + slot] =
-                    make_int4(sb, lo + t * kBwdRows, std::min(kBwdRows, cnt - t * kBwdRows), g);
+                    make_int4(sb, lo + t * ROWS, std::min(ROWS, cnt - t * ROWS), g);
         }
     }
 }
@@ -1170,8 +1693,9 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(const float *__restrict_
 
 struct BwdLayout {
     size_t drow, l2, dq_win, dk_win, dv_win, dq_grp, dk_grp, dv_grp, tiles, ntiles;
+    size_t tiles_w, ntiles_w;
     size_t kg, vg, qg, dog, gl2, gd, egm, total;
-    int max_tiles;
+    int max_tiles, max_tiles_w;
 };
 
 BwdLayout bwd_layout(const AttnShape &sh)
@@ -1180,6 +1704,7 @@ BwdLayout bwd_layout(const AttnShape &sh)
     const int64_t n = sh.n, E = n * sh.topk;
     const int nsb = num_subbuckets(sh.K, sh.topk);
     L.max_tiles = (int)((E + kBwdRows - 1) / kBwdRows + nsb);
+    L.max_tiles_w = (int)((E + kWideKeys - 1) / kWideKeys + nsb);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -1196,6 +1721,8 @@ BwdLayout bwd_layout(const AttnShape &sh)
     L.dv_grp = take(sizeof(float) * sh.hkv * E * sh.d);
     L.tiles = take(sizeof(int4) * sh.hkv * (size_t)L.max_tiles);
     L.ntiles = take(sizeof(int32_t) * sh.hkv);
+    L.tiles_w = take(sizeof(int4) * sh.hkv * (size_t)L.max_tiles_w);
+    L.ntiles_w = take(sizeof(int32_t) * sh.hkv);
     // bucket-order copies read by the group passes
     L.kg = take(sizeof(__bf16) * sh.hkv * E * sh.d);
     L.vg = take(sizeof(__bf16) * sh.hkv * E * sh.d);
@@ -1247,6 +1774,9 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
     p.tiles = reinterpret_cast<const int4 *>(base + L.tiles);
     p.ntiles = reinterpret_cast<const int32_t *>(base + L.ntiles);
     p.max_tiles = L.max_tiles;
+    p.tiles_w = reinterpret_cast<const int4 *>(base + L.tiles_w);
+    p.ntiles_w = reinterpret_cast<const int32_t *>(base + L.ntiles_w);
+    p.max_tiles_w = L.max_tiles_w;
     p.row_tiles = (int)((n + kBwdRows - 1) / kBwdRows);
 
     const int64_t qrows = (int64_t)sh.hq * n;
@@ -1254,10 +1784,12 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
                        static_cast<const __bf16 *>(out), p.dout, lse, qrows,
                        reinterpret_cast<float *>(base + L.drow),
                        reinterpret_cast<float *>(base + L.l2));
-    hipLaunchKernelGGL(bwd_plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets, sh.K, sh.topk,
-                       L.max_tiles,
-                       reinterpret_cast<int4 *>(base + L.tiles),
+    hipLaunchKernelGGL(bwd_plan_kernel<kBwdRows>, dim3(sh.hkv), dim3(256), 0, s, offsets, sh.K,
+                       sh.topk, L.max_tiles, reinterpret_cast<int4 *>(base + L.tiles),
                        reinterpret_cast<int32_t *>(base + L.ntiles));
+    hipLaunchKernelGGL(bwd_plan_kernel<kWideKeys>, dim3(sh.hkv), dim3(256), 0, s, offsets, sh.K,
+                       sh.topk, L.max_tiles_w, reinterpret_cast<int4 *>(base + L.tiles_w),
+                       reinterpret_cast<int32_t *>(base + L.ntiles_w));
 
     // window pass: rows in position order
     p.dq = reinterpret_cast<float *>(base + L.dq_win);
@@ -1300,7 +1832,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
         pg.dv = reinterpret_cast<float *>(base + L.dv_grp);
         hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(xcd_grid(sh.hq * L.max_tiles)),
                            dim3(kDqThreads), 0, s, pg);
-        hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3(xcd_grid(sh.hkv * L.max_tiles)),
+        hipLaunchKernelGGL(bwd_dkv_wide_kernel<D>, dim3(xcd_grid(sh.hkv * L.max_tiles_w)),
                            dim3(kBwdThreads), 0, s, pg);
     }
     // merge
