@@ -24,11 +24,13 @@
 //     S^T = K Q^T and dP^T = V dO^T put one query per lane column, dS^T
 //     feeds dq^T += K^T dS^T from registers, and the halves' sums are added
 //     at the end.
-//   * dk/dv pass (key-major): a block of 4 wavefronts owns 128 keys with K
-//     and V in registers and walks the 32-query tiles that see them, for
-//     every query head of the key/value head; S = Q K^T and dP = dO V^T put
-//     one key per lane column, P and dS feed dv^T += dO^T P and
-//     dk^T += Q^T dS.
+//   * dk/dv pass (key-major): a block of 4 wavefronts walks the 32-query
+//     tiles that see its keys, for every query head of the key/value head;
+//     S = Q K^T and dP = dO V^T put one key per lane column, P and dS feed
+//     dv^T += dO^T P and dk^T += Q^T dS.  The window pass gives each
+//     wavefront 32 keys (K and V in registers); the group pass gives it 64
+//     (two column blocks sharing every LDS fragment read, the dK / dV sums
+//     in AGPRs, K in LDS).
 // Each pass writes fp32 partials (per position for the window, per bucket
 // entry for the groups); a merge kernel adds a row's window part and its k
 // group parts and rounds to bf16.
@@ -601,10 +603,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dk/dv pass
+// dk/dv window pass (32 keys per wavefront)
 
-template <int D, bool GROUP>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_window_kernel(BwdParams p)
 {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -613,14 +615,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     struct Stage {
         char q[kKQueries * RB];
         char d[kKQueries * RB];
-        int pos[kWave];        // query positions (group pass)
         float l2[kWave];       // query log-sum-exp times log2(e)
         float dd[kWave];       // query D_i
-        uint32_t gm[kWave];    // query group bits (group pass)
     };
     __shared__ __attribute__((aligned(16))) Stage stg[kDkvStages];
-    __shared__ int sub_start[GROUP ? kMaxCodes : 1], sub_count[GROUP ? kMaxCodes : 1],
-        sub_owner[GROUP ? kMaxCodes : 1], sub_tiles;
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -631,34 +629,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     // contiguous range (the grid is a multiple of 8 long), so neighbouring
     // key tiles, which stream the same query tiles, share its L2
     const int b = xcd_remap(blockIdx.x, gridDim.x);
-    const int tiles_per_kvh = GROUP ? p.max_tiles : p.row_tiles;
-    if (b >= p.hkv * tiles_per_kvh)
+    if (b >= p.hkv * p.row_tiles)
         return;
-    const int slot = b % tiles_per_kvh;
-    const int kvh = b / tiles_per_kvh;
-    if (GROUP && slot >= p.ntiles[kvh])
-        return;
-    int g = 0, sbk = 0, tile_keys;
-    int64_t row0;
-    if (GROUP) {
-        const int4 t = p.tiles[(int64_t)kvh * p.max_tiles + slot];
-        sbk = t.x;
-        row0 = t.y;
-        tile_keys = t.z;
-        g = t.w;
-    } else {
-        row0 = (int64_t)slot * kBwdRows;
-        tile_keys = (int)std::min<int64_t>(kBwdRows, p.n - row0);
-    }
-    const int64_t rows = GROUP ? p.E : p.n;
-    const int32_t *tok = GROUP ? p.tokens + (int64_t)kvh * p.E : nullptr;
-    const uint32_t *egm = GROUP ? p.egm + (int64_t)kvh * p.E : nullptr;
+    const int slot = b % p.row_tiles;
+    const int kvh = b / p.row_tiles;
+    const int64_t row0 = (int64_t)slot * kBwdRows;
+    const int tile_keys = (int)std::min<int64_t>(kBwdRows, p.n - row0);
+    const int64_t rows = p.n;
 
     // ---- this lane's key (column m of the wavefront's 32 keys)
     const int kr = wave * 32 + m;
     const bool kvalid = kr < tile_keys;
     const int krc = kvalid ? kr : 0;
-    const int kpos = GROUP ? tok[row0 + krc] : (int)(row0 + krc);
+    const int kpos = (int)(row0 + krc);
     bf16x8 kf[KS], vf[KS];
     {
         const int64_t row = (int64_t)kvh * rows + row0 + krc;
@@ -670,145 +653,58 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             vf[ks] = vs_[ks * 2 + h];
         }
     }
-    const uint32_t kgm = GROUP ? egm[row0 + krc] : 0u;
     const int w = p.window;
 
-    // ---- query tiles, per query head
+    // ---- query tiles, per query head: the queries i with 0 <= i - j < w of
+    // the tile's keys j
     int tiles_per_head = 0;
     int64_t i_first = 0;
-    if (GROUP) {
-        const int bk_min = tok[row0];  // keys ascend inside the sub-bucket
-        // the query sub-buckets of group g whose lower sets miss the key
-        // tile's, with the queries at or after (first key position + w),
-        // packed by wave 0
-        if (wave == 0) {
-            int ka, kb;
-            decode_lower(g, sbk - group_base(g, p.topk), ka, kb);
-            const int ncode = codes_of_group(g, p.topk);
-            const int gb = group_base(g, p.topk);
-            const int32_t *offh =
-                p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
-            const int64_t lim = (int64_t)bk_min + w;  // queries at or after lim
-            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-            int kept = 0, tiles = 0;
-            for (int c0 = 0; c0 < ncode; c0 += 64) {
-                const int c = c0 + lane;
-                int cnt = 0, first = 0, owner = 0;
-                if (c < ncode) {
-                    int qa, qb;
-                    decode_lower(g, c, qa, qb);
-                    const bool meets = (qa >= 0 && (qa == ka || qa == kb)) ||
-                                       (qb >= 0 && (qb == ka || qb == kb));
-                    const int lo0 = offh[gb + c], hi0 = offh[gb + c + 1];
-                    first = hi0;
-                    if (!meets && hi0 > lo0) {
-                        int lo = lo0, hi = hi0;
-                        while (lo < hi) {
-                            const int mid = (lo + hi) >> 1;
-                            if ((int64_t)tok[mid] < lim)
-                                lo = mid + 1;
-                            else
-                                hi = mid;
-                        }
-                        first = lo;
-                    }
-                    cnt = hi0 - first;
-                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
-                }
-                const uint64_t keep = __ballot(cnt > 0);
-                if (cnt > 0) {
-                    const int at = kept + __popcll(keep & below);
-                    sub_start[at] = first;
-                    sub_count[at] = cnt;
-                    sub_owner[at] = owner;
-                }
-                kept += __popcll(keep);
-                tiles += (cnt + kKQueries - 1) / kKQueries;
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1)
-                tiles += __shfl_xor(tiles, o);
-            if (lane == 0)
-                sub_tiles = tiles;
-        }
-        __syncthreads();
-        tiles_per_head = sub_tiles;
-    } else if (w > 0) {
+    if (w > 0) {
         i_first = row0;
         const int64_t i_last = std::min<int64_t>(p.n - 1, row0 + tile_keys - 1 + w - 1);
         tiles_per_head = (int)((i_last - i_first) / kKQueries + 1);
     }
     tiles_per_head = __builtin_amdgcn_readfirstlane(tiles_per_head);
     const int T = tiles_per_head * p.ratio;
-    // a tile whose first query is at or after this wave's largest kpos + w
-    // is seen by every key of the wave (group pass)
-    int wave_lim = kvalid ? kpos + w : -0x7fffffff;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        wave_lim = std::max(wave_lim, __shfl_xor(wave_lim, off));
-    wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
 
     // ---- tiles in order, per query head (wave-uniform iterator; the issue
     // side runs two tiles ahead of the compute side)
     struct It {
-        int head, sub, tile, count, cnt, start, owner;
+        int head, tile, count;
     };
-    auto it_next = [&](It &t, int &head, int &origin, int &valid, int &owner) {
+    auto it_next = [&](It &t, int &head, int &origin, int &valid) {
         if (t.count == tiles_per_head) {  // next query head
             ++t.head;
-            t.sub = -1;
             t.tile = 0;
-            t.cnt = 0;
             t.count = 0;
         }
         ++t.count;
         head = kvh * p.ratio + t.head;
-        if (GROUP) {
-            while (t.tile * kKQueries >= t.cnt) {
-                ++t.sub;
-                t.tile = 0;
-                t.cnt = __builtin_amdgcn_readfirstlane(sub_count[t.sub]);
-                t.start = __builtin_amdgcn_readfirstlane(sub_start[t.sub]);
-                t.owner = __builtin_amdgcn_readfirstlane(sub_owner[t.sub]);
-            }
-            valid = std::min(kKQueries, t.cnt - t.tile * kKQueries);
-            origin = t.start + t.tile * kKQueries;
-            owner = t.owner;
-        } else {
-            origin = (int)(i_first + (int64_t)t.tile * kKQueries);
-            valid = (int)std::min<int64_t>(kKQueries, p.n - origin);
-            owner = 0;
-        }
+        origin = (int)(i_first + (int64_t)t.tile * kKQueries);
+        valid = (int)std::min<int64_t>(kKQueries, p.n - origin);
         ++t.tile;
     };
-    It it_issue{0, -1, 0, 0, 0, 0, 0}, it_comp{0, -1, 0, 0, 0, 0, 0};
+    It it_issue{0, 0, 0}, it_comp{0, 0, 0};
 
     // ---- staging: Q and dO tiles by LDS-DMA (all waves); per query, the
-    // log2-domain log-sum-exp (wave 1) and D (wave 2), and in the group pass
-    // the position (wave 0) and group bits (wave 3), by 4-byte DMA
+    // log2-domain log-sum-exp (wave 1) and D (wave 2) by 4-byte DMA
     Dma dma;
     dma.init(wave, lane);
     constexpr int DMA_QD = 2 * Dma::LOADS;
-    const bool extra = GROUP ? true : (wave == 1 || wave == 2);
+    const bool extra = wave == 1 || wave == 2;
     const int per_tile = DMA_QD + (extra ? 1 : 0);  // this wave's loads per tile
     constexpr int AHEAD = kDkvStages - 1;             // tiles in flight ahead
     auto issue = [&](int S) {
-        int head, origin, valid, owner;
-        it_next(it_issue, head, origin, valid, owner);
+        int head, origin, valid;
+        it_next(it_issue, head, origin, valid);
         const int64_t r0 = (int64_t)head * rows + origin;
         dma.issue(p.q + r0 * D, valid, lds_address(stg[S].q), wave);
         dma.issue(p.dout + r0 * D, valid, lds_address(stg[S].d), wave);
         const uint32_t lo = (uint32_t)std::min(lane, valid - 1) * 4u;
-        if (wave == 0) {
-            if (GROUP)
-                dma4(tok + origin, lo, lds_address(stg[S].pos));
-        } else if (wave == 1) {
+        if (wave == 1)
             dma4(p.l2 + r0, lo, lds_address(stg[S].l2));
-        } else if (wave == 2) {
+        else if (wave == 2)
             dma4(p.drow + r0, lo, lds_address(stg[S].dd));
-        } else if (GROUP) {
-            dma4(egm + origin, lo, lds_address(stg[S].gm));
-        }
     };
 
     f32x16 dk_acc[DB], dv_acc[DB];
@@ -837,8 +733,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
             }
     }
 
-    const uint32_t low = GROUP ? ((1u << g) - 1u) : 0u;
-
     // One query tile in stage S, ordered so that the vector work overlaps
     // the matrix cores: S = Q K^T (16-byte fragments streamed two steps
     // ahead, the transpose reads of dO^T in between); the key's query mask;
@@ -848,12 +742,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
     // transpose reads in between; dk^T += Q^T dS; then the DMA of tile
     // u + AHEAD and the end-of-tile barrier.
     auto body = [&](int S, int u) {
-        int head_c, origin, valid, owner;
-        it_next(it_comp, head_c, origin, valid, owner);
+        int head_c, origin, valid;
+        it_next(it_comp, head_c, origin, valid);
         (void)head_c;
         const char *ql = stg[S].q;
         const char *dl = stg[S].d;
-        const int qfirst = GROUP ? stg[S].pos[0] : 0;
 
         f32x16 s, dp;
 #pragma unroll
@@ -891,41 +784,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams p)
         for (int j = 0; j < 4; ++j)
             l4[j] = reinterpret_cast<const float4 *>(stg[S].l2)[4 * h + j];
 
-        // Queries this lane's key sees, as a bit mask over the tile: an
-        // interval (window: 0 <= qpos - kpos < w; group: the queries ascend,
-        // the far ones qpos >= kpos + w are a suffix), in the group pass's
-        // owner tiles also without a lower shared group.
-        uint32_t qmask;
-        if (GROUP) {
-            const uint32_t vmask = valid == kKQueries ? 0xffffffffu : ((1u << valid) - 1u);
-            int qlo = 0;
-            if (__builtin_amdgcn_readfirstlane(qfirst) < wave_lim && kvalid) {
-                const int lim = kpos + w;
-                if (qfirst < lim) {
-                    int lo = 0, hi = valid;
-                    while (lo < hi) {
-                        const int mid = (lo + hi) >> 1;
-                        if (stg[S].pos[mid] < lim)
-                            lo = mid + 1;
-                        else
-                            hi = mid;
-                    }
-                    qlo = lo;
-                }
-            }
-            qmask = kvalid && qlo < kKQueries ? (vmask & (0xffffffffu << qlo)) : 0u;
-            if (owner) {
-                for (int qi = 0; qi < valid; ++qi)
-                    if ((stg[S].gm[qi] & kgm & low) != 0u)
-                        qmask &= ~(1u << qi);
-            }
-        } else {
-            const int qlo = std::max(0, kpos - origin);
-            const int qhi = std::min(valid - 1, kpos - origin + w - 1);
-            qmask = kvalid && qhi >= qlo
-                        ? (uint32_t)((2ull << qhi) - (1ull << qlo))
-                        : 0u;
-        }
+        // Queries this lane's key sees, as a bit mask over the tile: the
+        // interval 0 <= qpos - kpos < w.
+        const int qlo = std::max(0, kpos - origin);
+        const int qhi = std::min(valid - 1, kpos - origin + w - 1);
+        const uint32_t qmask =
+            kvalid && qhi >= qlo ? (uint32_t)((2ull << qhi) - (1ull << qlo)) : 0u;
         // this lane's 16 queries are 16h .. 16h + 15; a wave whose valid
         // keys all see the whole tile skips the mask (the columns of keys
         // past the tile's end are never stored)
@@ -1797,7 +1661,7 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
     p.dv = reinterpret_cast<float *>(base + L.dv_win);
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(xcd_grid(sh.hq * p.row_tiles)),
                        dim3(kDqThreads), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3(xcd_grid(sh.hkv * p.row_tiles)),
+    hipLaunchKernelGGL(bwd_dkv_window_kernel<D>, dim3(xcd_grid(sh.hkv * p.row_tiles)),
                        dim3(kBwdThreads), 0, s, p);
 
     // group pass: rows gathered into bucket order first
