@@ -31,9 +31,10 @@
 //     wavefront 32 keys (K and V in registers); the group pass gives it 64
 //     (two column blocks sharing every LDS fragment read, the dK / dV sums
 //     in AGPRs, K in LDS).
-// Each pass writes fp32 partials (per position for the window, per bucket
-// entry for the groups); a merge kernel adds a row's window part and its k
-// group parts and rounds to bf16.
+// The group passes run first and write fp32 partials per bucket entry; the
+// window passes then add, in their epilogues, a row's window part and its k
+// group parts (found through slot_entry) and round the sum to bf16, so the
+// window parts never go to memory.
 //
 // Data movement.  The group passes read copies of their rows gathered into
 // bucket (entry) order by a prepare kernel, so that every staged tile, in
@@ -83,9 +84,14 @@ struct BwdParams {
     const int32_t *ntiles_w;
     int max_tiles_w;
     int row_tiles;  // window: 128-row tiles per head
-    // outputs (fp32 partials): rows are positions (window) or entries (group)
-    float *dq;      // [hq][rows][D]
-    float *dk, *dv; // [hkv][rows][D]
+    // group passes: fp32 partials per entry, [hq][E][D] and [hkv][E][D]
+    float *dq;
+    float *dk, *dv;
+    // window passes: the group partials to add, each row's entries, and the
+    // bf16 results [hq][n][D] and [hkv][n][D]
+    const float *grp_dq, *grp_dk, *grp_dv;
+    const int32_t *slot_entry;
+    __bf16 *out_dq, *out_dk, *out_dv;
 };
 
 // XOR swizzle of the 16-byte chunks of a row-major [rows][D] tile (chunk c of
@@ -199,6 +205,28 @@ __device__ __forceinline__ void wait_vm_n(int n)
         break;
     }
 #undef FOCUS_WAIT_CASE
+}
+
+// a += the group partials of a row's entries, in slot order, at one float4
+// of d: grp points at element d of the head's entry 0, rows D floats apart
+template <int D>
+__device__ __forceinline__ void add_group_parts(float4 &a, const float *grp,
+                                                const int32_t *slot_entry, int topk)
+{
+    for (int s = 0; s < topk; ++s) {
+        const float4 b = *reinterpret_cast<const float4 *>(grp + (int64_t)slot_entry[s] * D);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+}
+__device__ __forceinline__ void store_bf16x4(__bf16 *o, const float4 &a)
+{
+    o[0] = (__bf16)a.x;
+    o[1] = (__bf16)a.y;
+    o[2] = (__bf16)a.z;
+    o[3] = (__bf16)a.w;
 }
 
 // ---------------------------------------------------------------------------
@@ -587,17 +615,36 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
     }
     __syncthreads();
     if (kh == 0 && qvalid) {
-        float *dst = p.dq + ((int64_t)hq * rows + row0 + qr) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[db][r] += red[((qg * DB + db) * 16 + r) * kWave + lane];
+        if (GROUP) {
+            float *dst = p.dq + ((int64_t)hq * rows + row0 + qr) * D;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * h) =
-                    make_float4(acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale,
-                                acc[db][4 * j + 2] * p.scale, acc[db][4 * j + 3] * p.scale);
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * h) =
+                        make_float4(acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale,
+                                    acc[db][4 * j + 2] * p.scale, acc[db][4 * j + 3] * p.scale);
+        } else {
+            // the row's window part plus its group parts, rounded once
+            const int64_t t = row0 + qr;
+            const int32_t *se = p.slot_entry + ((int64_t)kvh * p.n + t) * p.topk;
+            __bf16 *dst = p.out_dq + ((int64_t)hq * p.n + t) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = db * 32 + 8 * j + 4 * h;
+                    float4 a = make_float4(acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale,
+                                           acc[db][4 * j + 2] * p.scale,
+                                           acc[db][4 * j + 3] * p.scale);
+                    add_group_parts<D>(a, p.grp_dq + (int64_t)hq * p.E * D + d, se, p.topk);
+                    store_bf16x4(dst + d, a);
+                }
         }
     }
 }
@@ -883,19 +930,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_window_kernel(BwdParam
         body(S, u);
 
     if (kvalid) {
-        float *dk = p.dk + ((int64_t)kvh * rows + row0 + kr) * D;
-        float *dv = p.dv + ((int64_t)kvh * rows + row0 + kr) * D;
+        // the key's window part plus its group parts, rounded once
+        const int32_t *se = p.slot_entry + ((int64_t)kvh * p.n + kpos) * p.topk;
+        __bf16 *dk = p.out_dk + ((int64_t)kvh * p.n + kpos) * D;
+        __bf16 *dv = p.out_dv + ((int64_t)kvh * p.n + kpos) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d = db * 32 + 8 * j + 4 * h;
-                *reinterpret_cast<float4 *>(dk + d) =
-                    make_float4(dk_acc[db][4 * j] * p.scale, dk_acc[db][4 * j + 1] * p.scale,
-                                dk_acc[db][4 * j + 2] * p.scale, dk_acc[db][4 * j + 3] * p.scale);
-                *reinterpret_cast<float4 *>(dv + d) =
-                    make_float4(dv_acc[db][4 * j], dv_acc[db][4 * j + 1], dv_acc[db][4 * j + 2],
-                                dv_acc[db][4 * j + 3]);
+                float4 a = make_float4(dk_acc[db][4 * j] * p.scale, dk_acc[db][4 * j + 1] * p.scale,
+                                       dk_acc[db][4 * j + 2] * p.scale,
+                                       dk_acc[db][4 * j + 3] * p.scale);
+                add_group_parts<D>(a, p.grp_dk + (int64_t)kvh * p.E * D + d, se, p.topk);
+                store_bf16x4(dk + d, a);
+                float4 b = make_float4(dv_acc[db][4 * j], dv_acc[db][4 * j + 1],
+                                       dv_acc[db][4 * j + 2], dv_acc[db][4 * j + 3]);
+                add_group_parts<D>(b, p.grp_dv + (int64_t)kvh * p.E * D + d, se, p.topk);
+                store_bf16x4(dv + d, b);
             }
     }
 }
@@ -1419,7 +1471,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_wide_kernel(BwdParams 
 }
 
 // ---------------------------------------------------------------------------
-// row statistics, plan and merge
+// row statistics, plan and the bucket-order copies
 
 // D_i = dO_i . O_i in fp32, one wavefront per row, and the row's
 // log-sum-exp in the log2 domain (L_i log2 e) for the exp2 of the passes.
@@ -1521,42 +1573,8 @@ __global__ __launch_bounds__(256) void bwd_gather_scalars_kernel(
         egm[idx] = gmask[(idx / E) * n + tokens[idx]];
 }
 
-// out[head][t] = win[head][t] + sum_s grp[head'][slot_entry[t][s]], in bf16;
-// the bucket arrays are per key/value head (head' = head / ratio).
-template <int D>
-__global__ __launch_bounds__(256) void bwd_merge_kernel(const float *__restrict__ win,
-                                                        const float *__restrict__ grp,
-                                                        const int32_t *__restrict__ slot_entry,
-                                                        int heads, int ratio, int64_t n,
-                                                        int64_t E, int topk,
-                                                        __bf16 *__restrict__ out)
-{
-    constexpr int V4 = D / 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (int64_t)heads * n * V4)
-        return;
-    const int c = (int)(idx % V4);
-    const int64_t ht = idx / V4;
-    const int64_t head = ht / n, t = ht % n;
-    const int64_t kvh = head / ratio;
-    float4 a = reinterpret_cast<const float4 *>(win + ht * D)[c];
-    for (int s = 0; s < topk; ++s) {
-        const int64_t e = slot_entry[(kvh * n + t) * topk + s];
-        const float4 b = reinterpret_cast<const float4 *>(grp + (head * E + e) * D)[c];
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
-    }
-    __bf16 *o = out + ht * D + c * 4;
-    o[0] = (__bf16)a.x;
-    o[1] = (__bf16)a.y;
-    o[2] = (__bf16)a.z;
-    o[3] = (__bf16)a.w;
-}
-
 struct BwdLayout {
-    size_t drow, l2, dq_win, dk_win, dv_win, dq_grp, dk_grp, dv_grp, tiles, ntiles;
+    size_t drow, l2, dq_grp, dk_grp, dv_grp, tiles, ntiles;
     size_t tiles_w, ntiles_w;
     size_t kg, vg, qg, dog, gl2, gd, egm, total;
     int max_tiles, max_tiles_w;
@@ -1577,9 +1595,6 @@ BwdLayout bwd_layout(const AttnShape &sh)
     };
     L.drow = take(sizeof(float) * sh.hq * n);
     L.l2 = take(sizeof(float) * sh.hq * n);
-    L.dq_win = take(sizeof(float) * sh.hq * n * sh.d);
-    L.dk_win = take(sizeof(float) * sh.hkv * n * sh.d);
-    L.dv_win = take(sizeof(float) * sh.hkv * n * sh.d);
     L.dq_grp = take(sizeof(float) * sh.hq * E * sh.d);
     L.dk_grp = take(sizeof(float) * sh.hkv * E * sh.d);
     L.dv_grp = take(sizeof(float) * sh.hkv * E * sh.d);
@@ -1655,16 +1670,8 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
                        sh.topk, L.max_tiles_w, reinterpret_cast<int4 *>(base + L.tiles_w),
                        reinterpret_cast<int32_t *>(base + L.ntiles_w));
 
-    // window pass: rows in position order
-    p.dq = reinterpret_cast<float *>(base + L.dq_win);
-    p.dk = reinterpret_cast<float *>(base + L.dk_win);
-    p.dv = reinterpret_cast<float *>(base + L.dv_win);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(xcd_grid(sh.hq * p.row_tiles)),
-                       dim3(kDqThreads), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_window_kernel<D>, dim3(xcd_grid(sh.hkv * p.row_tiles)),
-                       dim3(kBwdThreads), 0, s, p);
-
-    // group pass: rows gathered into bucket order first
+    // group pass first (rows gathered into bucket order), then the window
+    // pass, which adds each row's group partials and writes the results
     if (E > 0) {
         __bf16 *kg = reinterpret_cast<__bf16 *>(base + L.kg);
         __bf16 *vg = reinterpret_cast<__bf16 *>(base + L.vg);
@@ -1699,20 +1706,17 @@ hipError_t launch_bwd_d(const AttnShape &sh, const void *q, const void *k, const
         hipLaunchKernelGGL(bwd_dkv_wide_kernel<D>, dim3(xcd_grid(sh.hkv * L.max_tiles_w)),
                            dim3(kBwdThreads), 0, s, pg);
     }
-    // merge
-    const int64_t qv = qrows * (D / 4), kv = (int64_t)sh.hkv * n * (D / 4);
-    hipLaunchKernelGGL(bwd_merge_kernel<D>, dim3((unsigned)((qv + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<const float *>(base + L.dq_win),
-                       reinterpret_cast<const float *>(base + L.dq_grp), slot_entry, sh.hq,
-                       p.ratio, n, E, sh.topk, static_cast<__bf16 *>(dq));
-    hipLaunchKernelGGL(bwd_merge_kernel<D>, dim3((unsigned)((kv + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<const float *>(base + L.dk_win),
-                       reinterpret_cast<const float *>(base + L.dk_grp), slot_entry, sh.hkv, 1,
-                       n, E, sh.topk, static_cast<__bf16 *>(dk));
-    hipLaunchKernelGGL(bwd_merge_kernel<D>, dim3((unsigned)((kv + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<const float *>(base + L.dv_win),
-                       reinterpret_cast<const float *>(base + L.dv_grp), slot_entry, sh.hkv, 1,
-                       n, E, sh.topk, static_cast<__bf16 *>(dv));
+    p.grp_dq = reinterpret_cast<const float *>(base + L.dq_grp);
+    p.grp_dk = reinterpret_cast<const float *>(base + L.dk_grp);
+    p.grp_dv = reinterpret_cast<const float *>(base + L.dv_grp);
+    p.slot_entry = slot_entry;
+    p.out_dq = static_cast<__bf16 *>(dq);
+    p.out_dk = static_cast<__bf16 *>(dk);
+    p.out_dv = static_cast<__bf16 *>(dv);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(xcd_grid(sh.hq * p.row_tiles)),
+                       dim3(kDqThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_window_kernel<D>, dim3(xcd_grid(sh.hkv * p.row_tiles)),
+                       dim3(kBwdThreads), 0, s, p);
     return hipGetLastError();
 }
 

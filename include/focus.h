@@ -295,11 +295,10 @@ focus_status focus_attn_fwd_part(const void *q, const void *k, const void *v,
  *   dq            bf16 [Hq, n, d]  out
  *   dk, dv        bf16 [Hkv, n, d] out
  *   workspace     >= focus_attn_bwd_workspace_bytes(...) bytes: fp32
- *                 partials of every row and bucket entry, the tile plan,
- *                 and bf16 copies of q, dout, k and v (with the rows'
- *                 statistics) gathered into bucket order for the group
- *                 passes (about 113 GiB at 1M tokens, 32/8 heads of 128,
- *                 top-2)
+ *                 partials of every bucket entry, the tile plans, and bf16
+ *                 copies of q, dout, k and v (with the rows' statistics)
+ *                 gathered into bucket order for the group passes (about
+ *                 89 GiB at 1M tokens, 32/8 heads of 128, top-2)
  * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are
  * rounded to bf16 as MFMA operands; outputs rounded to nearest even.
  * Deterministic (no atomics): two runs give the same bits.
