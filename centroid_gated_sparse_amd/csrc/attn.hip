@@ -553,7 +553,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     const int h = lane / 32;
 
     // ---- which work item this block owns
-    const int b_lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int b_lin = (GROUP && p.order != nullptr) ? p.order[blockIdx.x]
+                                                    : xcd_remap(blockIdx.x, gridDim.x);
     if (b_lin >= p.total_blocks)
         return;
     int kvh, hg, slot;
@@ -1379,12 +1380,22 @@ __global__ __launch_bounds__(256) void gather_entries_kernel(const uint32_t *__r
 // Tile list of the group pass: for routing head h, every sub-bucket cut into
 // query tiles of `rows` entries, last tile (latest positions, most keys)
 // first.  tiles[h][i] = {sub-bucket, first entry, entry count, group}.
+//
+// With `work` given, each tile also gets an estimate of its key work, in
+// [0, 1]: (last query position - w) / n times the share of the head's
+// entries in the key sub-buckets its block visits (those whose lower sets
+// miss the tile's), which is the block's key count if keys spread evenly
+// over positions.  order_kernel sorts blocks by it.
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ offsets, int K,
                                                    int topk, int rows, int max_tiles,
                                                    int4 *__restrict__ tiles,
-                                                   int32_t *__restrict__ ntiles)
+                                                   int32_t *__restrict__ ntiles,
+                                                   const int32_t *__restrict__ tokens, int64_t n,
+                                                   int64_t E, int window,
+                                                   float *__restrict__ work)
 {
     __shared__ int start[kMaxSubbuckets + 1];
+    __shared__ int compat[kMaxSubbuckets];
     const int nsb = num_subbuckets(K, topk);
     const int h = blockIdx.x;
     const int32_t *off = offsets + (int64_t)h * (nsb + 1);
@@ -1397,8 +1408,30 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
         start[nsb] = acc;
         ntiles[h] = acc;
     }
+    if (work != nullptr) {
+        // entries of the key sub-buckets a query sub-bucket's blocks visit
+        for (int sb = threadIdx.x; sb < nsb; sb += blockDim.x) {
+            int g = 0;
+            while (g + 1 < K && group_base(g + 1, topk) <= sb)
+                ++g;
+            const int gb = group_base(g, topk);
+            int qa, qb;
+            decode_lower(g, sb - gb, qa, qb);
+            int c = 0;
+            for (int code = 0; code < codes_of_group(g, topk); ++code) {
+                int ka, kb;
+                decode_lower(g, code, ka, kb);
+                const bool meets = (ka >= 0 && (ka == qa || ka == qb)) ||
+                                   (kb >= 0 && (kb == qa || kb == qb));
+                if (!meets)
+                    c += off[gb + code + 1] - off[gb + code];
+            }
+            compat[sb] = c;
+        }
+    }
     __syncthreads();
     int4 *th = tiles + (int64_t)h * max_tiles;
+    const int32_t *tok = tokens + (int64_t)h * E;
     int g = 0;
     for (int sb = 0; sb < nsb; ++sb) {
         while (g + 1 < K && group_base(g + 1, topk) <= sb)
@@ -1407,9 +1440,77 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
         const int cnt = off[sb + 1] - off[sb];
         for (int j = threadIdx.x; j < nt; j += blockDim.x) {
             const int jj = nt - 1 - j;
-            th[start[sb] + j] = make_int4(sb, off[sb] + jj * rows, min(rows, cnt - jj * rows), g);
+            const int first = off[sb] + jj * rows, count = min(rows, cnt - jj * rows);
+            th[start[sb] + j] = make_int4(sb, first, count, g);
+            if (work != nullptr) {
+                const int64_t far = (int64_t)tok[first + count - 1] - window;
+                work[(int64_t)h * max_tiles + start[sb] + j] =
+                    far > 0 ? (float)far / (float)n * ((float)compat[sb] / (float)E) : 0.f;
+            }
         }
     }
+}
+
+// Group-pass blocks in descending order of estimated work (a counting sort
+// over kOrderBins bins), so that the longest blocks start first and the
+// grid's tail is short; slots past a head's tile count go last, and the
+// grid's padding gets `total` (those blocks exit at once).  Blocks are
+// independent, so the order changes no result.  One block of 1024 threads.
+constexpr int kOrderBins = 4096;
+constexpr int kOrderMaxBlocks = 16384;  // larger grids keep the XCD-contiguous order
+__global__ __launch_bounds__(1024) void order_kernel(const float *__restrict__ work,
+                                                     const int32_t *__restrict__ ntiles, int nhg,
+                                                     int max_tiles, int total, int grid,
+                                                     int32_t *__restrict__ order)
+{
+    __shared__ int hist[kOrderBins + 1];  // last bin: empty slots
+    __shared__ int part[1024];
+    const int tid = threadIdx.x;
+    for (int i = tid; i <= kOrderBins; i += 1024)
+        hist[i] = 0;
+    __syncthreads();
+    auto bin_of = [&](int b) {
+        const int slot = b % max_tiles;
+        const int kvh = b / max_tiles / nhg;
+        if (slot >= ntiles[kvh])
+            return kOrderBins;
+        const int q = (int)(work[(int64_t)kvh * max_tiles + slot] * (float)(kOrderBins - 1));
+        return kOrderBins - 1 - max(0, min(kOrderBins - 1, q));  // heavier first
+    };
+    for (int b = tid; b < total; b += 1024)
+        atomicAdd(&hist[bin_of(b)], 1);
+    __syncthreads();
+    // exclusive scan of the kOrderBins + 1 counts: 4 or 5 bins per thread,
+    // then the threads' sums
+    constexpr int PER = (kOrderBins + 1 + 1023) / 1024;
+    int local = 0;
+    for (int i = 0; i < PER; ++i) {
+        const int k = tid * PER + i;
+        if (k <= kOrderBins)
+            local += hist[k];
+    }
+    part[tid] = local;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int acc = part[tid] - local;
+    for (int i = 0; i < PER; ++i) {
+        const int k = tid * PER + i;
+        if (k <= kOrderBins) {
+            const int c = hist[k];
+            hist[k] = acc;
+            acc += c;
+        }
+    }
+    __syncthreads();
+    for (int b = tid; b < total; b += 1024)
+        order[atomicAdd(&hist[bin_of(b)], 1)] = b;
+    for (int b = total + tid; b < grid; b += 1024)
+        order[b] = total;
 }
 
 // ---------------------------------------------------------------------------
@@ -1418,7 +1519,9 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
 struct Layout {
     int hpb, nhg, rows_group, max_tiles;
     int64_t E, e_pad, n_pad;
-    size_t kb, vb, kp, vt, etok, egm, po, pl, tiles, ntiles, kpart, total;
+    size_t kb, vb, kp, vt, etok, egm, po, pl, tiles, ntiles, kpart, work, order, total;
+    int group_blocks;   // hkv x head groups x max_tiles
+    bool ordered;       // group blocks sorted by estimated work (small grids)
 };
 
 int heads_per_block(int ratio)
@@ -1459,6 +1562,10 @@ Layout make_layout(const AttnShape &sh)
     L.tiles = take((size_t)sh.hkv * L.max_tiles * sizeof(int4));
     L.ntiles = take((size_t)sh.hkv * sizeof(int32_t));
     L.kpart = take((size_t)sh.hkv * kNormBlocks * sizeof(float));
+    L.group_blocks = sh.hkv * L.nhg * L.max_tiles;
+    L.ordered = L.group_blocks <= kOrderMaxBlocks;
+    L.work = take(L.ordered ? (size_t)sh.hkv * L.max_tiles * sizeof(float) : 0);
+    L.order = take(L.ordered ? (size_t)(L.group_blocks + kXcds) * sizeof(int32_t) : 0);
     L.total = off;
     return L;
 }
@@ -1612,7 +1719,15 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
                 return e;
         }
         hipLaunchKernelGGL(plan_kernel, dim3(sh.hkv), dim3(256), 0, s, offsets, sh.K, sh.topk,
-                           L.rows_group, L.max_tiles, tiles, ntiles);
+                           L.rows_group, L.max_tiles, tiles, ntiles, tokens, sh.n, L.E,
+                           (int)std::min<int64_t>(sh.window, sh.n),
+                           L.ordered ? reinterpret_cast<float *>(w + L.work) : nullptr);
+        if (L.ordered)
+            hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s,
+                               reinterpret_cast<const float *>(w + L.work), ntiles, L.nhg,
+                               L.max_tiles, L.group_blocks,
+                               (L.group_blocks + kXcds - 1) / kXcds * kXcds,
+                               reinterpret_cast<int32_t *>(w + L.order));
         e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_key_norms(sh.d, bf16, k, sh.n, sh.hkv,
@@ -1645,7 +1760,8 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
         g.tiles = tiles;
         g.ntiles = ntiles;
         g.max_tiles = L.max_tiles;
-        g.total_blocks = sh.hkv * L.nhg * L.max_tiles;
+        g.total_blocks = L.group_blocks;
+        g.order = L.ordered ? reinterpret_cast<const int32_t *>(w + L.order) : nullptr;
         e = dispatch_attn<true>(sh.d, bf16, g, s);
         if (e != hipSuccess)
             return e;

@@ -36,6 +36,9 @@ struct Params {
     const uint32_t *egm;  // gmask of each bucket entry's token, [hkv][estride], 0 padded
     int64_t estride;
     const int4 *tiles;
+    // group pass: the work item of each block, heaviest first, when the grid
+    // is small enough for its tail to matter (nullptr: XCD-contiguous order)
+    const int32_t *order;
     const int32_t *ntiles;
     int max_tiles;
     int64_t E;
