@@ -108,6 +108,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ r,
     }
 }
 
+// One token per lane (K <= 8): each lane reads its token's 64-byte routing
+// vector, consecutive lanes consecutive tokens, so every byte of r is loaded
+// once and the loads coalesce; the centroids are wave-uniform scalar loads.
+// Same fixed-order scores and the same ranking as route_kernel (a scan that
+// takes a group only on a strictly larger score keeps the lower index on
+// equal scores, as the butterfly's order does).
+template <int KMAX>
+__global__ __launch_bounds__(256) void route_lane_kernel(const float *__restrict__ r,
+                                                         const float *__restrict__ centroids,
+                                                         int64_t n, int K, int topk,
+                                                         int32_t *__restrict__ groups,
+                                                         uint32_t *__restrict__ gmask);
+
 // ---------------------------------------------------------------------------
 // Fused projection + routing: r_t = W x_t, then every routing head's top-k
 // from r_t (Technical Summary, Core Architecture / Token Grouping: each
@@ -191,6 +204,7 @@ __device__ __forceinline__ float score_r(const float (&r)[16], const float *__re
 // Routing of one token for every head: selection of the k best groups,
 // scanning upward and taking a group only on a strictly larger score, so
 // equal scores go to the lower index.
+template <int KMAX = kMaxGroups>
 __device__ __forceinline__ void route_token(const float (&r)[16], int64_t t, int64_t n,
                                             const float *__restrict__ centroids, int H, int K,
                                             int topk, int32_t *__restrict__ groups,
@@ -198,9 +212,9 @@ __device__ __forceinline__ void route_token(const float (&r)[16], int64_t t, int
 {
     for (int h = 0; h < H; ++h) {
         const float *ch = centroids + (int64_t)h * K * kRouteDim;
-        float s[kMaxGroups];
+        float s[KMAX];
 #pragma unroll
-        for (int g = 0; g < kMaxGroups; ++g)
+        for (int g = 0; g < KMAX; ++g)
             s[g] = g < K ? score_r(r, ch + g * kRouteDim) : 0.f;
         uint32_t taken = 0;
         int32_t *gt = groups + ((int64_t)h * n + t) * topk;
@@ -208,7 +222,7 @@ __device__ __forceinline__ void route_token(const float (&r)[16], int64_t t, int
             int best = -1;
             float bs = 0.f;
 #pragma unroll
-            for (int g = 0; g < kMaxGroups; ++g) {
+            for (int g = 0; g < KMAX; ++g) {
                 if (g < K && !((taken >> g) & 1u) && (best < 0 || s[g] > bs)) {
                     best = g;
                     bs = s[g];
@@ -219,6 +233,31 @@ __device__ __forceinline__ void route_token(const float (&r)[16], int64_t t, int
         }
         gmask[(int64_t)h * n + t] = taken;
     }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(256) void route_lane_kernel(const float *__restrict__ r,
+                                                         const float *__restrict__ centroids,
+                                                         int64_t n, int K, int topk,
+                                                         int32_t *__restrict__ groups,
+                                                         uint32_t *__restrict__ gmask)
+{
+    const int h = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n)
+        return;
+    const float4 *rt = reinterpret_cast<const float4 *>(r + ((int64_t)h * n + t) * kRouteDim);
+    float rv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 v = rt[q];
+        rv[4 * q] = v.x;
+        rv[4 * q + 1] = v.y;
+        rv[4 * q + 2] = v.z;
+        rv[4 * q + 3] = v.w;
+    }
+    route_token<KMAX>(rv, t, n, centroids + (int64_t)h * K * kRouteDim, 1, K, topk,
+                      groups + (int64_t)h * n * topk, gmask + (int64_t)h * n);
 }
 
 // Adds one chunk of 8 elements to the sums, element by element in order.
@@ -330,6 +369,16 @@ __global__ __launch_bounds__(kProjBlock) void route_project_kernel(
 hipError_t launch_route(const float *r, const float *centroids, int H, int64_t n, int K,
                         int topk, int32_t *groups, uint32_t *gmask, hipStream_t s)
 {
+    if (K <= 8) {
+        const dim3 grid((unsigned)((n + 255) / 256), (unsigned)H);
+        if (K <= 4)
+            hipLaunchKernelGGL(route_lane_kernel<4>, grid, dim3(256), 0, s, r, centroids, n, K,
+                               topk, groups, gmask);
+        else
+            hipLaunchKernelGGL(route_lane_kernel<8>, grid, dim3(256), 0, s, r, centroids, n, K,
+                               topk, groups, gmask);
+        return hipGetLastError();
+    }
     int kp_log2 = 0;
     while ((1 << kp_log2) < K)
         ++kp_log2;
