@@ -652,17 +652,17 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         qlow = gmh[qpos] & ((1u << g) - 1u);
         // Key sub-buckets of group g: a pair belongs to a lower group exactly
         // when the two tokens' lower sets meet, so a key sub-bucket whose
-        // two lowest lower groups meet the query tile's is skipped whole.
-        // At top-k >= 4 a lower set can hold more than the two kept, and a
-        // per-key test on the group bits remains where either side keeps two.
+        // kept lower groups meet the query tile's is skipped whole.  Where a
+        // lower set can hold more groups than its code keeps, a per-key test
+        // on the group bits remains for the sub-buckets that keep all m.
         // Wave 0 walks the group's codes, 64 at a time; each lane counts the
         // keys at or before (last query position - w) of one kept code, and
         // the kept codes with keys are packed in order into LDS.
         if (wave == 0) {
-            int qa, qb;
-            decode_lower(g, sbq - group_base(g, p.topk), qa, qb);
-            const int ncode = codes_of_group(g, p.topk);
-            const int base = group_base(g, p.topk);
+            const int cm = code_members(p.K, p.topk);
+            const LowerSet qs = decode_lower(g, sbq - group_base(g, cm));
+            const int ncode = codes_of_group(g, cm);
+            const int base = group_base(g, cm);
             const int32_t *offh =
                 p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
             const int64_t lim = (int64_t)bq_max - w;
@@ -674,10 +674,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 const int c = c0 + lane;
                 int cnt = 0, lo0 = 0, owner = 0;
                 if (c < ncode) {
-                    int ka, kb;
-                    decode_lower(g, c, ka, kb);
-                    const bool meets = (ka >= 0 && (ka == qa || ka == qb)) ||
-                                       (kb >= 0 && (kb == qa || kb == qb));
+                    const LowerSet ks = decode_lower(g, c);
+                    const bool meets = lower_sets_meet(qs, ks);
                     lo0 = offh[base + c];
                     const int hi0 = offh[base + c + 1];
                     if (!meets && hi0 > lo0) {
@@ -691,7 +689,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                         }
                         cnt = lo - lo0;
                     }
-                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
+                    owner = owner_test_needed(p.topk, cm, qs, ks);
                 }
                 const uint64_t keep = __ballot(cnt > 0);
                 if (cnt > 0) {
@@ -1397,6 +1395,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
     __shared__ int start[kMaxSubbuckets + 1];
     __shared__ int compat[kMaxSubbuckets];
     const int nsb = num_subbuckets(K, topk);
+    const int cm = code_members(K, topk);
     const int h = blockIdx.x;
     const int32_t *off = offsets + (int64_t)h * (nsb + 1);
     if (threadIdx.x == 0) {
@@ -1412,18 +1411,13 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
         // entries of the key sub-buckets a query sub-bucket's blocks visit
         for (int sb = threadIdx.x; sb < nsb; sb += blockDim.x) {
             int g = 0;
-            while (g + 1 < K && group_base(g + 1, topk) <= sb)
+            while (g + 1 < K && group_base(g + 1, cm) <= sb)
                 ++g;
-            const int gb = group_base(g, topk);
-            int qa, qb;
-            decode_lower(g, sb - gb, qa, qb);
+            const int gb = group_base(g, cm);
+            const LowerSet qs = decode_lower(g, sb - gb);
             int c = 0;
-            for (int code = 0; code < codes_of_group(g, topk); ++code) {
-                int ka, kb;
-                decode_lower(g, code, ka, kb);
-                const bool meets = (ka >= 0 && (ka == qa || ka == qb)) ||
-                                   (kb >= 0 && (kb == qa || kb == qb));
-                if (!meets)
+            for (int code = 0; code < codes_of_group(g, cm); ++code) {
+                if (!lower_sets_meet(qs, decode_lower(g, code)))
                     c += off[gb + code + 1] - off[gb + code];
             }
             compat[sb] = c;
@@ -1434,7 +1428,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ o
     const int32_t *tok = tokens + (int64_t)h * E;
     int g = 0;
     for (int sb = 0; sb < nsb; ++sb) {
-        while (g + 1 < K && group_base(g + 1, topk) <= sb)
+        while (g + 1 < K && group_base(g + 1, cm) <= sb)
             ++g;
         const int nt = start[sb + 1] - start[sb];
         const int cnt = off[sb + 1] - off[sb];

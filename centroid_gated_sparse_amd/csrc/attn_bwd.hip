@@ -318,10 +318,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
         // the key sub-buckets of group g whose lower sets miss the query
         // tile's (as in the forward's group pass), packed by wave 0
         if (wave == 0) {
-            int qa, qb;
-            decode_lower(g, sbq - group_base(g, p.topk), qa, qb);
-            const int ncode = codes_of_group(g, p.topk);
-            const int gb = group_base(g, p.topk);
+            const int cm = code_members(p.K, p.topk);
+            const LowerSet qs = decode_lower(g, sbq - group_base(g, cm));
+            const int ncode = codes_of_group(g, cm);
+            const int gb = group_base(g, cm);
             const int32_t *offh =
                 p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
             const int64_t lim = (int64_t)bq_max - w;  // keys at or before lim
@@ -331,10 +331,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
                 const int c = c0 + lane;
                 int cnt = 0, lo0 = 0, owner = 0;
                 if (c < ncode) {
-                    int ka, kb;
-                    decode_lower(g, c, ka, kb);
-                    const bool meets = (ka >= 0 && (ka == qa || ka == qb)) ||
-                                       (kb >= 0 && (kb == qa || kb == qb));
+                    const LowerSet ks = decode_lower(g, c);
+                    const bool meets = lower_sets_meet(qs, ks);
                     lo0 = offh[gb + c];
                     const int hi0 = offh[gb + c + 1];
                     if (!meets && hi0 > lo0) {
@@ -348,7 +346,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
                         }
                         cnt = lo - lo0;
                     }
-                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
+                    owner = owner_test_needed(p.topk, cm, qs, ks);
                 }
                 const uint64_t keep = __ballot(cnt > 0);
                 if (cnt > 0) {
@@ -1102,10 +1100,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_wide_kernel(BwdParams 
     {
         const int bk_min = tok[row0];  // keys ascend inside the sub-bucket
         if (wave == 0) {
-            int ka, kb;
-            decode_lower(g, sbk - group_base(g, p.topk), ka, kb);
-            const int ncode = codes_of_group(g, p.topk);
-            const int gb = group_base(g, p.topk);
+            const int cm = code_members(p.K, p.topk);
+            const LowerSet ks = decode_lower(g, sbk - group_base(g, cm));
+            const int ncode = codes_of_group(g, cm);
+            const int gb = group_base(g, cm);
             const int32_t *offh =
                 p.offsets + (int64_t)kvh * (num_subbuckets(p.K, p.topk) + 1);
             const int64_t lim = (int64_t)bk_min + w;  // queries at or after lim
@@ -1115,10 +1113,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_wide_kernel(BwdParams 
                 const int c = c0 + lane;
                 int cnt = 0, first = 0, owner = 0;
                 if (c < ncode) {
-                    int qa, qb;
-                    decode_lower(g, c, qa, qb);
-                    const bool meets = (qa >= 0 && (qa == ka || qa == kb)) ||
-                                       (qb >= 0 && (qb == ka || qb == kb));
+                    const LowerSet qs = decode_lower(g, c);
+                    const bool meets = lower_sets_meet(qs, ks);
                     const int lo0 = offh[gb + c], hi0 = offh[gb + c + 1];
                     first = hi0;
                     if (!meets && hi0 > lo0) {
@@ -1133,7 +1129,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_wide_kernel(BwdParams 
                         first = lo;
                     }
                     cnt = hi0 - first;
-                    owner = p.topk >= 4 && (qb >= 0 || kb >= 0);
+                    owner = owner_test_needed(p.topk, cm, qs, ks);
                 }
                 const uint64_t keep = __ballot(cnt > 0);
                 if (cnt > 0) {
@@ -1522,7 +1518,7 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const int32_t *__restrict
     for (int sb = threadIdx.x; sb < nsb; sb += blockDim.x) {
         const int lo = off[sb], cnt = off[sb + 1] - lo;
         int g = 0;
-        while (g + 1 < K && group_base(g + 1, topk) <= sb)
+        while (g + 1 < K && group_base(g + 1, code_members(K, topk)) <= sb)
             ++g;
         for (int t = 0; t * ROWS < cnt; ++t) {
             const int slot = base[sb] + t;

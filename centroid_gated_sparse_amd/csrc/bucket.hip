@@ -4,12 +4,13 @@
 // within-group causal call (Technical Summary, Key Contributions 5) without
 // saying how tokens are gathered.  Here the n*topk (token, group) entries of
 // each routing head are counting-sorted, stably, by the sub-bucket
-// group_base(g) + lower_code(g, a, b), where a < b are the token's two lowest
-// groups below g (see common.hpp).  Inside a sub-bucket positions ascend, so
-// "causal" in bucket order is causal in positions, and a tile of one
-// sub-bucket meets a tile of another with a single owner decision: their
-// pairs belong to a lower group exactly when the two lower sets meet (at
-// top-k <= 3; above, the lower sets may hold more than the two kept).
+// group_base(g) + lower_code(g, a, b, c), where a < b (< c) are the token's
+// two (three) lowest groups below g (see common.hpp).  Inside a sub-bucket
+// positions ascend, so "causal" in bucket order is causal in positions, and a
+// tile of one sub-bucket meets a tile of another with a single owner
+// decision: their pairs belong to a lower group exactly when the two lower
+// sets meet (whenever the codes keep the whole lower set: top-k <= 3, and
+// top-k = 4 at K <= 16).
 //
 // Three kernels, all bound by HBM and integer only:
 //   count   one wavefront per chunk of tokens; LDS histogram per wave
@@ -33,46 +34,56 @@ constexpr size_t kHistLdsBytes = 64 * 1024;
 constexpr int kCachedTopk = 4;           // scatter keeps keys in registers up to here
 constexpr int kScanThreads = 1024;
 
-// Lowest and second-lowest group of token t (second = K at top-1).
-__device__ __forceinline__ int2 two_lowest(const int32_t *gt, int topk, int K)
+// Lowest three groups of token t (K where absent).
+struct Lowest3 {
+    int lo1, lo2, lo3;
+};
+__device__ __forceinline__ void take_lowest(Lowest3 &l, int g)
 {
-    int lo1 = K, lo2 = K;
-    for (int s = 0; s < topk; ++s) {
-        const int g = gt[s];
-        const int hi = max(g, lo1);
-        lo1 = min(g, lo1);
-        lo2 = min(hi, lo2);
-    }
-    return make_int2(lo1, lo2);
+    const int hi1 = max(g, l.lo1);
+    l.lo1 = min(g, l.lo1);
+    const int hi2 = max(hi1, l.lo2);
+    l.lo2 = min(hi1, l.lo2);
+    l.lo3 = min(hi2, l.lo3);
+}
+__device__ __forceinline__ Lowest3 three_lowest(const int32_t *gt, int topk, int K)
+{
+    Lowest3 l{K, K, K};
+    for (int s = 0; s < topk; ++s)
+        take_lowest(l, gt[s]);
+    return l;
 }
 
-// Sub-bucket of the token's entry in its group g, from its two lowest groups
-// lo1 < lo2: below the lowest it has no lower group, below the second only
-// lo1, and below any higher one lo1 and lo2 are the two lowest.
-__device__ __forceinline__ int subbucket(int g, int lo1, int lo2, int topk)
+// Sub-bucket of the token's entry in its group g, from its lowest groups
+// lo1 < lo2 < lo3: below lo1 it has no lower group, below lo2 only lo1,
+// below lo3 lo1 and lo2, and below any higher one lo1, lo2 and (with three
+// members kept, m = 3) lo3 are the kept members.
+__device__ __forceinline__ int subbucket(int g, const Lowest3 &l, int m)
 {
-    const int code = g == lo1 ? 0 : g == lo2 ? 1 + lo1 : 1 + g + lo2 * (lo2 - 1) / 2 + lo1;
-    return group_base(g, topk) + code;
+    const int code = g == l.lo1   ? 0
+                     : g == l.lo2 ? 1 + l.lo1
+                     : (g == l.lo3 || m < 3)
+                         ? 1 + g + choose2(l.lo2) + l.lo1
+                         : 1 + g + choose2(g) + choose3(l.lo3) + choose2(l.lo2) + l.lo1;
+    return group_base(g, m) + code;
 }
 
 // Sub-bucket keys of a token's entries, in registers (topk <= TK).  An
 // absent token (valid false) or slot s >= topk gets no key that is used.
 template <int TK>
-__device__ __forceinline__ void entry_keys(const int32_t *gt, int topk, int K, bool valid,
+__device__ __forceinline__ void entry_keys(const int32_t *gt, int topk, int K, int m, bool valid,
                                            int (&key)[TK])
 {
     int g[TK];
-    int lo1 = K, lo2 = K;
+    Lowest3 l{K, K, K};
 #pragma unroll
     for (int s = 0; s < TK; ++s) {
         g[s] = (valid && s < topk) ? gt[s] : K;  // K: no entry
-        const int hi = max(g[s], lo1);
-        lo1 = min(g[s], lo1);
-        lo2 = min(hi, lo2);
+        take_lowest(l, g[s]);
     }
 #pragma unroll
     for (int s = 0; s < TK; ++s)
-        key[s] = subbucket(g[s], lo1, lo2, topk);
+        key[s] = subbucket(g[s], l, m);
 }
 
 // counts[h][sb][chunk]; WPB wavefronts (chunks) per block
@@ -84,6 +95,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t *__rest
 {
     extern __shared__ int32_t hist[];  // [WPB][nsb]
     const int nsb = num_subbuckets(K, topk);
+    const int m = code_members(K, topk);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int h = blockIdx.y;
@@ -99,15 +111,15 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t *__rest
             const int32_t *gt = gh + t * topk;
             if constexpr (TK > 0) {
                 int key[TK];
-                entry_keys<TK>(gt, topk, K, true, key);
+                entry_keys<TK>(gt, topk, K, m, true, key);
 #pragma unroll
                 for (int s = 0; s < TK; ++s)
                     if (s < topk)
                         atomicAdd(&my[key[s]], 1);
             } else {
-                const int2 lo = two_lowest(gt, topk, K);
+                const Lowest3 lo = three_lowest(gt, topk, K);
                 for (int s = 0; s < topk; ++s)
-                    atomicAdd(&my[subbucket(gt[s], lo.x, lo.y, topk)], 1);
+                    atomicAdd(&my[subbucket(gt[s], lo, m)], 1);
             }
         }
     }
@@ -181,6 +193,7 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
 {
     extern __shared__ int32_t run[];  // [WPB][nsb] running cursor
     const int nsb = num_subbuckets(K, topk);
+    const int m = code_members(K, topk);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int h = blockIdx.y;
@@ -204,11 +217,11 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
         const bool valid = t < n;
         const int32_t *gt = gh + (valid ? t : tb) * topk;
         int key[TK > 0 ? TK : 1];
-        int2 lo = make_int2(K, K);
+        Lowest3 lo{K, K, K};
         if constexpr (TK > 0)
-            entry_keys<TK>(gt, topk, K, valid, key);
+            entry_keys<TK>(gt, topk, K, m, valid, key);
         else if (valid)
-            lo = two_lowest(gt, topk, K);
+            lo = three_lowest(gt, topk, K);
         uint32_t pending = valid ? (topk >= 32 ? ~0u : ((1u << topk) - 1u)) : 0u;
         // Each pass settles one sub-bucket key X: every lane holding an entry
         // with key X takes rank (cursor[X] + number of lower lanes holding X).
@@ -225,7 +238,7 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
                     if ((pending >> s) & 1u)
                         my_key = key[s];
             } else if (pending != 0) {
-                my_key = subbucket(gt[__ffs(pending) - 1], lo.x, lo.y, topk);
+                my_key = subbucket(gt[__ffs(pending) - 1], lo, m);
             }
             const int X = __builtin_amdgcn_readlane(my_key, leader);
             int sx = -1;
@@ -237,7 +250,7 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(
             } else {
                 for (uint32_t p = pending; p != 0; p &= p - 1) {
                     const int s = __ffs(p) - 1;
-                    if (subbucket(gt[s], lo.x, lo.y, topk) == X)
+                    if (subbucket(gt[s], lo, m) == X)
                         sx = s;
                 }
             }

@@ -12,8 +12,8 @@
 //   offsets  start at 0, never decrease, end at n*topk              (bit 1)
 //   tokens   in [0, n), strictly ascending inside each sub-bucket   (bit 2)
 //   groups   the entry's group is one of its token's gmask bits and the
-//            sub-bucket's lower-set code is the token's (its two lowest
-//            groups below the entry's group); every gmask holds exactly topk
+//            sub-bucket's lower-set code is the token's (its lowest two or
+//            three groups below the entry's group); every gmask holds exactly topk
 //            bits                                                  (bit 4)
 //   slots    slot_entry[t][s] is an entry of token t, and the groups of a
 //            token's topk entries are exactly its gmask bits          (bit 8)
@@ -48,7 +48,7 @@ __device__ __forceinline__ int find_subbucket(const int32_t *off, int nsb, int64
 __device__ __forceinline__ int group_of(int sb, int K, int topk)
 {
     int g = 0;
-    while (g + 1 < K && group_base(g + 1, topk) <= sb)
+    while (g + 1 < K && group_base(g + 1, code_members(K, topk)) <= sb)
         ++g;
     return g;
 }
@@ -94,12 +94,15 @@ __global__ __launch_bounds__(256) void check_entries_kernel(
         if (e + 1 < E && e + 1 < end && !(t < tokens[i + 1]))
             bits |= kBadTokens;
         const int g = group_of(sb, K, topk);
-        const int code = sb - group_base(g, topk);
+        const int cm = code_members(K, topk);
+        const int code = sb - group_base(g, cm);
         const uint32_t m = gmask[h * n + t];
         const uint32_t lower = m & ((1u << g) - 1u);     // the token's groups below g
         const uint32_t rest = lower & (lower - 1u);       // ... without the lowest
+        const uint32_t rest2 = rest & (rest - 1u);        // ... without the two lowest
         const int want = lower_code(g, lower ? __builtin_ctz(lower) : -1,
-                                    rest ? __builtin_ctz(rest) : -1);
+                                    rest ? __builtin_ctz(rest) : -1,
+                                    (cm >= 3 && rest2) ? __builtin_ctz(rest2) : -1);
         if (!((m >> g) & 1u) || code != want)
             bits |= kBadGroups;
     }

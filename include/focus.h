@@ -131,16 +131,19 @@ focus_status focus_route_project(const void *x, focus_dtype xdt, int64_t n, int3
  * causal call; the pages leave the gathering itself open).
  *
  * A stable counting sort of the entries of each head by sub-bucket: group g,
- * then the token's lower set inside g (its groups below g), keyed by the two
- * lowest of them as a code c:
- *     no group below g            c = 0
- *     only a below g              c = 1 + a
- *     a < b lowest below g        c = 1 + g + b (b - 1) / 2 + a
- * Group g holds codes_g = 1 (topk 1), 1 + g (topk 2) or 1 + g + g (g - 1) / 2
- * (topk >= 3) sub-buckets, and sub-bucket sb = (codes of the groups below g)
- * + c.  Inside a sub-bucket positions ascend.  Two tokens of g share a group
- * below g exactly when their lower sets meet, which the codes decide whole at
- * topk <= 3; focus_num_subbuckets(K, topk) gives the count per head.
+ * then the token's lower set inside g (its groups below g), keyed by its m
+ * lowest members as a code c, with m = topk - 1 for topk <= 3, m = 3 for
+ * topk >= 4 when K <= 16 and m = 2 for topk >= 4 when K > 16:
+ *     no group below g              c = 0
+ *     only a below g                c = 1 + a
+ *     a < b kept                    c = 1 + g + C(b, 2) + a
+ *     a < b < c3 kept (m = 3)       c = 1 + g + C(g, 2) + C(c3, 3) + C(b, 2) + a
+ * (sizes first, then colexicographic order).  Group g holds
+ * codes_g = C(g, 0) + ... + C(g, m) sub-buckets, and sub-bucket
+ * sb = (codes of the groups below g) + c.  Inside a sub-bucket positions
+ * ascend.  Two tokens of g share a group below g exactly when their lower
+ * sets meet, which the codes decide whole at topk <= 3, and at topk = 4 when
+ * K <= 16; focus_num_subbuckets(K, topk) gives the count per head.
  *
  *   groups      int32 [H, n, topk]      from focus_route
  *   offsets     int32 [H, S + 1]        out, S = focus_num_subbuckets(K, topk):

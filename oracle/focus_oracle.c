@@ -20,8 +20,8 @@
  *   attend: A(i) = { j <= i : i - j < w  or  G(i) and G(j) share a group }
  *           and the output is the exact softmax over A(i).
  *   bucket: the (token, group) entries sorted by group g, then by the
- *           token's lower set inside g (its groups below g: the two lowest
- *           of them, as a code), then by position.
+ *           token's lower set inside g (its groups below g: the lowest
+ *           two or three of them, as a code), then by position.
  *   project: r_t = W x_t, the hidden state projected into the routing space
  *           by one 16 x d_model matrix per layer (Technical Summary, Core
  *           Architecture and Token Grouping; the thelatestinai.com Tables 2
@@ -151,51 +151,72 @@ int oracle_project(const void *x, int32_t is_bf16, int64_t n, int32_t dm,
     return ORACLE_OK;
 }
 
-/* Lower-set code of token t inside group g.  The token's groups below g,
- * ascending, are a < b < ...; the code keeps the two lowest:
- *     no lower group      -> 0
- *     only a               -> 1 + a
- *     a, b (and any more)  -> 1 + g + b (b - 1) / 2 + a
- * Two tokens of group g share a group below g exactly when their full lower
- * sets meet; at top-k <= 3 a lower set has at most two groups, so the code is
- * the whole lower set. */
-static int lower_code(const int32_t *gt, int topk, int g)
+/* How many of a token's lowest groups below g its code keeps: all of them
+ * while top-k <= 3 (a lower set then has at most two), at top-k >= 4 the
+ * lowest three when K <= 16 and the lowest two above that. */
+static int kept_members(int K, int topk)
 {
-    int a = -1, b = -1; /* the lowest and second-lowest groups below g */
-    for (int s = 0; s < topk; ++s) {
-        const int x = gt[s];
-        if (x >= g)
-            continue;
-        if (a < 0 || x < a) {
-            b = a;
-            a = x;
-        } else if (b < 0 || x < b) {
-            b = x;
-        }
-    }
-    if (a < 0)
-        return 0;
-    if (b < 0)
-        return 1 + a;
-    return 1 + g + b * (b - 1) / 2 + a;
+    if (topk <= 3)
+        return topk - 1;
+    return K <= 16 ? 3 : 2;
 }
 
-/* Number of lower-set codes a token of group g can take at this top-k. */
-static int codes_of_group(int g, int topk)
+/* Binomial coefficient C(x, k) for small non-negative x, k (0 when k > x). */
+static int binom(int x, int k)
 {
-    if (topk == 1)
-        return 1;
-    if (topk == 2)
-        return 1 + g;
-    return 1 + g + g * (g - 1) / 2;
+    if (k < 0 || k > x)
+        return 0;
+    long long r = 1;
+    for (int i = 1; i <= k; ++i)
+        r = r * (x - k + i) / i;
+    return (int)r;
+}
+
+/* Lower-set code of token t inside group g.  The token's groups below g,
+ * ascending, are x_1 < x_2 < ...; the code keeps the lowest r of them
+ * (r = min(their number, kept_members)) and numbers the kept set among all
+ * subsets of {0, ..., g-1}: first by size, then in colexicographic order,
+ * i.e. by the combinatorial number system,
+ *     code = sum_{j < r} C(g, j) + sum_{i = 1..r} C(x_i, i).
+ * Two tokens of group g share a group below g exactly when their full lower
+ * sets meet; whenever a lower set has at most kept_members groups, the code
+ * is the whole lower set. */
+static int lower_code(const int32_t *gt, int topk, int g, int m)
+{
+    int low[32];
+    int r = 0;
+    for (int x = 0; x < g; ++x) { /* the groups below g, ascending */
+        int in = 0;
+        for (int s = 0; s < topk; ++s)
+            in |= gt[s] == x;
+        if (in && r < m)
+            low[r++] = x;
+    }
+    int code = 0;
+    for (int j = 0; j < r; ++j)
+        code += binom(g, j);
+    for (int i = 1; i <= r; ++i)
+        code += binom(low[i - 1], i);
+    return code;
+}
+
+/* Number of lower-set codes a token of group g can take: the subsets of
+ * {0, ..., g-1} of at most m groups. */
+static int codes_of_group(int g, int m)
+{
+    int total = 0;
+    for (int j = 0; j <= m; ++j)
+        total += binom(g, j);
+    return total;
 }
 
 /* Sub-buckets per routing head: every (group, lower-set code). */
 int oracle_num_subbuckets(int32_t K, int32_t topk)
 {
+    const int m = kept_members(K, topk);
     int total = 0;
     for (int g = 0; g < K; ++g)
-        total += codes_of_group(g, topk);
+        total += codes_of_group(g, m);
     return total;
 }
 
@@ -214,9 +235,10 @@ int oracle_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
         K < 1 || K > 32 || topk < 1 || topk > K || n * topk > INT32_MAX)
         return ORACLE_BAD_ARG;
     const int nsb = oracle_num_subbuckets(K, topk);
+    const int m = kept_members(K, topk);
     int32_t *code = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
     int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
-    char *present = (char *)malloc((size_t)codes_of_group(K - 1, topk));
+    char *present = (char *)malloc((size_t)codes_of_group(K - 1, m));
     if (!code || !slot || !present) {
         free(code);
         free(slot);
@@ -231,7 +253,7 @@ int oracle_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
         int32_t cursor = 0;
         int base = 0; /* first sub-bucket of group g */
         for (int g = 0; g < K; ++g) {
-            const int ncode = codes_of_group(g, topk);
+            const int ncode = codes_of_group(g, m);
             memset(present, 0, (size_t)ncode);
             /* membership slot and lower-set code of every token for g */
             for (int64_t t = 0; t < n; ++t) {
@@ -239,7 +261,7 @@ int oracle_bucket(const int32_t *groups, int32_t H, int64_t n, int32_t K,
                 for (int s = 0; s < topk; ++s)
                     if (gh[t * topk + s] == g)
                         slot[t] = s;
-                code[t] = slot[t] >= 0 ? lower_code(gh + t * topk, topk, g) : -1;
+                code[t] = slot[t] >= 0 ? lower_code(gh + t * topk, topk, g, m) : -1;
                 if (code[t] >= 0)
                     present[code[t]] = 1;
             }

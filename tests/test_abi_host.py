@@ -43,11 +43,15 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_sizes(L):
-    # sub-buckets: group g of K holds 1, 1 + g or 1 + g + C(g, 2) lower-set
-    # codes at top-1, top-2 and top-3 or more
+    # sub-buckets: group g of K holds 1, 1 + g, 1 + g + C(g, 2) or
+    # 1 + g + C(g, 2) + C(g, 3) lower-set codes at top-1, top-2, top-3 (and
+    # top-4 or more above K = 16), and top-4 or more up to K = 16
     assert F.focus_num_subbuckets(8, 1) == 8
     assert F.focus_num_subbuckets(8, 2) == 8 + 28
-    assert F.focus_num_subbuckets(8, 3) == F.focus_num_subbuckets(8, 6) == 8 + 28 + 56
+    assert F.focus_num_subbuckets(8, 3) == 8 + 28 + 56
+    assert F.focus_num_subbuckets(8, 4) == F.focus_num_subbuckets(8, 6) == 8 + 28 + 56 + 70
+    assert F.focus_num_subbuckets(16, 5) == 16 + 120 + 560 + 1820
+    assert F.focus_num_subbuckets(17, 4) == 17 + 136 + 680
     assert F.focus_num_subbuckets(32, 4) == 32 + 496 + 4960
     assert F.focus_num_subbuckets(0, 1) == F.focus_num_subbuckets(4, 5) == 0
     assert F.focus_num_subbuckets(33, 2) == 0

@@ -82,8 +82,11 @@ CASES = [
     W("bwd_gqa_d128_top2", 700, 4, 2, 128, 4, 2, 32, "bf16", qkv_std=1.0),
     W("bwd_mha_d64_top1", 513, 2, 2, 64, 3, 1, 16, "bf16", qkv_std=0.125),
     W("bwd_d128_top3", 600, 4, 1, 128, 6, 3, 8, "bf16", qkv_std=0.6),
-    W("bwd_d128_k8_top4_owner", 600, 4, 2, 128, 8, 4, 8, "bf16", qkv_std=0.6),
+    # top-4 at K <= 16: three-member codes settle every sub-bucket pair;
+    # top-5 (K = 12) and top-4 above K = 16 keep the per-key owner test
+    W("bwd_d128_k8_top4", 600, 4, 2, 128, 8, 4, 8, "bf16", qkv_std=0.6),
     W("bwd_d64_k12_top5_owner", 500, 2, 1, 64, 12, 5, 16, "bf16", qkv_std=0.7),
+    W("bwd_d128_k20_top4_owner", 700, 4, 2, 128, 20, 4, 16, "bf16", qkv_std=0.6),
     W("bwd_d64_w0", 400, 2, 1, 64, 4, 2, 0, "bf16", qkv_std=1.0),
     W("bwd_d128_w_ge_n", 300, 2, 1, 128, 4, 2, 300, "bf16", qkv_std=0.5),
     W("bwd_d128_K1", 333, 2, 2, 128, 1, 1, 8, "bf16", qkv_std=0.5),
@@ -92,8 +95,7 @@ CASES = [
     # 2 top-k > K: every pair shares a group, all of them in the window pass
     W("bwd_d128_k4_top3_allpairs", 500, 4, 2, 128, 4, 3, 24, "bf16", qkv_std=0.6),
     # K = 16 and 32 (thelatestinai.com Table 9): lower-set sub-buckets, up to
-    # 5488 per head at K = 32, top-3; at top-3 the code decides every pair, at
-    # top-4 and more the per-key owner test runs in both passes
+    # 5488 per head at K = 32, top-3; at top-3 the code decides every pair
     W("bwd_gqa_d128_k16_top3", 900, 4, 2, 128, 16, 3, 16, "bf16", qkv_std=0.5),
     W("bwd_gqa_d128_k32_top2", 1200, 4, 1, 128, 32, 2, 32, "bf16", qkv_std=0.5),
     W("bwd_mha_d64_k32_top3", 800, 2, 2, 64, 32, 3, 8, "bf16", qkv_std=0.7),

@@ -85,6 +85,8 @@ CASES = [
     Workload("check_k4_top1", 900, 2, 2, 128, 4, 1, 16, "bf16", qkv_std=0.09),
     Workload("check_k16_top3", 1100, 4, 2, 64, 16, 3, 8, "bf16", qkv_std=0.125),
     Workload("check_k8_top4", 1000, 2, 2, 64, 8, 4, 16, "bf16", qkv_std=0.125),
+    Workload("check_k16_top5", 900, 2, 2, 64, 16, 5, 16, "bf16", qkv_std=0.125),
+    Workload("check_k20_top4", 900, 2, 2, 64, 20, 4, 16, "bf16", qkv_std=0.125),
 ]
 
 

@@ -107,9 +107,11 @@ def test_route_forced_ties(K, topk):
 
 
 # Bucketing alone on random distinct group ids: the chunk length follows H and
-# n (64 to 512 tokens), and the keys sit in registers up to top-4.
+# n (64 to 512 tokens), and the keys sit in registers up to top-4.  Top-4
+# and more up to K = 16 take three-member lower-set codes, above K = 16 two.
 @pytest.mark.parametrize("H,n,K,topk", [(8, 300001, 8, 3), (2, 5000, 6, 5), (16, 1_000_003, 4, 1),
-                                        (3, 65, 32, 17)])
+                                        (3, 65, 32, 17), (4, 200001, 16, 4), (2, 50000, 16, 7),
+                                        (2, 40000, 20, 4)])
 def test_bucket_chunk_lengths_bitexact(H, n, K, topk):
     log(f"bucket H={H} n={n} K={K} top{topk}")
     rng = np.random.default_rng(n + 7 * K + topk)
@@ -149,11 +151,15 @@ SMALL = [
     W("bf16_d128_gqa4_skew", 1300, 8, 2, 128, 4, 2, 100, "bf16", z_probs=(0.4, 0.3, 0.2, 0.1)),
     W("bf16_d128_gqa4_k8", 2000, 8, 2, 128, 8, 2, 64, "bf16"),
     W("bf16_d128_top3", 900, 4, 1, 128, 8, 3, 32, "bf16"),
-    # top-4 and more: sub-bucket pairs whose two lowest lower-set groups are
-    # disjoint run with the per-key owner test
-    W("bf16_d128_k8_top4_owner", 900, 4, 2, 128, 8, 4, 24, "bf16"),
+    # top-4 up to K = 16: three-member codes hold the whole lower set, and
+    # every sub-bucket pair is settled whole (the last group of K = 16 has
+    # 576 codes); top-5 at K = 16 and top-4 at K = 20 keep the per-key owner
+    # test for the sub-buckets whose codes are full
+    W("bf16_d128_k8_top4", 900, 4, 2, 128, 8, 4, 24, "bf16"),
+    W("bf16_d128_k16_top4", 1500, 4, 2, 128, 16, 4, 32, "bf16", z_probs=SKEW16),
     W("bf16_d128_k16_top5_owner", 1200, 4, 2, 128, 16, 5, 32, "bf16", z_probs=SKEW16),
-    W("f32_d64_k10_top4_owner", 400, 2, 1, 64, 10, 4, 16, "f32"),
+    W("bf16_d128_k20_top4_owner", 1200, 4, 2, 128, 20, 4, 32, "bf16"),
+    W("f32_d64_k10_top4", 400, 2, 1, 64, 10, 4, 16, "f32"),
     W("bf16_d64_w0", 800, 2, 2, 64, 4, 2, 0, "bf16"),
     W("bf16_d64_w_ge_n", 600, 2, 1, 64, 4, 2, 600, "bf16"),
     W("bf16_d128_K1", 700, 4, 4, 128, 1, 1, 16, "bf16"),

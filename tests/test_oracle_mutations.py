@@ -25,8 +25,10 @@ MUTATIONS = {
     "lse_without_max": ("lse[r] = mx + log(l);", "lse[r] = log(l);"),
     "not_causal_self": ("for (int64_t j = 0; j <= i; ++j) {\n                int in_window",
                         "for (int64_t j = 0; j < i; ++j) {\n                int in_window"),
-    "lower_set_highest": ("if (a < 0 || x < a) {", "if (a < 0 || x > a) {"),
-    "lower_code_swapped": ("return 1 + g + b * (b - 1) / 2 + a;", "return 1 + g + a * (a - 1) / 2 + b;"),
+    "lower_set_highest": ("for (int x = 0; x < g; ++x) {", "for (int x = g - 1; x >= 0; --x) {"),
+    "lower_code_swapped": ("code += binom(low[i - 1], i);", "code += binom(low[r - i], i);"),
+    "kept_two_at_top4": ("return K <= 16 ? 3 : 2;", "return 2;"),
+    "code_sizes_dropped": ("code += binom(g, j);", "code += 0 * binom(g, j);"),
     "count_far_edge": ("int64_t far_end = i - w;", "int64_t far_end = i - w + 1;"),
     "value_index": ("acc[e] += p * widen(v, is_bf16, vb + e);",
                     "acc[e] += p * widen(v, is_bf16, kb_unused(vb) + e);"),

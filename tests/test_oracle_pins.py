@@ -132,30 +132,38 @@ def test_route_recovers_cluster_labels():
 # ----------------------------------------------------------------------------
 # bucketing: properties that together determine the output uniquely
 
-def _low2(gt, g):
-    """The token's groups below g, ascending, at most the two lowest: what a
-    sub-bucket of group g holds in common (all of the lower set at top-k <= 3)."""
-    return tuple(sorted(x for x in gt if x < g)[:2])
+def _kept(K, topk):
+    """How many of the lowest groups below g a sub-bucket's key keeps: the
+    whole lower set at top-k <= 3, three at top-k >= 4 with K <= 16, else two."""
+    return topk - 1 if topk <= 3 else (3 if K <= 16 else 2)
+
+
+def _low(gt, g, m):
+    """The token's groups below g, ascending, at most the m lowest: what a
+    sub-bucket of group g holds in common."""
+    return tuple(sorted(x for x in gt if x < g)[:m])
 
 
 @pytest.mark.parametrize("K,topk,n", [(4, 1, 300), (4, 2, 500), (8, 3, 257), (5, 5, 64),
-                                      (1, 1, 33), (8, 4, 400), (6, 3, 300), (3, 2, 40)])
+                                      (1, 1, 33), (8, 4, 400), (6, 3, 300), (3, 2, 40),
+                                      (16, 6, 200), (20, 4, 200)])
 def test_bucket_properties(K, topk, n):
     """The bucketing, pinned by properties that fix it uniquely: every group's
     run of sub-buckets holds exactly the tokens of that group (brute force),
-    two tokens share a sub-bucket exactly when their two lowest groups below g
-    agree, sub-buckets follow one another by lower-set size, then by its
-    higher and lower member, positions ascend inside each, every token
-    appears topk times, slot_entry inverts tokens, and the number of
-    sub-buckets of group g is the number of lower sets it can hold,
-    C(g, 0) + C(g, 1) + C(g, 2) capped at topk - 1 members."""
+    two tokens share a sub-bucket exactly when their m lowest groups below g
+    agree, sub-buckets follow one another by the size of that set, then
+    colexicographically (highest member first), positions ascend inside each,
+    every token appears topk times, slot_entry inverts tokens, and the number
+    of sub-buckets of group g is the number of sets it can hold,
+    C(g, 0) + ... + C(g, m)."""
     rng = np.random.default_rng(K * 100 + topk)
     H = 3
     r = rng.standard_normal((H, n, 16)).astype(np.float32)
     c = rng.standard_normal((H, K, 16)).astype(np.float32)
     groups, _ = oracle.route(r, c, topk)
     offsets, tokens, slot_entry = oracle.bucket(groups, K)
-    per_group = [sum(math.comb(g, s) for s in range(min(2, topk - 1) + 1)) for g in range(K)]
+    m = _kept(K, topk)
+    per_group = [sum(math.comb(g, s) for s in range(m + 1)) for g in range(K)]
     nsb = sum(per_group)
     assert oracle.num_subbuckets(K, topk) == nsb == offsets.shape[1] - 1
     first = np.concatenate([[0], np.cumsum(per_group)])
@@ -175,14 +183,14 @@ def test_bucket_properties(K, topk, n):
                 assert (np.diff(toks) > 0).all()          # ascending positions
                 if toks.size == 0:
                     continue
-                keys = {_low2(groups[h, t].tolist(), g) for t in toks}
+                keys = {_low(groups[h, t].tolist(), g, m) for t in toks}
                 assert len(keys) == 1                     # one lower set per sub-bucket
                 key = keys.pop()
                 assert key not in [k for k, _ in order]   # and one sub-bucket per lower set
                 order.append((key, sb))
                 for t in toks:
                     where[(int(t), g)] = sb
-            ranks = [(len(k), k[-1] if k else -1, k[0] if k else -1) for k, _ in order]
+            ranks = [(len(k), tuple(reversed(k))) for k, _ in order]
             assert ranks == sorted(ranks)
             for _, sb in order:
                 seen[tokens[h, off[sb]:off[sb + 1]]] += 1
