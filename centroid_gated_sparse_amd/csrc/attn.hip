@@ -825,6 +825,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             const int fhi = qpos - p.gate_w - kpos[0];
             if (__builtin_amdgcn_ballot_w64(fhi >= 0) != 0) {
                 const bool all_far = __builtin_amdgcn_ballot_w64(!(fhi >= kKeyTile - 1)) == 0;
+                // register r of lane half h holds key index kb*32 + 16h + r:
+                // compare the constant kb*32 + r with the bound shifted by
+                // 16h (a per-register index would hold 32 registers)
+                const int fhi_h = fhi - 16 * h;
                 const char *al = stage(I).a;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
@@ -843,8 +847,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                     for (int r = 0; r < 16; ++r) {
                         const float gate = __builtin_amdgcn_rcpf(
                             1.f + __builtin_amdgcn_exp2f(-p.lam2 * a[r]));
-                        const int kk = kb * 32 + 16 * h + r;
-                        s[kb][r] *= (all_far || kk <= fhi) ? gate : 1.f;
+                        s[kb][r] *= (all_far || kb * 32 + r <= fhi_h) ? gate : 1.f;
                     }
                 }
             }
