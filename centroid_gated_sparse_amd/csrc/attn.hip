@@ -987,18 +987,22 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // in each wavefront), read when the tile is computed; stage indices
         // are compile-time, so the ring stays in scalar registers
         int ring_valid[NSTAGE] = {}, ring_owner[NSTAGE] = {};
-        auto issue = [&](auto I) {
+        // (is_a: this wavefront's role, a compile-time constant inside the
+        // role loops, so that role B's copies carry no load code or branches;
+        // the gated pass keeps the run-time test, with which its registers
+        // fit the loop without reloads)
+        auto issue = [&](auto I, bool is_a) {
             int nv, no;
             const int64_t origin = tile_origin(nv, no);
-            if (role_a_wave)
+            if (is_a)
                 TL::prefetch(st, p, kvh, origin, stage(I).k, stage(I).v);
             int *kp = stage(I).key;
             if (GROUP) {
-                if (key_wave) {
+                if (is_a && key_wave) {
                     dma4(etk + origin, (uint32_t)lane * 4u, lds_address(kp));
                     dma4(egh + origin, (uint32_t)lane * 4u, lds_address(kp) + kKeyTile * 4);
                 }
-            } else if (threadIdx.x < kKeyTile) {
+            } else if ((GATED || is_a) && threadIdx.x < kKeyTile) {
                 kp[threadIdx.x] = (int)(origin + threadIdx.x);
             }
             if constexpr (GATED) {
@@ -1024,14 +1028,14 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // lgkmcnt 11:8; 0x70 | n = "vmcnt(n) lgkmcnt(0)", expcnt untouched.
         // The builtin, unlike inline asm, is visible to the compiler's own
         // wait tracking, so it adds no waits of its own for these loads.)
-        auto close_interval = [&](bool newest_in_flight) {
+        auto close_interval = [&](bool newest_in_flight, bool is_a) {
             if (!newest_in_flight)
                 __builtin_amdgcn_s_waitcnt(0x70);
-            else if (key_wave)
+            else if (is_a && key_wave)
                 __builtin_amdgcn_s_waitcnt(0x70 | (DMA_KV + 2));
             else if (a_wave)
                 __builtin_amdgcn_s_waitcnt(0x70 | (DMA_KV + DMA_A));
-            else if (role_a_wave)
+            else if (is_a)
                 __builtin_amdgcn_s_waitcnt(0x70 | DMA_KV);
             else
                 __builtin_amdgcn_s_waitcnt(0x70);
@@ -1043,10 +1047,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
 
         // prologue: tiles 0 and 1 (tile 0's iterator position is current)
         if (T > 0)
-            issue(I0{});
+            issue(I0{}, role_a_wave);
         if (T > 1) {
             ++it_tile;
-            issue(I1{});
+            issue(I1{}, role_a_wave);
         }
         __builtin_amdgcn_s_waitcnt(0x70);
         __syncthreads();
@@ -1065,7 +1069,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 auto issue_ahead = [&] {
                     if (ahead) {
                         ++it_tile;
-                        issue(AHEAD);
+                        issue(AHEAD, GATED ? role_a_wave : ROLE_A);
                     }
                 };
                 TL::refresh(lo);
@@ -1090,7 +1094,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                                ring_owner[decltype(CUR)::value]);
                     }
                 }
-                close_interval(ahead);
+                close_interval(ahead, GATED ? role_a_wave : ROLE_A);
             };
             // interval 0 (role B has no previous tile to finish) is peeled
             // off, so that every interval of the unrolled loop has one shape
