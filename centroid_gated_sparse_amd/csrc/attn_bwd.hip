@@ -47,6 +47,7 @@
 // Q^T and dO^T) with the LDS transpose read ds_read_b64_tr_b16 from the same
 // row-major tile.
 #include <algorithm>
+#include <cstddef>
 
 #include "attn_common.hpp"
 
@@ -181,6 +182,16 @@ struct TileDma {
 
 // "s_waitcnt vmcnt(n) lgkmcnt(0)" for a wave-uniform n in 0..47 (larger n
 // waits for 47, which is only more conservative)
+// LDS byte address of the member at byte offset `off` of stage S of a
+// __shared__ stage ring, from the ring's own address: indexing the ring
+// with a run-time S and converting the member's generic pointer back would
+// cost a shared-aperture add and a null test per address.
+template <class StageT, int N>
+__device__ __forceinline__ uint32_t stage_lds(StageT (&ring)[N], int S, size_t off)
+{
+    return lds_address(ring) + (uint32_t)S * (uint32_t)sizeof(StageT) + (uint32_t)off;
+}
+
 __device__ __forceinline__ void wait_vm_n(int n)
 {
 #define FOCUS_WAIT_CASE(k) \
@@ -419,14 +430,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
         int origin, valid, owner;
         it_next(it_issue, origin, valid, owner);
         const int64_t r0 = (int64_t)kvh * rows + origin;
-        dma.issue(p.k + r0 * D, valid, lds_address(stg[S].k), wave);
-        dma.issue(p.v + r0 * D, valid, lds_address(stg[S].v), wave);
+        dma.issue(p.k + r0 * D, valid, stage_lds(stg, S, offsetof(Stage, k)), wave);
+        dma.issue(p.v + r0 * D, valid, stage_lds(stg, S, offsetof(Stage, v)), wave);
         if (GROUP) {
             const uint32_t lo = (uint32_t)std::min(lane, valid - 1) * 4u;
             if (wave == 0)
-                dma4(tok + origin, lo, lds_address(stg[S].pos));
+                dma4(tok + origin, lo, stage_lds(stg, S, offsetof(Stage, pos)));
             else if (wave == 1)
-                dma4(egm + origin, lo, lds_address(stg[S].gm));
+                dma4(egm + origin, lo, stage_lds(stg, S, offsetof(Stage, gm)));
         }
     };
 
@@ -579,7 +590,16 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p)
         if (u + AHEAD < T)
             issue(S == 0 ? kDqStages - 1 : S - 1);
         if (u + 1 < T) {
-            wait_vm_n((std::min(T - 1, u + AHEAD) - u - 1) * per_tile);
+            // AHEAD - 1 tiles may fly on in the steady state (an immediate
+            // count), fewer at the ring's tail
+            if (u + AHEAD < T) {
+                if (extra)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((AHEAD - 1) * (DMA_KV + 1)));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((AHEAD - 1) * DMA_KV));
+            } else {
+                wait_vm_n((T - 2 - u) * per_tile);
+            }
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
@@ -743,13 +763,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_window_kernel(BwdParam
         int head, origin, valid;
         it_next(it_issue, head, origin, valid);
         const int64_t r0 = (int64_t)head * rows + origin;
-        dma.issue(p.q + r0 * D, valid, lds_address(stg[S].q), wave);
-        dma.issue(p.dout + r0 * D, valid, lds_address(stg[S].d), wave);
+        dma.issue(p.q + r0 * D, valid, stage_lds(stg, S, offsetof(Stage, q)), wave);
+        dma.issue(p.dout + r0 * D, valid, stage_lds(stg, S, offsetof(Stage, d)), wave);
         const uint32_t lo = (uint32_t)std::min(lane, valid - 1) * 4u;
         if (wave == 1)
-            dma4(p.l2 + r0, lo, lds_address(stg[S].l2));
+            dma4(p.l2 + r0, lo, stage_lds(stg, S, offsetof(Stage, l2)));
         else if (wave == 2)
-            dma4(p.drow + r0, lo, lds_address(stg[S].dd));
+            dma4(p.drow + r0, lo, stage_lds(stg, S, offsetof(Stage, dd)));
     };
 
     f32x16 dk_acc[DB], dv_acc[DB];
@@ -909,7 +929,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_window_kernel(BwdParam
         if (u + AHEAD < T)
             issue(S == 0 ? kDkvStages - 1 : S - 1);
         if (u + 1 < T) {
-            wait_vm_n((std::min(T - 1, u + AHEAD) - u - 1) * per_tile);
+            if (u + AHEAD < T) {
+                if (extra)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((AHEAD - 1) * (DMA_QD + 1)));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((AHEAD - 1) * DMA_QD));
+            } else {
+                wait_vm_n((T - 2 - u) * per_tile);
+            }
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
@@ -1203,17 +1230,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_wide_kernel(BwdParams 
         int head, origin, valid, owner;
         it_next(it_issue, head, origin, valid, owner);
         const int64_t r0 = (int64_t)head * rows + origin;
-        dma.issue(p.q + r0 * D, valid, lds_address(stg[S].q), wave);
-        dma.issue(p.dout + r0 * D, valid, lds_address(stg[S].d), wave);
+        dma.issue(p.q + r0 * D, valid, stage_lds(stg, S, offsetof(Stage, q)), wave);
+        dma.issue(p.dout + r0 * D, valid, stage_lds(stg, S, offsetof(Stage, d)), wave);
         const uint32_t lo = (uint32_t)std::min(lane, valid - 1) * 4u;
         if (wave == 0)
-            dma4(tok + origin, lo, lds_address(stg[S].pos));
+            dma4(tok + origin, lo, stage_lds(stg, S, offsetof(Stage, pos)));
         else if (wave == 1)
-            dma4(p.l2 + r0, lo, lds_address(stg[S].l2));
+            dma4(p.l2 + r0, lo, stage_lds(stg, S, offsetof(Stage, l2)));
         else if (wave == 2)
-            dma4(p.drow + r0, lo, lds_address(stg[S].dd));
+            dma4(p.drow + r0, lo, stage_lds(stg, S, offsetof(Stage, dd)));
         else
-            dma4(egm + origin, lo, lds_address(stg[S].gm));
+            dma4(egm + origin, lo, stage_lds(stg, S, offsetof(Stage, gm)));
     };
 
     // dK^T and dV^T of both key blocks, in AGPRs, cleared by zero products
@@ -1419,7 +1446,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_wide_kernel(BwdParams 
         if (u + AHEAD < T)
             issue(S == 0 ? kDkvStages - 1 : S - 1);
         if (u + 1 < T) {
-            wait_vm_n((std::min(T - 1, u + AHEAD) - u - 1) * per_tile);
+            if (u + AHEAD < T)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((AHEAD - 1) * per_tile));
+            else
+                wait_vm_n((T - 2 - u) * per_tile);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
