@@ -180,8 +180,6 @@ struct TileDma {
     }
 };
 
-// "s_waitcnt vmcnt(n) lgkmcnt(0)" for a wave-uniform n in 0..47 (larger n
-// waits for 47, which is only more conservative)
 // LDS byte address of the member at byte offset `off` of stage S of a
 // __shared__ stage ring, from the ring's own address: indexing the ring
 // with a run-time S and converting the member's generic pointer back would
@@ -192,6 +190,8 @@ __device__ __forceinline__ uint32_t stage_lds(StageT (&ring)[N], int S, size_t o
     return lds_address(ring) + (uint32_t)S * (uint32_t)sizeof(StageT) + (uint32_t)off;
 }
 
+// "s_waitcnt vmcnt(n) lgkmcnt(0)" for a wave-uniform n in 0..47 (larger n
+// waits for 47, which is only more conservative)
 __device__ __forceinline__ void wait_vm_n(int n)
 {
 #define FOCUS_WAIT_CASE(k) \
