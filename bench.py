@@ -64,25 +64,43 @@ def window_pairs(n: int, w: int) -> int:
     return w * (w + 1) // 2 + (n - w) * w
 
 
+def _far_pairs_by_subsets(g: np.ndarray, w: int) -> int:
+    """Pairs (i, j), j <= i - w, whose group sets meet, for one routing head
+    (g: [n, topk] distinct groups per token), by inclusion-exclusion over the
+    shared subsets: sum over nonempty T of (-1)^(|T|+1) times the pairs
+    whose sets both contain T.  Memory is O(n * 2^topk), whatever K is."""
+    from itertools import combinations
+
+    n, topk = g.shape
+    pos = np.arange(n, dtype=np.int64)
+    one = np.int64(1)
+    assert n < (1 << 31)
+    total = 0
+    for size in range(1, topk + 1):
+        masks = np.concatenate([
+            np.bitwise_or.reduce(one << g[:, list(c)].astype(np.int64), axis=1)
+            for c in combinations(range(topk), size)])
+        # (subset, position) keys, sorted: masks < 2^32 and positions < 2^31
+        keys = np.sort((masks << np.int64(31)) + np.tile(pos, masks.size // n))
+        # first entry of each key's subset, and the entries of that subset at
+        # positions <= position - w (a query below the subset's first entry
+        # counts nothing)
+        idx = np.arange(keys.size, dtype=np.int64)
+        new_subset = np.ones(keys.size, bool)
+        new_subset[1:] = (keys[1:] >> 31) != (keys[:-1] >> 31)
+        start = np.maximum.accumulate(np.where(new_subset, idx, 0))
+        cnt = np.searchsorted(keys, keys - w, side="right") - start
+        total += (1 if size % 2 else -1) * int(np.clip(cnt, 0, None).sum())
+    return total
+
+
 def surviving_pairs(groups: np.ndarray, K: int, w: int) -> np.ndarray:
     """|A(i)| summed over rows, per routing head (host-side count from the GPU
     routing: window keys plus earlier keys j <= i - w sharing a group)."""
     H, n, topk = groups.shape
-    bits = np.zeros((H, n), np.int64)
-    for s in range(topk):
-        bits |= np.int64(1) << groups[..., s].astype(np.int64)
     out = np.zeros(H, np.int64)
     for h in range(H):
-        classes, cls = np.unique(bits[h], return_inverse=True)
-        onehot_prefix = np.zeros((n + 1, classes.size), np.int64)
-        np.add.at(onehot_prefix, (np.arange(1, n + 1), cls), 1)
-        np.cumsum(onehot_prefix, axis=0, out=onehot_prefix)
-        meets = (classes[None, :] & classes[:, None]) != 0        # [class_i, class_j]
-        far_end = np.arange(n) - w + 1                            # keys 0 .. i-w
-        far_end = np.clip(far_end, 0, None)
-        prefix_at = onehot_prefix[far_end]                        # [n, classes]
-        far = (prefix_at * meets[cls]).sum(axis=1)
-        out[h] = far.sum() + window_pairs(n, w)
+        out[h] = _far_pairs_by_subsets(groups[h], w) + window_pairs(n, w)
     return out
 
 
@@ -188,13 +206,15 @@ def timed_ms(fn, warmup: int, steps: int) -> float:
     for _ in range(warmup):
         fn()
     ts = []
-    for _ in range(steps):
+    for i in range(steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
+        if ts[-1] > 5000.0:  # long steps report as they finish
+            log(f"timed step {i + 1}/{steps}: {ts[-1]:.0f} ms")
     return float(np.median(ts))
 
 
