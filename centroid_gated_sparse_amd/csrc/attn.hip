@@ -607,12 +607,13 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
 
     typename TL::QFrag qf;
     TL::load_q(qf, static_cast<const T *>(p.q), ((int64_t)hq * p.n + qpos) * D, h);
-    // gated pass: this lane's query's assignment as the B operand of the
-    // affinity product (groups 16j + 8h .. 16j + 8h + 7 for k-step j)
+    // gated pass: this lane's query's assignment, scaled by -lambda log2(e)
+    // (the second copy of the packed rows), as the B operand of the affinity
+    // product (groups 16j + 8h .. 16j + 8h + 7 for k-step j)
     bf16x8 aq[GATED ? GA / 16 : 1];
     if constexpr (GATED) {
-        const bf16x8 *arow =
-            static_cast<const bf16x8 *>(p.apack) + ((int64_t)kvh * p.krows + qpos) * GCH;
+        const bf16x8 *arow = static_cast<const bf16x8 *>(p.apack) +
+                             ((int64_t)(p.hkv + kvh) * p.krows + qpos) * GCH;
 #pragma unroll
         for (int j = 0; j < GA / 16; ++j)
             aq[j] = arow[2 * j + h];
@@ -845,8 +846,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                             aq[j], a, 0, 0, 0);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float gate = __builtin_amdgcn_rcpf(
-                            1.f + __builtin_amdgcn_exp2f(-p.lam2 * a[r]));
+                        const float gate =
+                            __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a[r]));
                         s[kb][r] *= (all_far || kb * 32 + r <= fhi_h) ? gate : 1.f;
                     }
                 }
@@ -1782,11 +1783,15 @@ hipError_t launch_attn(const AttnShape &sh, const void *q, const void *k, const 
 }
 
 namespace {
-// The assignment rounded to bf16, padded to ga groups (16 or 32) and to
-// n_pad zero rows per head: [hkv][n_pad][ga].
+// The assignment padded to ga groups (16 or 32) and to n_pad zero rows per
+// head, twice: [2][hkv][n_pad][ga] bf16.  The first copy holds A itself (the
+// keys' side of the affinity product), the second -lambda log2(e) A (the
+// queries' side), each rounded to bf16 once, so that the product lands
+// directly in the exponent of the gate's 2^(-lambda log2(e) a).
 __global__ __launch_bounds__(256) void gate_pack_kernel(const float *__restrict__ assign,
                                                         int64_t n, int64_t n_pad, int K, int ga,
-                                                        int64_t total, __bf16 *__restrict__ apack)
+                                                        int64_t total, float neg_lam2,
+                                                        __bf16 *__restrict__ apack)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total)
@@ -1794,7 +1799,9 @@ __global__ __launch_bounds__(256) void gate_pack_kernel(const float *__restrict_
     const int g = (int)(idx % ga);
     const int64_t ht = idx / ga;
     const int64_t h = ht / n_pad, t = ht % n_pad;
-    apack[idx] = (__bf16)((t < n && g < K) ? assign[(h * n + t) * K + g] : 0.f);
+    const float x = (t < n && g < K) ? assign[(h * n + t) * K + g] : 0.f;
+    apack[idx] = (__bf16)x;
+    apack[total + idx] = (__bf16)(neg_lam2 * x);
 }
 }  // namespace
 
@@ -1802,7 +1809,7 @@ size_t gated_dense_workspace_bytes(const AttnShape &sh)
 {
     const int64_t n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
     return dense_workspace_bytes(sh) +
-           align_up((size_t)sh.hkv * n_pad * kGateGroups * 2, 256);
+           align_up((size_t)2 * sh.hkv * n_pad * kGateGroups * 2, 256);
 }
 
 namespace {
@@ -1837,7 +1844,7 @@ hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k,
     const int ga = sh.K > 16 ? 32 : 16;
     const int64_t total = (int64_t)sh.hkv * n_pad * ga;
     hipLaunchKernelGGL(gate_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       assign, sh.n, n_pad, sh.K, ga, total, apack);
+                       assign, sh.n, n_pad, sh.K, ga, total, -lambda * kLog2e, apack);
     e = hipGetLastError();
     float *kpart = dense_kpart(ws, gated_dense_workspace_bytes(sh), sh.hkv);
     if (e == hipSuccess)
@@ -1857,7 +1864,6 @@ hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k,
     p.total_blocks = sh.hkv * L.nhg * p.row_tiles;
     p.apack = apack;
     p.gate_w = (int)std::min<int64_t>(sh.window, sh.n);
-    p.lam2 = lambda * kLog2e;
     p.kpart = kpart;
     if (ga == 16)
         return sh.d == 64 ? launch_attn_kernel<64, true, false, 16>(p, s)

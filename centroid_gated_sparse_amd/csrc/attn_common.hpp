@@ -52,11 +52,10 @@ struct Params {
     int row_tiles;
     int total_blocks;
     // gated dense pass (training mode): bf16 assignment rows padded to 16
-    // or 32 groups, [hkv][krows][16 or 32]; far pairs (i - j >= gate_w)
-    // multiply their score by sigmoid(lambda a_ij)
+    // or 32 groups, [2][hkv][krows][16 or 32] (A, then -lambda log2(e) A);
+    // far pairs (i - j >= gate_w) multiply their score by sigmoid(lambda a_ij)
     const void *apack;
     int gate_w;
-    float lam2;  // lambda * log2(e)
     // per key/value head, kNormBlocks partial maxima of the keys' Euclidean
     // norms (their largest bounds every key of the head)
     const float *kpart;

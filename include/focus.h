@@ -351,13 +351,15 @@ focus_status focus_sinkhorn(const float *r, const float *centroids, int32_t H, i
  * a_ij = sum_g assign[i][g] assign[j][g] (the key/value head's assignment);
  * exact softmax over all j <= i.
  *   q          bf16 [Hq, n, d];  k, v  bf16 [Hkv, n, d]
- *   assign     fp32 [Hkv, n, K]  from focus_sinkhorn (rounded to bf16 for
- *                                the affinity product, a bf16 MFMA)
+ *   assign     fp32 [Hkv, n, K]  from focus_sinkhorn (the keys' rows
+ *                                rounded to bf16, the queries' rows scaled by
+ *                                -lambda log2(e) and then rounded, for the
+ *                                affinity product, a bf16 MFMA)
  *   lambda     any finite value; window w >= 0; scale > 0
  *   out        bf16 [Hq, n, d];  lse  fp32 [Hq, n] (natural log)
  *   workspace  >= focus_gated_attn_workspace_bytes(Hkv, n, d, K) bytes:
- *              padded copies of K and V^T and the assignment rounded to
- *              bf16, padded to 32 groups
+ *              padded copies of K and V^T and two bf16 copies of the
+ *              assignment (plain and scaled), padded to 32 groups
  * Errors: INVALID_ARGUMENT as focus_attn_fwd (and a non-finite lambda);
  * UNSUPPORTED for dt other than FOCUS_BF16, d not in {64, 128}, K > 32;
  * WORKSPACE if short.

@@ -5,10 +5,11 @@ Bars:
   * Sinkhorn assignment: max |A_gpu - A_oracle| <= 2e-5 (fp32 on the GPU,
     double in the oracle; entries lie in [0, 1]).
   * gated attention: O max-abs <= 2e-2 (bf16 output), LSE <= 5e-3.  The
-    affinity a_ij is formed from the assignment rounded to bf16 (2^-9
-    relative), so the gate moves by at most |lambda| / 4 * 2^-8 and a logit
-    of size |x| by that fraction of |x|; at the inputs here that bounds the
-    LSE change well below 5e-3.
+    affinity's exponent -lambda log2(e) a_ij is formed from the keys'
+    assignment rows rounded to bf16 and the queries' rows scaled by
+    -lambda log2(e) and then rounded (2^-9 relative each), so the gate moves
+    by at most |lambda| / 4 * 2^-8 and a logit of size |x| by that fraction
+    of |x|; at the inputs here that bounds the LSE change well below 5e-3.
 The oracle uses its own Sinkhorn assignment; the GPU chain uses its own.
 """
 import numpy as np
