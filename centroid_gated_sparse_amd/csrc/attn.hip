@@ -475,12 +475,14 @@ struct Acc {
 // ---------------------------------------------------------------------------
 // the attention kernel: GROUP selects the gathered within-group pass
 
-// GA != 0 (bf16 dense window pass only): the training-mode gate of the far
-// pairs (Technical Summary, Gated Attention: s_ij = q_i.k_j *
-// sigmoid(lambda a_ij)).  Each stage also holds the tile's keys' assignment
-// rows (bf16, GA = 16 or 32 groups wide, LDS-DMA'd by wavefront 0); the
-// affinity tile a^T = A_k A_q^T is GA / 16 more MFMAs per 32 keys, and far
-// scores are multiplied by sigmoid(lambda a) before the softmax.
+// GA != 0 (bf16 dense pass only): the training-mode gate of the far pairs
+// (Technical Summary, Gated Attention: s_ij = q_i.k_j * sigmoid(lambda a_ij)).
+// This pass takes the far keys j <= i - gate_w only and writes a normalised
+// partial O and LSE per row; the plain window pass then merges the window
+// keys in.  Each stage also holds the tile's keys' assignment rows (bf16,
+// GA = 16 or 32 groups wide, LDS-DMA'd by wavefront 0); the affinity tile
+// a^T = A_k A_q^T is GA / 16 more MFMAs per 32 keys, and every score is
+// multiplied by sigmoid(lambda a) before the softmax.
 template <int D, bool BF16, bool GROUP, int GA>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
 {
@@ -604,6 +606,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     const int wq_max = GROUP ? tok[e_start + (wave_active ? wave_last_row : 0)]
                              : (int)(p_start + wave_last_row);
     const int bq_max = GROUP ? tok[e_start + tile_rows - 1] : (int)(p_start + tile_rows - 1);
+    // The gated pass covers only the far keys (j <= i - gate_w), all of them
+    // gated; a plain window pass merges the window keys in afterwards.  Its
+    // key range is the causal range of the query shifted back by gate_w, so
+    // the masks and the tile range below use positions shifted by qsh.
+    const int qsh = GATED ? p.gate_w : 0;
 
     typename TL::QFrag qf;
     TL::load_q(qf, static_cast<const T *>(p.q), ((int64_t)hq * p.n + qpos) * D, h);
@@ -611,6 +618,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     // (the second copy of the packed rows), as the B operand of the affinity
     // product (groups 16j + 8h .. 16j + 8h + 7 for k-step j)
     bf16x8 aq[GATED ? GA / 16 : 1];
+    // and the byte offset of its affinity A fragment in a stage: row sigma(m)
+    // of the tile's keys, 16-byte chunk 2j + h swizzled by row bit 4 (the
+    // chunk of k-step j and key block kb sits kb * 32 * GCH + 2j chunks on)
+    const uint32_t a_off =
+        GATED ? (uint32_t)((sigma(m) * GCH + (h ^ ((sigma(m) >> 4) & 1))) * 16) : 0u;
     if constexpr (GATED) {
         const bf16x8 *arow = static_cast<const bf16x8 *>(p.apack) +
                              ((int64_t)(p.hkv + kvh) * p.krows + qpos) * GCH;
@@ -711,10 +723,12 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         __syncthreads();
         n_tiles_total = __builtin_amdgcn_readfirstlane(sub_tiles);
     } else {
-        const int64_t lo = max<int64_t>(0, p_start - w + 1);
+        const int64_t lo = max<int64_t>(0, p_start - qsh - w + 1);
         j_first = (lo / kKeyTile) * kKeyTile;
-        const int64_t j_last = p_start + tile_rows - 1;
-        n_tiles_total = (w > 0) ? (int)((j_last - j_first) / kKeyTile + 1) : 0;
+        const int64_t j_last = p_start + tile_rows - 1 - qsh;
+        n_tiles_total = (w > 0 && (!GATED || j_last >= 0))
+                            ? (int)((j_last - j_first) / kKeyTile + 1)
+                            : 0;
     }
 
     // iterator over key tiles: (sub-bucket, tile) for the group pass.  The
@@ -817,40 +831,30 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             masked = (valid < kKeyTile) | (owner != 0) | (last_key > wq_min - w);
         } else {
             const int j0 = kpos[0];
-            masked = !((j0 + kKeyTile - 1 <= wq_min) && (j0 > wq_max - w));
+            masked = !((j0 + kKeyTile - 1 <= wq_min - qsh) && (j0 > wq_max - qsh - w));
         }
         TL::qk(s, qf, stage(I).k, lo);
         if constexpr (GATED) {
-            // far keys (position <= qpos - gate_w) take the gate; in the
-            // dense pass key index i of the tile is position kpos[0] + i
-            const int fhi = qpos - p.gate_w - kpos[0];
-            if (__builtin_amdgcn_ballot_w64(fhi >= 0) != 0) {
-                const bool all_far = __builtin_amdgcn_ballot_w64(!(fhi >= kKeyTile - 1)) == 0;
-                // register r of lane half h holds key index kb*32 + 16h + r:
-                // compare the constant kb*32 + r with the bound shifted by
-                // 16h (a per-register index would hold 32 registers)
-                const int fhi_h = fhi - 16 * h;
-                const char *al = stage(I).a;
+            // every key of the gated pass is far: each score takes the gate
+            // 1 / (1 + 2^a), a = -lambda log2(e) a_ij from the affinity
+            // product (keys past the causal bound are masked below).  The
+            // fragment address is formed here, by one add the compiler cannot
+            // hoist: hoisted, it would hold one address per stage for the
+            // whole loop and spill them.
+            const uint32_t a_at = lds_add(lds_address(stage(I).a), a_off);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int row = kb * 32 + sigma(m);
-                    f32x16 a;
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x16 a;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        a[r] = 0.f;
+                for (int r = 0; r < 16; ++r)
+                    a[r] = 0.f;
 #pragma unroll
-                    for (int j = 0; j < GA / 16; ++j)
-                        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            *reinterpret_cast<const bf16x8 *>(
-                                al + (row * GCH + ((2 * j + h) ^ ((row >> 4) & 1))) * 16),
-                            aq[j], a, 0, 0, 0);
+                for (int j = 0; j < GA / 16; ++j)
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        lds_read16(a_at + (kb * 32 * GCH + 2 * j) * 16), aq[j], a, 0, 0, 0);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float gate =
-                            __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a[r]));
-                        s[kb][r] *= (all_far || kb * 32 + r <= fhi_h) ? gate : 1.f;
-                    }
-                }
+                for (int r = 0; r < 16; ++r)
+                    s[kb][r] *= __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a[r]));
             }
         }
         if (masked) {
@@ -875,8 +879,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             } else {
                 // window pass: key index i is position j0 + i
                 const int j0 = kpos[0];
-                lo = qpos - w + 1 - j0;
-                hi = qpos - j0;
+                lo = qpos - qsh - w + 1 - j0;
+                hi = qpos - qsh - j0;
             }
             if (!qvalid)
                 hi = lo - 1;
@@ -1133,12 +1137,13 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     // log2-domain log-sum-exp of the scaled logits
     const float lse2 = (l_tot > 0.f) ? acc.m + __builtin_amdgcn_logf(l_tot) : -INFINITY;
 
-    if (GROUP) {
+    if (GROUP || GATED) {
         // normalised partial O (in the I/O dtype: bf16 for bf16 inputs, as
         // the merged output is) and natural-log LSE at the query's entry
+        // (the gated pass: at its row, for the window pass to merge)
         if (!qvalid)
             return;
-        const int64_t e = e_start + qr;
+        const int64_t e = GROUP ? (int64_t)(e_start + qr) : (int64_t)qpos;
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
         T *po = static_cast<T *>(p.part_o) + ((int64_t)hq * p.E + e) * D;
 #pragma unroll
@@ -1803,13 +1808,24 @@ __global__ __launch_bounds__(256) void gate_pack_kernel(const float *__restrict_
     apack[idx] = (__bf16)x;
     apack[total + idx] = (__bf16)(neg_lam2 * x);
 }
+
+// slot[h][i] = i: each row's one partial (the gated far pass's) sits at the
+// row itself, for the window pass's merge
+__global__ __launch_bounds__(256) void row_slots_kernel(int64_t n, int64_t total,
+                                                        int32_t *__restrict__ slot)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx < total)
+        slot[idx] = (int32_t)(idx % n);
+}
 }  // namespace
 
 size_t gated_dense_workspace_bytes(const AttnShape &sh)
 {
     const int64_t n_pad = (sh.n + kKeyTile - 1) / kKeyTile * kKeyTile + kKeyTile;
     return dense_workspace_bytes(sh) +
-           align_up((size_t)2 * sh.hkv * n_pad * kGateGroups * 2, 256);
+           align_up((size_t)2 * sh.hkv * n_pad * kGateGroups * 2, 256) +
+           align_up((size_t)sh.hkv * sh.n * 4, 256);
 }
 
 namespace {
@@ -1834,6 +1850,9 @@ hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k,
     __bf16 *vt = static_cast<__bf16 *>(ws);
     __bf16 *kp = reinterpret_cast<__bf16 *>(static_cast<char *>(ws) + half);
     __bf16 *apack = reinterpret_cast<__bf16 *>(static_cast<char *>(ws) + 2 * half);
+    int32_t *slots = reinterpret_cast<int32_t *>(
+        static_cast<char *>(ws) + 2 * half +
+        align_up((size_t)2 * sh.hkv * n_pad * kGateGroups * 2, 256));
     hipError_t e = launch_transpose(sh.d, static_cast<const __bf16 *>(v), nullptr, sh.n, sh.n,
                                     n_pad, sh.hkv, vt, s);
     if (e == hipSuccess)
@@ -1845,6 +1864,10 @@ hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k,
     const int64_t total = (int64_t)sh.hkv * n_pad * ga;
     hipLaunchKernelGGL(gate_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        assign, sh.n, n_pad, sh.K, ga, total, -lambda * kLog2e, apack);
+    const int64_t nslots = (int64_t)sh.hkv * sh.n;
+    if (nslots > 0)
+        hipLaunchKernelGGL(row_slots_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0,
+                           s, sh.n, nslots, slots);
     e = hipGetLastError();
     float *kpart = dense_kpart(ws, gated_dense_workspace_bytes(sh), sh.hkv);
     if (e == hipSuccess)
@@ -1865,11 +1888,26 @@ hipError_t launch_gated_dense(const AttnShape &sh, const void *q, const void *k,
     p.apack = apack;
     p.gate_w = (int)std::min<int64_t>(sh.window, sh.n);
     p.kpart = kpart;
+    // far pass (gated scores): its normalised partial O and LSE go to out
+    // and lse, which the window pass reads back and overwrites row by row
+    p.part_o = out;
+    p.part_lse = lse;
     if (ga == 16)
-        return sh.d == 64 ? launch_attn_kernel<64, true, false, 16>(p, s)
-                          : launch_attn_kernel<128, true, false, 16>(p, s);
-    return sh.d == 64 ? launch_attn_kernel<64, true, false, 32>(p, s)
-                      : launch_attn_kernel<128, true, false, 32>(p, s);
+        e = sh.d == 64 ? launch_attn_kernel<64, true, false, 16>(p, s)
+                       : launch_attn_kernel<128, true, false, 16>(p, s);
+    else
+        e = sh.d == 64 ? launch_attn_kernel<64, true, false, 32>(p, s)
+                       : launch_attn_kernel<128, true, false, 32>(p, s);
+    if (e != hipSuccess)
+        return e;
+    // window pass (plain scores over i - w < j <= i) with the merge
+    Params pw = p;
+    pw.window = p.gate_w;
+    pw.merge = 1;
+    pw.slot_entry = slots;
+    pw.apack = nullptr;
+    return sh.d == 64 ? launch_attn_kernel<64, true, false>(pw, s)
+                      : launch_attn_kernel<128, true, false>(pw, s);
 }
 
 hipError_t launch_dense(const AttnShape &sh, const void *q, const void *k, const void *v,

@@ -143,6 +143,22 @@ __device__ __forceinline__ void dma4(const void *gbase, uint32_t voff, uint32_t 
                  : "memory");
 }
 
+// base + off as one vector add the compiler can neither hoist nor fold:
+// for an address that would otherwise be kept, per stage, in registers
+// across a loop (base wave-uniform, in a scalar register)
+__device__ __forceinline__ uint32_t lds_add(uint32_t base, uint32_t off)
+{
+    uint32_t r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(base), "v"(off));
+    return r;
+}
+
+// 16-byte LDS read at a 32-bit LDS byte address
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(addr);
+}
+
 // Immediate of "s_waitcnt vmcnt(n) lgkmcnt(0)" (expcnt untouched) on gfx9:
 // vmcnt is split over bits 3:0 and 15:14, expcnt is bits 6:4, lgkmcnt 11:8.
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
