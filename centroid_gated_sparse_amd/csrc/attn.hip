@@ -245,8 +245,11 @@ struct Tile<D, true> {
     // (The sum is taken before rounding: near-uniform rows round their
     // probabilities the same way, and a sum of the rounded values would bias
     // the log-sum-exp by up to ~1e-3.)
+    // (PRE: s already holds the exponent c s - m)
+    template <bool PRE = false>
     __device__ static float exp_tile(const f32x16 (&s)[2], float c, float negm, PFrag &pf)
     {
+        auto arg = [&](float x) { return PRE ? x : __builtin_fmaf(x, c, negm); };
         float l0 = 0.f, l1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -254,10 +257,8 @@ struct Tile<D, true> {
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const float p0 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e], c, negm));
-                    const float p1 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][kk * 8 + e + 1], c, negm));
+                    const float p0 = __builtin_amdgcn_exp2f(arg(s[kb][kk * 8 + e]));
+                    const float p1 = __builtin_amdgcn_exp2f(arg(s[kb][kk * 8 + e + 1]));
                     l0 += p0;
                     l1 += p1;
                     pf.v[kb][kk][e] = (__bf16)p0;
@@ -380,8 +381,10 @@ struct Tile<D, false> {
             }
     }
 
+    template <bool PRE = false>
     __device__ static float exp_tile(const f32x16 (&s)[2], float c, float negm, PFrag &pf)
     {
+        static_assert(!PRE, "the fp32 path forms its exponents here");
         float l = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -442,7 +445,8 @@ struct Acc {
     // forms the row max; the threshold and the exponent offset are kept with
     // m, so a tile that leaves m alone costs the half maxima and one compare.
     // (c > 0: the entry points require a positive scale.)
-    template <bool FIXED>
+    // PRE (with FIXED only): s already holds the exponents c s - m
+    template <bool FIXED, bool PRE = false>
     __device__ void softmax(const f32x16 (&s)[2], float c, typename TL::PFrag &pf)
     {
         if constexpr (!FIXED) {
@@ -468,7 +472,8 @@ struct Acc {
                         o[db][r] *= alpha;
             }
         }
-        l += TL::exp_tile(s, c, negm, pf);
+        static_assert(FIXED || !PRE, "exponents are formed early only at a fixed offset");
+        l += TL::template exp_tile<PRE>(s, c, negm, pf);
     }
 };
 
@@ -649,7 +654,9 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     // With mb <= kFixedOffsetMax the offset m = mb needs no running max:
     // every P = 2^(c s - mb) lies in [2^-2mb, 1], inside the normal range of
     // fp32 and bf16, and fp32 keeps its relative precision at any scale.
-    const bool fixed_offset = BF16 && !GATED && mb <= kFixedOffsetMax;
+    // (the gate lies in (0, 1), so the bound holds for gated logits too)
+    const bool fixed_offset = BF16 && mb <= kFixedOffsetMax;
+    const float rcp_c = 1.f / p.c;
     Acc<TL> acc;
     if (fixed_offset)
         acc.init_fixed(mb);
@@ -817,7 +824,12 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     // Raw logits of one tile for this wavefront, masked where a pair falls
     // outside the pass: QK^T on the tile's K rows, then (only on tiles that
     // need it) the window / causal / owner tests on key positions in LDS.
-    auto scores = [&](f32x16 (&s)[2], auto I, int valid, int owner) {
+    // (FIXED, gated pass: the gate and the fixed offset are folded in here,
+    // and s leaves as the exponent c s g - m itself; see the gate below)
+    // (j0_tile: the tile's first key position, used by the gated pass in
+    // place of the stage's position list, which it does not fill)
+    auto scores = [&](f32x16 (&s)[2], auto I, int valid, int owner, int j0_tile, auto fixed_tag) {
+        constexpr bool FIXED = decltype(fixed_tag)::value;
         const int *kpos = stage(I).key;
         const uint32_t *kgm = reinterpret_cast<const uint32_t *>(kpos + kKeyTile);
         // Does any pair of this tile x wavefront need a mask?  Decided from
@@ -830,7 +842,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             const int last_key = kpos[valid - 1];  // valid >= 1
             masked = (valid < kKeyTile) | (owner != 0) | (last_key > wq_min - w);
         } else {
-            const int j0 = kpos[0];
+            const int j0 = GATED ? j0_tile : kpos[0];
             masked = !((j0 + kKeyTile - 1 <= wq_min - qsh) && (j0 > wq_max - qsh - w));
         }
         TL::qk(s, qf, stage(I).k, lo);
@@ -852,9 +864,21 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 for (int j = 0; j < GA / 16; ++j)
                     a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         lds_read16(a_at + (kb * 32 * GCH + 2 * j) * 16), aq[j], a, 0, 0, 0);
+                if constexpr (FIXED) {
+                    // c g = 1 / ((1 + 2^a) / c): the softmax's exponent
+                    // c s g - m in two fused multiply-adds and a reciprocal
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[kb][r] *= __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a[r]));
+                    for (int r = 0; r < 16; ++r)
+                        s[kb][r] = __builtin_fmaf(
+                            s[kb][r],
+                            __builtin_amdgcn_rcpf(
+                                __builtin_fmaf(__builtin_amdgcn_exp2f(a[r]), rcp_c, rcp_c)),
+                            acc.negm);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        s[kb][r] *= __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(a[r]));
+                }
             }
         }
         if (masked) {
@@ -878,7 +902,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 hi = cnt - 1;
             } else {
                 // window pass: key index i is position j0 + i
-                const int j0 = kpos[0];
+                const int j0 = GATED ? j0_tile : kpos[0];
                 lo = qpos - qsh - w + 1 - j0;
                 hi = qpos - qsh - j0;
             }
@@ -940,7 +964,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
             // a register copy of O per tile.
             f32x16 s[2];
             TL::refresh(lo);
-            scores(s, CUR, valid, owner);
+            scores(s, CUR, valid, owner, 0, FIXED);
             typename TL::PFrag pf;
             acc.template softmax<decltype(FIXED)::value>(s, p.c, pf);
             TL::pv(acc.o, pf, stage(CUR).v, lo);
@@ -991,7 +1015,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
         // every wavefront when it issues the tile's loads (the iterator runs
         // in each wavefront), read when the tile is computed; stage indices
         // are compile-time, so the ring stays in scalar registers
-        int ring_valid[NSTAGE] = {}, ring_owner[NSTAGE] = {};
+        int ring_valid[NSTAGE] = {}, ring_owner[NSTAGE] = {}, ring_origin[NSTAGE] = {};
         // (is_a: this wavefront's role, a compile-time constant inside the
         // role loops, so that role B's copies carry no load code or branches;
         // the gated pass keeps the run-time test, with which its registers
@@ -1007,25 +1031,29 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                     dma4(etk + origin, (uint32_t)lane * 4u, lds_address(kp));
                     dma4(egh + origin, (uint32_t)lane * 4u, lds_address(kp) + kKeyTile * 4);
                 }
-            } else if ((GATED || is_a) && threadIdx.x < kKeyTile) {
+            } else if (!GATED && is_a && threadIdx.x < kKeyTile) {
                 kp[threadIdx.x] = (int)(origin + threadIdx.x);
             }
             if constexpr (GATED) {
                 if (a_wave) {
                     const char *abase = static_cast<const char *>(p.apack) +
                                         ((int64_t)kvh * p.krows + origin) * GA * 2;
+                    // slot P = 64i + lane takes byte (P ^ b) * 16 of the
+                    // rows, b = bit 4 of its row P / GCH: lane bit 5 for
+                    // 16-group rows, i odd for 32-group rows.  The 1 KB step
+                    // goes to the scalar base, so the lane keeps one or two
+                    // offsets, not one per load.
 #pragma unroll
                     for (int i = 0; i < DMA_A; ++i) {
-                        const int P = i * kWave + lane;
-                        const int row = P / GCH;
-                        const int c = (P % GCH) ^ ((row >> 4) & 1);
-                        dma16(abase, (uint32_t)(row * GCH + c) * 16u,
+                        const uint32_t b = GCH == 2 ? ((uint32_t)lane >> 5) & 1u : (uint32_t)i & 1u;
+                        dma16(abase + i * 1024, (16u * (uint32_t)lane) ^ (b << 4),
                               lds_address(stage(I).a) + i * 1024);
                     }
                 }
             }
             ring_valid[decltype(I)::value] = nv;
             ring_owner[decltype(I)::value] = no;
+            ring_origin[decltype(I)::value] = (int)origin;
         };
         // end of an interval: everything but the newest tile's loads landed,
         // this interval's LDS traffic done, then the block barrier
@@ -1081,22 +1109,24 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
                 if (ROLE_A) {
                     if (u < T) {
                         scores(s, CUR, ring_valid[decltype(CUR)::value],
-                               ring_owner[decltype(CUR)::value]);
+                               ring_owner[decltype(CUR)::value],
+                               ring_origin[decltype(CUR)::value], fixed_tag);
                         issue_ahead();
-                        acc.template softmax<FIXED>(s, p.c, pf);
+                        acc.template softmax<FIXED, GATED && FIXED>(s, p.c, pf);
                         TL::pv(acc.o, pf, stage(CUR).v, lo);
                     }
                 } else {
                     if constexpr (decltype(FIRST)::value) {
                         issue_ahead();
                     } else {
-                        acc.template softmax<FIXED>(s, p.c, pf);
+                        acc.template softmax<FIXED, GATED && FIXED>(s, p.c, pf);
                         issue_ahead();
                         TL::pv(acc.o, pf, stage(PREV).v, lo);
                     }
                     if (u < T) {
                         scores(s, CUR, ring_valid[decltype(CUR)::value],
-                               ring_owner[decltype(CUR)::value]);
+                               ring_owner[decltype(CUR)::value],
+                               ring_origin[decltype(CUR)::value], fixed_tag);
                     }
                 }
                 close_interval(ahead, GATED ? role_a_wave : ROLE_A);

@@ -89,9 +89,10 @@ def run_gated(wl, lam, iters, seed):
     return c, r, q, k, v, out, lse
 
 
-def compare(tag, out, lse, q, k, v, A_ref, wl, lam, rh, rp):
+def compare(tag, out, lse, q, k, v, A_ref, wl, lam, rh, rp, scale=None):
+    scale = wl.scale if scale is None else scale
     o_ref, lse_ref = oracle.gated_attn_rows(to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v),
-                                            A_ref, wl.window, lam, wl.scale, rh, rp)
+                                            A_ref, wl.window, lam, scale, rh, rp)
     ih = torch.from_numpy(rh).long().to(DEV)
     ip = torch.from_numpy(rp).long().to(DEV)
     o = out[ih, ip].float().cpu().double().numpy()
@@ -121,3 +122,28 @@ def test_gated_attention_7b_shape_sampled_rows():
     A_ref = oracle.sinkhorn(r, c, iters)
     rh, rp = sample_rows(wl, 4300, 512)
     compare(wl.name, out, lse, q, k, v, A_ref, wl, lam, rh, rp)
+
+
+def test_gated_attention_running_max_path():
+    """Logits past the fixed-offset bound: with scale 1 every row's bound
+    |q_i| max|k| scale log2(e) exceeds 60 log2 units, so every wavefront of
+    the gated pass takes the running-max softmax (the cases above all fit
+    the fixed offset).  Every row; lambda small, so that the gate's bf16
+    rounding (at most |lambda| / 4 * 2^-8 of a logit) stays inside the LSE
+    bar at these larger logits."""
+    wl = W("g_lazy_d128", 600, 4, 2, 128, 8, 1, 48, "bf16", qkv_std=0.7)
+    lam, iters, scale = 0.05, 3, 1.0
+    c, r, _ = routing_inputs(wl, 4400)
+    q, k, v = qkv_inputs(wl, 4400, DEV)
+    qn = q.float().norm(dim=-1)
+    kmax = k.float().norm(dim=-1).amax(dim=-1)
+    ratio = wl.hq // wl.hkv
+    bound = qn * kmax.repeat_interleave(ratio)[:, None] * scale * 1.4426950408889634
+    assert float(bound.min()) > 64.0
+    A = F.focus_sinkhorn(torch.from_numpy(r).to(DEV), torch.from_numpy(c).to(DEV), iters)
+    out, lse = F.focus_gated_attn_fwd(q, k, v, A, wl.window, lam, scale)
+    torch.cuda.synchronize()
+    A_ref = oracle.sinkhorn(r, c, iters)
+    rh = np.repeat(np.arange(wl.hq, dtype=np.int32), wl.n)
+    rp = np.tile(np.arange(wl.n, dtype=np.int64), wl.hq)
+    compare(wl.name, out, lse, q, k, v, A_ref, wl, lam, rh, rp, scale=scale)
