@@ -358,8 +358,13 @@ focus_status focus_sinkhorn(const float *r, const float *centroids, int32_t H, i
  *   lambda     any finite value; window w >= 0; scale > 0
  *   out        bf16 [Hq, n, d];  lse  fp32 [Hq, n] (natural log)
  *   workspace  >= focus_gated_attn_workspace_bytes(Hkv, n, d, K) bytes:
- *              padded copies of K and V^T and two bf16 copies of the
- *              assignment (plain and scaled), padded to 32 groups
+ *              padded copies of K and V^T, two bf16 copies of the
+ *              assignment (plain and scaled) padded to 32 groups, and a
+ *              row-to-partial map (Hkv x n int32)
+ * Two passes: the far keys (i - j >= w, gated) first, written to out and
+ * lse as a normalised partial; then the window keys, merged with that
+ * partial by log-sum-exp, row by row in place.  out and lse must not
+ * overlap q, k, v or the workspace.
  * Errors: INVALID_ARGUMENT as focus_attn_fwd (and a non-finite lambda);
  * UNSUPPORTED for dt other than FOCUS_BF16, d not in {64, 128}, K > 32;
  * WORKSPACE if short.
