@@ -508,7 +508,8 @@ def run_train_forward(workload: str, steps: int, warmup: int, lam: float = 2.0,
         "tokens_per_s": wl.n / ((sk_ms + at_ms) / 1e3),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "kernel": "attn_kernel gated dense pass (4 d FLOPs per causal pair)"},
+                     "kernel": "focus_gated_attn_fwd: gated far pass + window pass "
+                               "(4 d FLOPs per causal pair)"},
     }
     log(f"train forward: sinkhorn {sk_ms:.3f} ms, gated attention {at_ms:.1f} ms, "
         f"{achieved:.0f} TFLOP/s")
