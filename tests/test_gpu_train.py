@@ -77,6 +77,10 @@ GATED = [
     (W("g_d64_w_ge_n", 257, 2, 1, 64, 4, 1, 257, "bf16", qkv_std=1.0), 5.0, 1),
     (W("g_single", 1, 2, 1, 128, 3, 1, 4, "bf16", qkv_std=1.0), 1.0, 2),
     (W("g_gqa4_d128_n1100", 1100, 8, 2, 128, 8, 1, 64, "bf16", qkv_std=0.4), 0.8, 3),
+    # w = 1: the window pass takes only j = i, the gated far pass the rest
+    (W("g_d128_w1", 333, 2, 1, 128, 6, 1, 1, "bf16", qkv_std=0.5), 1.2, 2),
+    # w = n - 1 with 32-group rows: one far pair per head, (n - 1, 0)
+    (W("g_d64_k24_wn1", 300, 4, 2, 64, 24, 1, 299, "bf16", qkv_std=0.6), -0.7, 3),
 ]
 
 
