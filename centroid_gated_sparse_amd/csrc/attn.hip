@@ -555,11 +555,9 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_kernel(Params p)
     __shared__ int sub_tiles;
 
     const int lane = threadIdx.x % kWave;
-    // (the gated and fp32 passes keep the wave index, and so the head, in
-    // scalar registers: the vector registers it frees avoid their spills)
-    const int wave = (GATED || !BF16)
-                         ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave)
-                         : (int)(threadIdx.x / kWave);
+    // (the wave index, and so the head, in scalar registers: the vector
+    // registers it frees keep the gated and fp32 passes free of spills)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int m = lane % 32;
     const int h = lane / 32;
 
